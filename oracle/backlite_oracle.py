@@ -1,0 +1,290 @@
+"""Plain fp64 CPU oracle for BackLite's forward / mask / sparse-backward path.
+
+TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
+bench's CPU-baseline leg may import or run this module; the product path never
+does, and this module imports nothing from the GPU package.
+
+It computes, slowly and directly, what the pages define:
+
+* Attention forward S = scale*Q K^T, P = row-softmax(S), O = P V, with the row
+  log-sum-exp kept for the backward ("Introducing BackLite", section
+  "Backpropagation for attention", forward equations; safe softmax with the
+  row maximum subtracted, FlashAttention tutorial, "Safe Softmax Algorithm").
+* A log-sum-exp per (query row, key tile) recorded by the forward, and the tile
+  probability p_tile = exp(LSE_tile - LSE_row) (BackLite README, "How It Works /
+  Sparse Backward Masking", phases 1 and 2).
+* The tile weight of a (query tile, key tile) pair = the maximum of p_tile over
+  the valid rows of the query tile (our reading: the blog's "sum of P over the
+  tile" and the README's per-tile LSE are both aggregations of the same
+  per-row numbers; the max is the conservative one, since it bounds every row's
+  neglected mass).
+* For each query tile, the smallest-weight key tiles whose cumulative weight
+  stays strictly below negl_prob are skipped ("Introducing BackLite", "Using
+  Sparsity"; README "Overview" and "Usage": cumulative weight < negl_prob).
+* The backward G_V = P^T G_O, G_P = G_O V^T, D = rowsum(G_O * O),
+  G_S = P * (G_P - D), G_Q = scale G_S K, G_K = scale G_S^T Q ("Introducing
+  BackLite", backward equations; D as the row sum, FlashAttention tutorial,
+  "Flash Attention Backward Pass"), with every skipped tile's entries of P and
+  G_S set to zero ("Using Sparsity": the mask on P carries over to G_S).
+
+Readings where the pages are silent (each also listed in the design notes):
+natural-log LSEs; strict "<"; ties among equal weights broken by the lower key
+tile index first; the order is taken on the exact exponent a = log(w) (equal
+a <=> equal w); prefix sums are sequential fp64 adds in sorted order; causally
+empty tiles are not candidates; padded rows/columns of a ragged last tile never
+enter any sum or maximum; D uses the full (unmasked) output row.
+
+Layouts: Q, O, G_O, G_Q are [B, n, H, d]; K, V, G_K, G_V are [B, n, Hk, d];
+LSE is [B, H, n]; the oracle's tile LSE is [B, H, n, T] (row-major by query
+row), T = ceil(n / tile).  Query head h reads kv head h // (H // Hk).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TILE = 128
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+def to_f64(x) -> np.ndarray:
+    """bf16/fp32 torch tensor or numpy array -> float64 numpy (exact upcast)."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch  # local: only to convert torch inputs
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def ntiles(n: int, tile: int = TILE) -> int:
+    return (n + tile - 1) // tile
+
+
+def kv_head(h: int, H: int, Hk: int) -> int:
+    return h // (H // Hk)
+
+
+def candidates(n: int, causal: bool, tile: int = TILE) -> np.ndarray:
+    """cand[qt, kt]: the key tile holds at least one (i, j) with i, j < n that the
+    causal rule (j <= i) allows.  Causally empty tiles are never candidates."""
+    T = ntiles(n, tile)
+    qt = np.arange(T)[:, None]
+    kt = np.arange(T)[None, :]
+    if causal:
+        return kt <= qt   # tile kt's first key 128*kt is <= the last row of tile qt
+    return np.ones((T, T), bool)
+
+
+def _score_block(qh, kh, rows, scale, causal):
+    """S for query rows `rows` against all keys, -inf where causally masked."""
+    S = scale * (qh[rows] @ kh.T)
+    if causal:
+        j = np.arange(kh.shape[0])[None, :]
+        S = np.where(j <= rows[:, None], S, -np.inf)
+    return S
+
+
+def _row_lse(S):
+    """Safe log-sum-exp per row: m + log(sum exp(S - m))."""
+    m = S.max(axis=1, keepdims=True)
+    return (m + np.log(np.exp(S - m).sum(axis=1, keepdims=True)))[:, 0]
+
+
+def _tile_lse(S, n, tile):
+    """log-sum-exp of S over each key tile's columns; -inf if none is finite."""
+    T = ntiles(n, tile)
+    pad = np.full((S.shape[0], T * tile), -np.inf)
+    pad[:, :n] = S
+    Z = pad.reshape(S.shape[0], T, tile)
+    m = Z.max(axis=2)
+    fin = np.isfinite(m)
+    msafe = np.where(fin, m, 0.0)
+    with np.errstate(divide="ignore"):
+        s = np.log(np.exp(Z - msafe[:, :, None]).sum(axis=2))
+    return np.where(fin, msafe + s, -np.inf)
+
+
+# ----------------------------------------------------------------------------
+# forward with per-(row, key tile) statistics
+# ----------------------------------------------------------------------------
+def forward(q, k, v, scale=None, causal=False, tile=TILE, heads=None, rows=None, block=128):
+    """Exact attention forward plus tile statistics.
+
+    Returns dict with O [B, nr, H', d], lse [B, H', nr], tile_lse [B, H', nr, T]
+    where nr = len(rows) (all rows by default) and H' = len(heads).
+    """
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    heads = list(range(H)) if heads is None else list(heads)
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    T = ntiles(n, tile)
+    O = np.zeros((B, len(rows), len(heads), d))
+    lse = np.zeros((B, len(heads), len(rows)))
+    tl = np.zeros((B, len(heads), len(rows), T))
+    for b in range(B):
+        for hi, h in enumerate(heads):
+            g = kv_head(h, H, Hk)
+            qh, kh, vh = q[b, :, h], k[b, :, g], v[b, :, g]
+            for s in range(0, len(rows), block):
+                r = rows[s:s + block]
+                S = _score_block(qh, kh, r, scale, causal)
+                L = _row_lse(S)
+                P = np.exp(S - L[:, None])
+                O[b, s:s + block, hi] = P @ vh
+                lse[b, hi, s:s + block] = L
+                tl[b, hi, s:s + block] = _tile_lse(S, n, tile)
+    return {"O": O, "lse": lse, "tile_lse": tl}
+
+
+# ----------------------------------------------------------------------------
+# mask from statistics
+# ----------------------------------------------------------------------------
+def tile_log_weights(tile_lse, lse, n, causal, tile=TILE):
+    """a[b, h, qt, kt] = max over valid rows i of the query tile of
+    (LSE_tile[i, kt] - LSE_row[i]), in fp64; the tile weight is w = exp(a)
+    (README phase 2: p_tile = exp(LSE_tile - LSE_row)).  -inf off-candidate.
+
+    tile_lse: [B, H, n, T] (fp32 or fp64 values); lse: [B, H, n].
+    """
+    tl = np.asarray(tile_lse, dtype=np.float64)
+    ls = np.asarray(lse, dtype=np.float64)
+    B, H, nn, T = tl.shape
+    assert nn == n
+    diff = tl - ls[..., None]
+    pad = np.full((B, H, T * tile, T), -np.inf)
+    pad[:, :, :n] = diff
+    a = pad.reshape(B, H, T, tile, T).max(axis=3)
+    cand = candidates(n, causal, tile)
+    return np.where(cand[None, None], a, -np.inf)
+
+
+def select_keep(a, cand, negl_prob):
+    """keep[b, h, qt, kt] from log-weights a.
+
+    Per query tile: order the candidate key tiles by (a ascending, kt ascending),
+    form sequential fp64 prefix sums c_r of w = exp(a) in that order, and skip
+    position r iff c_r < negl_prob.  Weights are >= 0 so the skipped set is a
+    prefix of the order.  Everything else among the candidates is kept.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    B, H, T, _ = a.shape
+    keep = np.zeros((B, H, T, T), bool)
+    for b in range(B):
+        for h in range(H):
+            for qt in range(T):
+                idx = np.nonzero(cand[qt])[0]
+                if idx.size == 0:
+                    continue
+                av = a[b, h, qt, idx]
+                order = np.lexsort((idx, av))          # primary a, then kt
+                c = np.add.accumulate(np.exp(av[order]))  # sequential left-to-right
+                skipped = idx[order][c < negl_prob]
+                kp = np.ones(idx.size, bool)
+                kp[np.isin(idx, skipped)] = False
+                keep[b, h, qt, idx[kp]] = True
+    return keep
+
+
+def mask_from_stats(tile_lse, lse, n, causal, negl_prob, tile=TILE):
+    a = tile_log_weights(tile_lse, lse, n, causal, tile)
+    cand = candidates(n, causal, tile)
+    return select_keep(a, cand, negl_prob)
+
+
+def lists_from_keep(keep):
+    """Compacted work lists.  q-list(qt) = kept kt ascending; k-list(kt) = kept
+    qt ascending.  Returns (qcnt, qidx, kcnt, kidx); rows of qidx/kidx hold the
+    list in their first cnt entries and zeros after."""
+    keep = np.asarray(keep, bool)
+    B, H, T, _ = keep.shape
+    qcnt = keep.sum(axis=3).astype(np.int32)
+    kcnt = keep.sum(axis=2).astype(np.int32)
+    qidx = np.zeros((B, H, T, T), np.uint16)
+    kidx = np.zeros((B, H, T, T), np.uint16)
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                r = np.nonzero(keep[b, h, t])[0]
+                qidx[b, h, t, :r.size] = r
+                c = np.nonzero(keep[b, h, :, t])[0]
+                kidx[b, h, t, :c.size] = c
+    return qcnt, qidx, kcnt, kidx
+
+
+# ----------------------------------------------------------------------------
+# D and the (masked) backward
+# ----------------------------------------------------------------------------
+def delta(do, o):
+    """D[b, h, i] = sum_c G_O[b, i, h, c] * O[b, i, h, c]."""
+    do, o = to_f64(do), to_f64(o)
+    return np.einsum("bihc,bihc->bhi", do, o)
+
+
+def backward(q, k, v, do, keep=None, scale=None, causal=False, tile=TILE,
+             heads=None, q_rows=None):
+    """Masked attention backward in fp64.
+
+    keep: [B, H, T, T] bool tile mask over *all* heads (None = every candidate).
+    heads: restrict to these query heads (G_K/G_V then sum over those heads only).
+    q_rows: restrict the query rows that contribute (G_Q is returned for those
+    rows only; G_K/G_V then hold only those rows' contributions).
+    Returns dict dQ [B, nr, H', d], dK, dV [B, n, Hk, d], plus O, lse, D.
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    heads = list(range(H)) if heads is None else list(heads)
+    rows = np.arange(n) if q_rows is None else np.asarray(q_rows)
+    T = ntiles(n, tile)
+    cand = candidates(n, causal, tile)
+    dQ = np.zeros((B, len(rows), len(heads), d))
+    dK = np.zeros((B, n, Hk, d))
+    dV = np.zeros((B, n, Hk, d))
+    Oall = np.zeros((B, len(rows), len(heads), d))
+    Lall = np.zeros((B, len(heads), len(rows)))
+    Dall = np.zeros((B, len(heads), len(rows)))
+    kt_of_col = np.arange(n) // tile
+    for b in range(B):
+        for hi, h in enumerate(heads):
+            g = kv_head(h, H, Hk)
+            qh, kh, vh, doh = q[b, :, h], k[b, :, g], v[b, :, g], do[b, :, h]
+            km = cand if keep is None else np.asarray(keep[b, h], bool)
+            for s in range(0, len(rows), tile):
+                r = rows[s:s + tile]
+                S = _score_block(qh, kh, r, scale, causal)
+                L = _row_lse(S)
+                P = np.exp(S - L[:, None])
+                O = P @ vh
+                D = (doh[r] * O).sum(axis=1)           # full-row D
+                M = km[(r // tile)[:, None], kt_of_col[None, :]]
+                Ph = np.where(M, P, 0.0)
+                dP = doh[r] @ vh.T
+                dS = Ph * (dP - D[:, None])
+                dQ[b, s:s + tile, hi] = scale * (dS @ kh)
+                dK[b, :, g] += scale * (dS.T @ qh[r])
+                dV[b, :, g] += Ph.T @ doh[r]
+                Oall[b, s:s + tile, hi] = O
+                Lall[b, hi, s:s + tile] = L
+                Dall[b, hi, s:s + tile] = D
+    return {"dQ": dQ, "dK": dK, "dV": dV, "O": Oall, "lse": Lall, "D": Dall}
+
+
+# ----------------------------------------------------------------------------
+# comparison metrics (rel-L2 and cosine on the flattened tensors)
+# ----------------------------------------------------------------------------
+def rel_l2(a, ref):
+    a, ref = to_f64(a).ravel(), to_f64(ref).ravel()
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(a - ref) / (den if den > 0 else 1.0))
+
+
+def cosine(a, ref):
+    a, ref = to_f64(a).ravel(), to_f64(ref).ravel()
+    na, nr = np.linalg.norm(a), np.linalg.norm(ref)
+    if na == 0 and nr == 0:
+        return 1.0
+    return float(a @ ref / (na * nr))

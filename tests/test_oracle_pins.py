@@ -1,0 +1,373 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test fixes the oracle to a library routine, a closed form, a value the
+pages print, brute force on a tiny input, or an invariant the pages state, so
+that a dropped term, a wrong sign or index, or a transposed operand in the
+oracle fails at least one of them.  CPU only.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import backlite_oracle as orc
+from workloads import TINY, make_inputs, small
+
+
+def _rand(shape, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    return scale * g.standard_normal(shape)
+
+
+def _torch_attention(q, k, v, scale, causal):
+    """Reference via torch fp64 library ops on CPU: [B,n,H,d] layout, GQA by repeat."""
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    G = H // Hk
+    qt = q.permute(0, 2, 1, 3)
+    kt = k.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    vt = v.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    S = scale * torch.matmul(qt, kt.transpose(-1, -2).contiguous())
+    if causal:
+        m = torch.ones(n, n, dtype=torch.bool).tril()
+        S = S.masked_fill(~m, float("-inf"))
+    lse = torch.logsumexp(S, dim=-1)
+    P = torch.softmax(S, dim=-1)
+    O = torch.matmul(P, vt).permute(0, 2, 1, 3)
+    return O, lse, S, P
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n,H,Hk,d,causal", [(200, 2, 2, 16, False), (200, 4, 2, 16, True),
+                                              (129, 2, 1, 8, True), (1, 1, 1, 4, False)])
+def test_forward_matches_torch_library(n, H, Hk, d, causal):
+    q, k, v = _rand((1, n, H, d), 1), _rand((1, n, Hk, d), 2), _rand((1, n, Hk, d), 3)
+    sc = 0.37
+    out = orc.forward(q, k, v, scale=sc, causal=causal, tile=64)
+    O, lse, _, _ = _torch_attention(*(torch.from_numpy(x) for x in (q, k, v)), sc, causal)
+    np.testing.assert_allclose(out["O"], O.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out["lse"], lse.numpy(), rtol=0, atol=1e-12)
+
+
+def test_softmax_overflow_case(golden_dir):
+    vals = {}
+    for line in open(os.path.join(golden_dir, "softmax_overflow.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, *nums = line.split()
+        vals[key] = [float(x) for x in nums]
+    # one query, three keys, d = 1, scale 1: S = q * k = [1000, 1001, 1002]
+    q = np.ones((1, 1, 1, 1))
+    k = np.array(vals["scores"]).reshape(1, 3, 1, 1)
+    v = np.array([1.0, 0.0, 0.0]).reshape(1, 3, 1, 1)
+    # pad the query to 3 rows so the shapes agree; only row 0 is examined
+    qq = np.ones((1, 3, 1, 1))
+    out = orc.forward(qq, k, v, scale=1.0, causal=False, tile=4)
+    assert np.isfinite(out["lse"]).all()
+    assert out["lse"][0, 0, 0] == pytest.approx(vals["lse"][0], abs=1e-12)
+    # O with V = e_0 picks P[0]; check all three probabilities with three one-hot V's
+    for c in range(3):
+        vc = np.zeros((1, 3, 1, 1))
+        vc[0, c, 0, 0] = 1.0
+        o = orc.forward(qq, k, vc, scale=1.0, tile=4)["O"][0, 0, 0, 0]
+        # exp(S - LSE) with S ~ 1e3 carries the rounding of LSE (ulp 1.1e-13)
+        assert o == pytest.approx(vals["p"][c], rel=1e-12)
+    del q
+
+
+def test_tile_lse_identities():
+    """logsumexp over a row's tile LSEs equals the row LSE; p_tile sums to 1."""
+    for causal in (False, True):
+        q, k, v = _rand((1, 300, 2, 8), 4, 2.0), _rand((1, 300, 1, 8), 5, 2.0), _rand((1, 300, 1, 8), 6)
+        out = orc.forward(q, k, v, causal=causal, tile=64)
+        tl, L = out["tile_lse"], out["lse"]
+        m = tl.max(axis=-1, keepdims=True)
+        lse_of_tiles = (m + np.log(np.exp(tl - m).sum(-1, keepdims=True)))[..., 0]
+        np.testing.assert_allclose(lse_of_tiles, L, atol=1e-12)
+        np.testing.assert_allclose(np.exp(tl - L[..., None]).sum(-1), 1.0, atol=1e-12)
+        if causal:
+            # a tile that lies entirely above the diagonal has no valid key: -inf
+            rows = np.arange(300)
+            for kt in range(tl.shape[-1]):
+                empty = rows < 64 * kt
+                assert np.isneginf(tl[0, :, empty, kt]).all()
+                assert np.isfinite(tl[0, :, ~empty, kt]).all()
+
+
+def test_tile_lse_brute_force_small():
+    """Per-element brute force with Python loops on a tiny ragged causal case."""
+    n, d, t = 11, 3, 4
+    q, k, v = _rand((1, n, 1, d), 7), _rand((1, n, 1, d), 8), _rand((1, n, 1, d), 9)
+    sc = 0.5
+    out = orc.forward(q, k, v, scale=sc, causal=True, tile=t)
+    for i in range(n):
+        for kt in range((n + t - 1) // t):
+            terms = [math.exp(sc * float(q[0, i, 0] @ k[0, j, 0]))
+                     for j in range(kt * t, min(n, kt * t + t)) if j <= i]
+            ref = math.log(sum(terms)) if terms else -math.inf
+            got = out["tile_lse"][0, 0, i, kt]
+            if terms:
+                assert got == pytest.approx(ref, abs=1e-12)
+            else:
+                assert got == -math.inf
+
+
+def test_causal_block_classification(golden_dir):
+    """The page's N=16, block-4 worked example: which query blocks see key block 1."""
+    rows = [l.split() for l in open(os.path.join(golden_dir, "causal_blocks_n16_t4.txt"))
+            if l.strip() and not l.startswith("#")]
+    n, t = 16, 4
+    cand = orc.candidates(n, True, t)
+    q = _rand((1, n, 1, 2), 10)
+    k = _rand((1, n, 1, 2), 11)
+    tl = orc.forward(q, k, k, causal=True, tile=t)["tile_lse"][0, 0]   # [n, T]
+    for qb, r0, r1, cls in rows:
+        qb, r0, r1 = int(qb), int(r0), int(r1)
+        valid = np.array([[j <= i for j in range(4, 8)] for i in range(r0, r1 + 1)])
+        if cls == "empty":
+            assert not cand[qb, 1] and not valid.any()
+            assert np.isneginf(tl[r0:r1 + 1, 1]).all()
+        elif cls == "partial":
+            assert cand[qb, 1] and valid.any() and not valid.all()
+        else:
+            assert cand[qb, 1] and valid.all()
+        if cls != "empty":
+            assert np.isfinite(tl[r0:r1 + 1, 1]).all()
+
+
+# --------------------------------------------------------------------------
+# selection
+# --------------------------------------------------------------------------
+def test_selection_closed_form_uniform():
+    """Q = 0 => S = 0 => every tile weight is 1/8 (n = 1024, 8 key tiles)."""
+    n, d = 1024, 64
+    q = np.zeros((1, n, 1, d))
+    k = _rand((1, n, 1, d), 12)
+    v = _rand((1, n, 1, d), 13)
+    out = orc.forward(q, k, v)
+    assert out["lse"] == pytest.approx(math.log(1024.0), abs=1e-12)
+    assert out["tile_lse"] == pytest.approx(math.log(128.0), abs=1e-12)
+    np.testing.assert_allclose(out["O"][0, :, 0], np.broadcast_to(v[0, :, 0].mean(0), (n, d)), atol=1e-12)
+    a = orc.tile_log_weights(out["tile_lse"], out["lse"], n, False)
+    np.testing.assert_allclose(np.exp(a), 0.125, rtol=1e-15)
+    cand = orc.candidates(n, False)
+    expect = {0.05: [], 0.3: [0, 1], 0.9: [0, 1, 2, 3, 4, 5, 6]}
+    for pi, skipped in expect.items():
+        keep = orc.select_keep(a, cand, pi)
+        for qt in range(8):
+            assert sorted(set(range(8)) - set(np.nonzero(keep[0, 0, qt])[0])) == skipped
+
+
+def test_selection_strictness_and_ties():
+    """Exact weights 1/4 (exp(log 0.25) == 0.25 in fp64): the prefix sums are
+    0.25, 0.5, 0.75, 1.0 exactly, so negl_prob = 0.5 skips only the first tile
+    (0.5 is not < 0.5), and among equal weights the lower kt goes first."""
+    assert math.exp(math.log(0.25)) == 0.25
+    a = np.full((1, 1, 4, 4), math.log(0.25))
+    cand = orc.candidates(4 * 128, False)
+    keep = orc.select_keep(a, cand, 0.5)
+    assert (keep[0, 0] == np.array([False, True, True, True])).all()
+    keep = orc.select_keep(a, cand, np.nextafter(0.5, 1.0))
+    assert (keep[0, 0] == np.array([False, False, True, True])).all()
+    keep = orc.select_keep(a, cand, 0.0)
+    assert keep.all()
+
+
+def _brute_keep(w, pi):
+    """Brute force: tile t is skipped iff the total weight of every tile that
+    precedes-or-equals it in the (w, kt) order is < pi (pairwise comparisons,
+    no sort)."""
+    T = len(w)
+    out = np.ones(T, bool)
+    for t in range(T):
+        le = [u for u in range(T) if (w[u], u) <= (w[t], t)]
+        if math.fsum(w[u] for u in le) < pi:
+            out[t] = False
+    return out
+
+
+def test_selection_brute_force():
+    g = np.random.default_rng(14)
+    for trial in range(300):
+        T = int(g.integers(1, 8))
+        w = g.dirichlet(np.ones(T) * 0.5)
+        if trial % 5 == 0:
+            w = np.round(w * 8) / 8 + 1e-3          # force equal weights
+        pi = float(g.uniform(0, 1))
+        a = np.log(w).reshape(1, 1, 1, T)
+        a = np.broadcast_to(a, (1, 1, T, T)).copy()
+        keep = orc.select_keep(a, orc.candidates(T * 128, False), pi)[0, 0, 0]
+        ref = _brute_keep(np.exp(np.log(w)), pi)
+        # a sum within 1e-12 of pi may round either way between fsum and the
+        # sequential sum; skip those draws
+        cs = np.sort(w)
+        if np.min(np.abs(np.cumsum(cs) - pi)) < 1e-12:
+            continue
+        assert (keep == ref).all(), (w, pi, keep, ref)
+
+
+def test_selection_invariants_on_block_workload():
+    """I3: skipped mass per row < negl_prob; I5: every query tile keeps >= 1;
+    I6: the keep set shrinks as negl_prob grows; off-diagonal tiles of the
+    block-structured workload are negligible so only the diagonal is kept."""
+    x = make_inputs(TINY)
+    out = orc.forward(x["q"], x["k"], x["v"])
+    a = orc.tile_log_weights(out["tile_lse"], out["lse"], TINY.n, False)
+    cand = orc.candidates(TINY.n, False)
+    prev = None
+    p = np.exp(out["tile_lse"] - out["lse"][..., None])     # [B,H,n,T]
+    for pi in (0.0, 1e-12, 0.01, 0.05, 0.1, 0.5, 0.99):
+        keep = orc.select_keep(a, cand, pi)
+        assert keep.sum(axis=3).min() >= 1
+        if prev is not None:
+            assert not (keep & ~prev).any()
+        prev = keep
+        for qt in range(8):
+            skip = ~keep[0, :, qt, :]                        # [H, T]
+            w = np.exp(a[0, :, qt, :])
+            assert ((w * skip).sum(-1) < pi + 0.0).all() or pi == 0.0
+            rows = p[0, :, qt * 128:(qt + 1) * 128, :]
+            assert ((rows * skip[:, None, :]).sum(-1) < max(pi, 1e-300)).all() or pi == 0.0
+        if pi >= 1e-6:      # the largest off-diagonal weight here is ~4e-10
+            assert (keep[0, :] == np.eye(8, dtype=bool)[None]).all()
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def _loss_fd(q, k, v, do, scale, causal):
+    O = orc.forward(q, k, v, scale=scale, causal=causal, tile=16)["O"]
+    return float((do * O).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_grads_central_differences(causal):
+    """n = 64, d = 16: central differences of L = sum(G_O * O), step 1e-6."""
+    n, d = 64, 16
+    q, k, v, do = (_rand((1, n, 1, d), s, 0.7) for s in (20, 21, 22, 23))
+    sc = 1.0 / math.sqrt(d)
+    g = orc.backward(q, k, v, do, scale=sc, causal=causal, tile=16)
+    h = 1e-6
+    rng = np.random.default_rng(24)
+    for name, X, G in (("q", q, g["dQ"]), ("k", k, g["dK"]), ("v", v, g["dV"])):
+        for _ in range(40):
+            i, c = int(rng.integers(n)), int(rng.integers(d))
+            Xp, Xm = X.copy(), X.copy()
+            Xp[0, i, 0, c] += h
+            Xm[0, i, 0, c] -= h
+            args = {"q": q, "k": k, "v": v}
+            fp = _loss_fd(*(Xp if nm == name else args[nm] for nm in ("q", "k", "v")), do, sc, causal)
+            fm = _loss_fd(*(Xm if nm == name else args[nm] for nm in ("q", "k", "v")), do, sc, causal)
+            fd = (fp - fm) / (2 * h)
+            an = G[0, i, 0, c]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, i, c, fd, an)
+
+
+@pytest.mark.parametrize("n,H,Hk,causal", [(200, 2, 2, False), (200, 4, 1, True), (130, 4, 2, False)])
+def test_dense_grads_torch_autograd(n, H, Hk, causal):
+    d = 16
+    q, k, v, do = _rand((1, n, H, d), 30), _rand((1, n, Hk, d), 31), _rand((1, n, Hk, d), 32), _rand((1, n, H, d), 33)
+    sc = 0.3
+    g = orc.backward(q, k, v, do, scale=sc, causal=causal, tile=64)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    O, _, _, _ = _torch_attention(tq, tk, tv, sc, causal)
+    O.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(g["dQ"], tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(g["dK"], tk.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(g["dV"], tv.grad.numpy(), atol=1e-11)
+
+
+def test_masked_grads_torch_autograd():
+    """A mask that drops heavy tiles.  Independent route: dS_dense from torch
+    autograd through softmax, restricted by the element mask; G_Q, G_K from
+    autograd of S = scale Q K^T fed that restricted dS; G_V from autograd of
+    (masked P, held constant) @ V."""
+    n, d, t = 192, 8, 64
+    q, k, v, do = _rand((1, n, 1, d), 40, 1.5), _rand((1, n, 1, d), 41, 1.5), _rand((1, n, 1, d), 42), _rand((1, n, 1, d), 43)
+    sc = 0.5
+    for causal in (False, True):
+        keep = orc.candidates(n, causal, t).copy()
+        keep[2, 0] = False
+        keep[1, 1] = False
+        keep[0, 0] = True
+        g = orc.backward(q, k, v, do, keep=keep[None, None], scale=sc, causal=causal, tile=t)
+        tq, tk, tv = (torch.from_numpy(x[0, :, 0]).requires_grad_() for x in (q, k, v))
+        tdo = torch.from_numpy(do[0, :, 0])
+        S = sc * tq @ tk.T
+        if causal:
+            S = S.masked_fill(~torch.ones(n, n, dtype=torch.bool).tril(), float("-inf"))
+        P = torch.softmax(S, -1)
+        O = P @ tv
+        dS_dense, = torch.autograd.grad(O, S, tdo, retain_graph=True)
+        M = torch.from_numpy(np.kron(keep, np.ones((t, t), bool))[:n, :n])
+        dQ, dK = torch.autograd.grad(S, (tq, tk), torch.where(M, dS_dense, 0.0))
+        dV, = torch.autograd.grad(torch.where(M, P, 0.0).detach() @ tv, tv, tdo)
+        np.testing.assert_allclose(g["dQ"][0, :, 0], dQ.numpy(), atol=1e-11)
+        np.testing.assert_allclose(g["dK"][0, :, 0], dK.numpy(), atol=1e-11)
+        np.testing.assert_allclose(g["dV"][0, :, 0], dV.numpy(), atol=1e-11)
+
+
+def test_all_keep_and_zero_negl_are_dense():
+    """I4/I7: negl_prob = 0 keeps every candidate; the all-keep mask reproduces
+    the dense backward exactly."""
+    w = small(300, H=2, Hk=1, d=16, causal=True, kind="blocks")
+    x = make_inputs(w)
+    out = orc.forward(x["q"], x["k"], x["v"], causal=True)
+    keep = orc.mask_from_stats(out["tile_lse"], out["lse"], w.n, True, 0.0)
+    assert (keep == orc.candidates(w.n, True)[None, None]).all()
+    g0 = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=None, causal=True)
+    g1 = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=True)
+    for key in ("dQ", "dK", "dV"):
+        assert np.array_equal(g0[key], g1[key])
+
+
+def test_block_diagonal_limit():
+    """With the tiny block workload every off-diagonal tile weight is below
+    ~4e-10, so the sparse gradients differ from the dense ones by no more than
+    about that much, relative."""
+    x = make_inputs(TINY)
+    out = orc.forward(x["q"], x["k"], x["v"])
+    keep = orc.mask_from_stats(out["tile_lse"], out["lse"], TINY.n, False, 0.05)
+    assert keep.sum() == 2 * 8
+    a = orc.tile_log_weights(out["tile_lse"], out["lse"], TINY.n, False)
+    wmax = float(np.exp(a[~keep]).max())
+    assert wmax < 1e-9
+    gd = orc.backward(x["q"], x["k"], x["v"], x["do"])
+    gs = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep)
+    for key in ("dQ", "dK", "dV"):
+        r = orc.rel_l2(gs[key], gd[key])
+        assert 0 < r < 10 * wmax
+
+
+def test_gqa_equals_repeated_mha():
+    n, H, Hk, d = 160, 4, 2, 8
+    q, k, v, do = _rand((1, n, H, d), 50), _rand((1, n, Hk, d), 51), _rand((1, n, Hk, d), 52), _rand((1, n, H, d), 53)
+    keep = np.random.default_rng(54).random((1, H, 3, 3)) < 0.6
+    keep[..., 0] = True
+    g = orc.backward(q, k, v, do, keep=keep, causal=False, tile=64)
+    kr, vr = np.repeat(k, 2, axis=2), np.repeat(v, 2, axis=2)
+    gr = orc.backward(q, kr, vr, do, keep=keep, causal=False, tile=64)
+    np.testing.assert_allclose(g["dQ"], gr["dQ"], atol=1e-13)
+    np.testing.assert_allclose(g["dK"], gr["dK"].reshape(1, n, Hk, 2, d).sum(3), atol=1e-13)
+    np.testing.assert_allclose(g["dV"], gr["dV"].reshape(1, n, Hk, 2, d).sum(3), atol=1e-13)
+
+
+def test_lists_from_keep():
+    keep = np.zeros((1, 1, 3, 3), bool)
+    keep[0, 0] = [[1, 0, 1], [0, 0, 1], [1, 1, 1]]
+    qcnt, qidx, kcnt, kidx = orc.lists_from_keep(keep)
+    assert qcnt.tolist() == [[[2, 1, 3]]]
+    assert qidx[0, 0, 0, :2].tolist() == [0, 2] and qidx[0, 0, 1, :1].tolist() == [2]
+    assert kcnt.tolist() == [[[2, 1, 3]]]
+    assert kidx[0, 0, 0, :2].tolist() == [0, 2] and kidx[0, 0, 2, :3].tolist() == [0, 1, 2]
+
+
+def test_metrics():
+    a = np.array([1.0, 2.0, 3.0])
+    assert orc.rel_l2(a, a) == 0.0 and orc.cosine(a, a) == pytest.approx(1.0)
+    assert orc.rel_l2(2 * a, a) == pytest.approx(1.0)
+    assert orc.cosine(-a, a) == pytest.approx(-1.0)
