@@ -1,0 +1,180 @@
+"""ctypes binding of libbacklite.so (argument marshalling only).
+
+Every function here takes torch CUDA tensors, checks dtype/shape/device on the
+host, and passes raw device pointers and the current HIP stream to the C ABI
+declared in include/backlite.h.  All computation happens in the library's HIP
+kernels; there is no fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("BACKLITE_LIB", os.path.join(_PKG, "libbacklite.so"))
+TILE = 128
+
+_lib = None
+
+
+class BackliteError(RuntimeError):
+    pass
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise BackliteError(
+            f"{LIB_PATH} not found: build it with `python -m block_sparse_attention_fa_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.backlite_tile_lse_elems.argtypes = [I, I, I, I]
+    lib.backlite_tile_lse_elems.restype = Z
+    lib.backlite_mask_elems.argtypes = [I, I, I]
+    lib.backlite_mask_elems.restype = Z
+    lib.backlite_count_elems.argtypes = [I, I, I]
+    lib.backlite_count_elems.restype = Z
+    lib.backlite_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.backlite_bwd_workspace_bytes.restype = Z
+    lib.backlite_fwd.argtypes = [P, P, P, I, I, I, I, I, F, I, P, P, P, P, P]
+    lib.backlite_fwd.restype = I
+    lib.backlite_mask.argtypes = [P, P, I, I, I, I, F, P, P, P, P, P, P, P]
+    lib.backlite_mask.restype = I
+    lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, P, P, P, Z, P]
+    lib.backlite_bwd.restype = I
+    lib.backlite_status_string.argtypes = [I]
+    lib.backlite_status_string.restype = ctypes.c_char_p
+    lib.backlite_last_error.argtypes = []
+    lib.backlite_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def lib():
+    return _load()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        L = _load()
+        raise BackliteError(f"{what} failed: {L.backlite_status_string(rc).decode()} "
+                            f"({L.backlite_last_error().decode()})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def ntiles(n: int) -> int:
+    return (n + TILE - 1) // TILE
+
+
+def tile_lse_elems(B, H, n, causal) -> int:
+    return int(_load().backlite_tile_lse_elems(B, H, n, 1 if causal else 0))
+
+
+def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_residual=False):
+    """O, lse_row [B,H,n] fp32, tile_lse (flat fp32 or None); with
+    with_residual=True a fourth value, O_lo (bf16 rounding residual of O)."""
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, n, Hk, d))
+    _need(v, "v", torch.bfloat16, (B, n, Hk, d))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    olo = torch.empty_like(q) if with_residual else None
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=q.device)
+    if with_stats and tile_lse is None:
+        tile_lse = torch.empty(tile_lse_elems(B, H, n, causal), dtype=torch.float32, device=q.device)
+    if tile_lse is not None:
+        _need(tile_lse, "tile_lse", torch.float32, (tile_lse_elems(B, H, n, causal),))
+    rc = _load().backlite_fwd(_ptr(q), _ptr(k), _ptr(v), B, n, H, Hk, d, scale, int(causal),
+                              _ptr(o), _ptr(olo), _ptr(lse), _ptr(tile_lse), _stream(q.device))
+    _check(rc, "backlite_fwd")
+    if with_residual:
+        return o, lse, tile_lse, olo
+    return o, lse, tile_lse
+
+
+def mask(tile_lse, lse, n, causal, negl_prob, stats=None):
+    """keep [B,H,T,T] u8, qcnt [B,H,T] i32, qidx [B,H,T,T] i16 (uint16 bits), kcnt, kidx."""
+    B, H, nn = lse.shape
+    assert nn == n
+    _need(lse, "lse", torch.float32)
+    if tile_lse is not None:
+        _need(tile_lse, "tile_lse", torch.float32, (tile_lse_elems(B, H, n, causal),))
+    T = ntiles(n)
+    dev = lse.device
+    out = {
+        "keep": torch.empty((B, H, T, T), dtype=torch.uint8, device=dev),
+        "qcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
+        "qidx": torch.empty((B, H, T, T), dtype=torch.int16, device=dev),
+        "kcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
+        "kidx": torch.empty((B, H, T, T), dtype=torch.int16, device=dev),
+    }
+    if stats is not None:
+        _need(stats, "stats", torch.int64, (2,))
+    rc = _load().backlite_mask(_ptr(tile_lse), _ptr(lse), B, H, n, int(causal), float(negl_prob),
+                               _ptr(out["keep"]), _ptr(out["qcnt"]), _ptr(out["qidx"]),
+                               _ptr(out["kcnt"]), _ptr(out["kidx"]), _ptr(stats), _stream(dev))
+    _check(rc, "backlite_mask")
+    return out
+
+
+def bwd_workspace_bytes(B, H, Hk, n, d) -> int:
+    return int(_load().backlite_bwd_workspace_bytes(B, H, Hk, n, d))
+
+
+def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, out=None, o_lo=None):
+    """G_Q, G_K, G_V (bf16) for the tile set in `lists` (qcnt/qidx/kcnt/kidx).
+    o_lo: the forward's residual output (recommended; D then uses O + O_lo)."""
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    for name, t, shp in (("q", q, (B, n, H, d)), ("k", k, (B, n, Hk, d)), ("v", v, (B, n, Hk, d)),
+                         ("o", o, (B, n, H, d)), ("do", do, (B, n, H, d))):
+        _need(t, name, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (B, H, n))
+    if o_lo is not None:
+        _need(o_lo, "o_lo", torch.bfloat16, (B, n, H, d))
+    T = ntiles(n)
+    _need(lists["qcnt"], "qcnt", torch.int32, (B, H, T))
+    _need(lists["kcnt"], "kcnt", torch.int32, (B, H, T))
+    _need(lists["qidx"], "qidx", torch.int16, (B, H, T, T))
+    _need(lists["kidx"], "kidx", torch.int16, (B, H, T, T))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    need = bwd_workspace_bytes(B, H, Hk, n, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    rc = _load().backlite_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
+                              _ptr(lists["qcnt"]), _ptr(lists["qidx"]), _ptr(lists["kcnt"]),
+                              _ptr(lists["kidx"]), B, n, H, Hk, d, scale, int(causal),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                              _stream(q.device))
+    _check(rc, "backlite_bwd")
+    return dq, dk, dv

@@ -1,0 +1,90 @@
+"""The BackLite attention module: exact forward, block-sparse backward.
+
+Mirrors the interface the BackLite README describes ("Usage"):
+``BackLite(negl_prob=0.05)`` is called as ``attn(query, key, value, scale=None,
+return_softmax_lse=False, tile_stats=None)`` on (batch, seq_len, heads,
+head_dim) bf16 tensors, with ``key``/``value`` carrying ``heads_k <= heads``.
+With ``negl_prob > 0`` the forward records the tile statistics in
+``tile_stats`` (allocated here unless the caller passes one) and hands them to
+the backward, which builds the tile mask and skips the masked tiles; with
+``negl_prob == 0`` no statistics are recorded and the backward is dense.  A
+``causal`` flag is added (the pages' LLM use is causal).
+
+Every step runs in the HIP library through ``_lib``; torch supplies device
+memory, streams and autograd plumbing only.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import torch
+
+from . import _lib
+
+
+class _BackLiteFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal, negl_prob, tile_stats, stats_out):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse, tl, olo = _lib.fwd(q, k, v, scale=scale, causal=causal, with_stats=negl_prob > 0,
+                                   tile_lse=tile_stats if negl_prob > 0 else None, with_residual=True)
+        ctx.save_for_backward(q, k, v, o, olo, lse)
+        ctx.tl = tl
+        ctx.scale, ctx.causal, ctx.negl = scale, causal, negl_prob
+        ctx.stats_out = stats_out
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, olo, lse = ctx.saved_tensors
+        n = q.shape[1]
+        lists = _lib.mask(ctx.tl, lse, n, ctx.causal, ctx.negl, stats=ctx.stats_out)
+        dq, dk, dv = _lib.bwd(q, k, v, o, do.contiguous(), lse, lists, scale=ctx.scale,
+                              causal=ctx.causal, o_lo=olo)
+        ctx.tl = None
+        return dq, dk, dv, None, None, None, None, None
+
+
+class BackLite(torch.nn.Module):
+    """Attention with an exact forward and a block-sparse backward.
+
+    negl_prob: tiles are skipped in the backward, smallest weight first, while
+    their cumulative weight stays below this value (0 = dense backward).
+    """
+
+    def __init__(self, negl_prob: float = 0.05, causal: bool = False):
+        super().__init__()
+        if not (0.0 <= negl_prob < 1.0) or math.isnan(negl_prob):
+            raise ValueError("negl_prob must be in [0, 1)")
+        self.negl_prob = float(negl_prob)
+        self.causal = bool(causal)
+        self.verbose = os.environ.get("BACKLITE_VERBOSE", "0") not in ("", "0")
+        self.last_stats = None
+
+    def forward(self, query, key, value, scale=None, return_softmax_lse=False, tile_stats=None,
+                causal=None):
+        causal = self.causal if causal is None else bool(causal)
+        d = query.shape[-1]
+        scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        stats = None
+        if self.verbose:
+            stats = torch.zeros(2, dtype=torch.int64, device=query.device)
+            self.last_stats = stats
+        o, lse = _BackLiteFn.apply(query, key, value, scale, causal, self.negl_prob, tile_stats, stats)
+        if return_softmax_lse:
+            return o, lse
+        return o
+
+    def extra_repr(self) -> str:
+        return f"negl_prob={self.negl_prob}, causal={self.causal}"
+
+
+def sparsity(stats: torch.Tensor) -> float:
+    """1 - kept / candidate tile pairs from a stats buffer filled by the mask."""
+    s = stats.tolist()
+    return 1.0 - s[1] / s[0] if s[0] else 0.0
+
+
+__all__ = ["BackLite", "sparsity"]

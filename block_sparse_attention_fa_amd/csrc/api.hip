@@ -1,0 +1,228 @@
+// C ABI of the BackLite hot path: argument validation, sizes, error strings,
+// and dispatch to the HIP kernels.  Declarations and the contract of every
+// entry point are in include/backlite.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/backlite.h"
+
+namespace backlite {
+hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int n, int H,
+                      int Hk, int d, float scale, int causal, uint16_t* o, uint16_t* olo, float* lse,
+                      float* tlse, hipStream_t st);
+hipError_t launch_mask(const float* tlse, const float* lse, int B, int H, int n, int causal,
+                       double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
+                       uint16_t* kidx, int64_t* stats, hipStream_t st);
+hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                      const uint16_t* olo, const uint16_t* dout, const float* lse, const int32_t* qcnt,
+                      const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
+                      int H, int Hk, int d, float scale, int causal, uint16_t* dq, uint16_t* dk,
+                      uint16_t* dv, float* dbuf, float* kbar, hipStream_t st);
+}  // namespace backlite
+
+namespace {
+
+constexpr int kTile = 128;
+constexpr int kMaxN = 131072;  // 1024 tiles: the mask kernel's LDS sort capacity
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return BACKLITE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ntiles(int n) { return (n + kTile - 1) / kTile; }
+
+// Shape checks shared by fwd and bwd.  Sizes must keep every element index of
+// the largest tensor below 2^62 and the grid below 2^31 workgroups.
+int check_shape(int B, int n, int H, int Hk, int d) {
+  if (B < 1 || n < 1 || H < 1 || Hk < 1)
+    return fail(BACKLITE_ERR_INVALID_ARG, "B, n, H, H_k must be >= 1 (got B=%d n=%d H=%d H_k=%d)", B, n,
+                H, Hk);
+  if (H % Hk != 0) return fail(BACKLITE_ERR_INVALID_ARG, "H (%d) must be a multiple of H_k (%d)", H, Hk);
+  if (n > kMaxN) return fail(BACKLITE_ERR_UNSUPPORTED, "n = %d exceeds the supported maximum %d", n, kMaxN);
+  if (d != 64 && d != 128) return fail(BACKLITE_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d);
+  if ((long long)B * H * ntiles(n) > 0x7fffffffLL)
+    return fail(BACKLITE_ERR_INVALID_ARG, "B*H*ceil(n/128) exceeds 2^31");
+  return BACKLITE_OK;
+}
+
+int check_ptr(const void* p, const char* name, bool allow_null = false) {
+  if (p == nullptr) {
+    if (allow_null) return BACKLITE_OK;
+    return fail(BACKLITE_ERR_INVALID_ARG, "%s is NULL", name);
+  }
+  if (!aligned16(p)) return fail(BACKLITE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return BACKLITE_OK;
+}
+
+int check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(BACKLITE_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+  return BACKLITE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BACKLITE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define TRY(x)                        \
+  do {                                \
+    int _r = (x);                     \
+    if (_r != BACKLITE_OK) return _r; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t backlite_tile_lse_elems(int B, int H, int n, int causal) {
+  if (B < 1 || H < 1 || n < 1) return 0;
+  const size_t T = (size_t)ntiles(n);
+  const size_t pairs = causal ? T * (T + 1) / 2 : T * T;
+  return (size_t)B * H * pairs * kTile;
+}
+
+size_t backlite_mask_elems(int B, int H, int n) {
+  if (B < 1 || H < 1 || n < 1) return 0;
+  const size_t T = (size_t)ntiles(n);
+  return (size_t)B * H * T * T;
+}
+
+size_t backlite_count_elems(int B, int H, int n) {
+  if (B < 1 || H < 1 || n < 1) return 0;
+  return (size_t)B * H * ntiles(n);
+}
+
+namespace {
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+size_t delta_bytes(int B, int H, int n) { return round256((size_t)B * H * n * sizeof(float)); }
+}  // namespace
+
+size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d) {
+  if (B < 1 || H < 1 || H_k < 1 || n < 1 || d < 1) return 0;
+  return delta_bytes(B, H, n) + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
+}
+
+int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int n, int H,
+                 int H_k, int d, float scale, int causal, uint16_t* O, uint16_t* O_lo,
+                 float* lse_row, float* tile_lse, void* stream) {
+  TRY(check_shape(B, n, H, H_k, d));
+  TRY(check_scale(scale));
+  TRY(check_ptr(Q, "Q"));
+  TRY(check_ptr(K, "K"));
+  TRY(check_ptr(V, "V"));
+  TRY(check_ptr(O, "O"));
+  TRY(check_ptr(O_lo, "O_lo", true));
+  TRY(check_ptr(lse_row, "lse_row"));
+  TRY(check_ptr(tile_lse, "tile_lse", true));
+  return hip_status(backlite::launch_fwd(Q, K, V, B, n, H, H_k, d, scale, causal ? 1 : 0, O, O_lo,
+                                         lse_row, tile_lse, (hipStream_t)stream),
+                    "backlite_fwd launch");
+}
+
+int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int n, int causal,
+                  float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
+                  uint16_t* kidx, int64_t* stats, void* stream) {
+  if (B < 1 || n < 1 || H < 1)
+    return fail(BACKLITE_ERR_INVALID_ARG, "B, n, H must be >= 1 (got B=%d n=%d H=%d)", B, n, H);
+  if (n > kMaxN) return fail(BACKLITE_ERR_UNSUPPORTED, "n = %d exceeds the supported maximum %d", n, kMaxN);
+  if ((long long)B * H * ntiles(n) > 0x7fffffffLL)
+    return fail(BACKLITE_ERR_INVALID_ARG, "B*H*ceil(n/128) exceeds 2^31");
+  if (!std::isfinite(negl_prob) || negl_prob < 0.f || negl_prob >= 1.f)
+    return fail(BACKLITE_ERR_INVALID_ARG, "negl_prob must be finite and in [0, 1) (got %g)",
+                (double)negl_prob);
+  if (tile_lse == nullptr && negl_prob != 0.f)
+    return fail(BACKLITE_ERR_INVALID_ARG, "tile_lse may be NULL only with negl_prob == 0");
+  TRY(check_ptr(tile_lse, "tile_lse", true));
+  TRY(check_ptr(lse_row, "lse_row"));
+  TRY(check_ptr(keep, "keep"));
+  TRY(check_ptr(qcnt, "qcnt"));
+  TRY(check_ptr(qidx, "qidx"));
+  TRY(check_ptr(kcnt, "kcnt"));
+  TRY(check_ptr(kidx, "kidx"));
+  TRY(check_ptr(stats, "stats", true));
+  hipError_t e = backlite::launch_mask(tile_lse, lse_row, B, H, n, causal ? 1 : 0, (double)negl_prob,
+                                       keep, qcnt, qidx, kcnt, kidx, stats, (hipStream_t)stream);
+  int r = hip_status(e, "backlite_mask launch");
+  if (r == BACKLITE_OK && stats) {
+    const char* env = std::getenv("BACKLITE_VERBOSE");
+    if (env && env[0] && env[0] != '0') {
+      long long hs[2] = {0, 0};
+      e = hipMemcpyAsync(hs, stats, sizeof(hs), hipMemcpyDeviceToHost, (hipStream_t)stream);
+      if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+      if (e != hipSuccess) return hip_status(e, "BACKLITE_VERBOSE stats readback");
+      std::fprintf(stderr,
+                   "[backlite] mask B=%d H=%d n=%d causal=%d negl_prob=%g: candidate tiles %lld, kept %lld, "
+                   "sparsity %.4f (accumulated)\n",
+                   B, H, n, causal ? 1 : 0, (double)negl_prob, hs[0], hs[1],
+                   hs[0] ? 1.0 - (double)hs[1] / (double)hs[0] : 0.0);
+    }
+  }
+  return r;
+}
+
+int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
+                 const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt, const uint16_t* qidx,
+                 const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k, int d,
+                 float scale, int causal, uint16_t* dQ, uint16_t* dK, uint16_t* dV, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  TRY(check_shape(B, n, H, H_k, d));
+  TRY(check_scale(scale));
+  TRY(check_ptr(Q, "Q"));
+  TRY(check_ptr(K, "K"));
+  TRY(check_ptr(V, "V"));
+  TRY(check_ptr(O, "O"));
+  TRY(check_ptr(O_lo, "O_lo", true));
+  TRY(check_ptr(dO, "dO"));
+  TRY(check_ptr(lse_row, "lse_row"));
+  TRY(check_ptr(qcnt, "qcnt"));
+  TRY(check_ptr(qidx, "qidx"));
+  TRY(check_ptr(kcnt, "kcnt"));
+  TRY(check_ptr(kidx, "kidx"));
+  TRY(check_ptr(dQ, "dQ"));
+  TRY(check_ptr(dK, "dK"));
+  TRY(check_ptr(dV, "dV"));
+  const size_t need = backlite_bwd_workspace_bytes(B, H, H_k, n, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(BACKLITE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  TRY(check_ptr(workspace, "workspace"));
+  return hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d,
+                                         scale, causal ? 1 : 0, dQ, dK, dV, (float*)workspace,
+                                         (float*)((char*)workspace + delta_bytes(B, H, n)),
+                                         (hipStream_t)stream),
+                    "backlite_bwd launch");
+}
+
+const char* backlite_status_string(int status) {
+  switch (status) {
+    case BACKLITE_OK: return "ok";
+    case BACKLITE_ERR_INVALID_ARG: return "invalid argument";
+    case BACKLITE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BACKLITE_ERR_WORKSPACE: return "workspace too small";
+    case BACKLITE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* backlite_last_error(void) { return g_err; }
+
+}  // extern "C"

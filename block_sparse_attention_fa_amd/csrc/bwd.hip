@@ -1,0 +1,436 @@
+// Block-sparse attention backward: D preprocess, G_K/G_V pass, G_Q pass.
+//
+// What it computes ("Introducing BackLite", backward equations and "Using
+// Sparsity"; BackLite README, "How It Works"): with P rebuilt from Q, K and the
+// stored row LSE (FlashAttention tutorial, "Flash Attention Backward Pass"),
+//   D = rowsum(G_O * O)                 (full row, once, before the tiles)
+//   G_V += P^T G_O,  G_P = G_O V^T,  G_S = P * (G_P - D),
+//   G_K += scale * G_S^T Q,  G_Q += scale * G_S K
+// over the kept tile pairs only; skipped tiles are never loaded.
+//
+// dkdv_kernel: one workgroup per (b, kv head g, key tile kt); wave w owns keys
+//   32w .. 32w+31 and keeps their K, V fragments and G_K, G_V accumulators in
+//   registers while it walks, for every query head of the group, that head's
+//   list of kept query tiles.  Per query tile, Q and G_O sit row-major in LDS;
+//   S = Q K^T and G_P = G_O V^T read them as row operands, G_V and G_K read them
+//   through the LDS transpose read.
+// dq_kernel: one workgroup per (b, h, query tile qt); wave w owns 32 query rows
+//   (Q, G_O fragments and the G_Q^T accumulator in registers) and walks the
+//   tile's list of kept key tiles with K, V row-major in LDS.
+// Both passes are free of atomics, so results are bit-reproducible.
+#include "bl_device.h"
+
+namespace backlite {
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* olo;  // optional bf16 residual of O (O_fp32 ~ O + olo)
+  const uint16_t* dout;
+  const float* lse;
+  const int32_t* qcnt;
+  const uint16_t* qidx;
+  const int32_t* kcnt;
+  const uint16_t* kidx;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dbuf;  // D, [B, H, n]
+  float* kbar;  // per key tile mean of K over its valid keys, [B, Hk, T, d]
+  int B, n, H, Hk, T;
+  float scale;
+  float scale_log2;
+};
+
+// ---------------------------------------------------------------------------
+// D[b,h,i] = sum_c G_O[b,i,h,c] * O[b,i,h,c]; 16 lanes per (i, h) row of d = 128
+// (8 lanes for d = 64), one 16-byte load of each operand per lane.  With the
+// forward's residual, O is taken as O + O_lo (about 16 significant bits): an
+// error in D shifts a whole row of G_S, whose row sum should vanish, and G_Q
+// then picks up that shift times the mean key vector.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const long rows = (long)a.B * a.n * a.H;
+  const long row = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(a.o + row * D + sub * 8);
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(a.dout + row * D + sub * 8);
+    const bf16x8 o8 = __builtin_bit_cast(bf16x8, ov);
+    const bf16x8 g8 = __builtin_bit_cast(bf16x8, gv);
+    float of[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) of[u] = (float)o8[u];
+    if (a.olo) {
+      const bf16x8 r8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.olo + row * D + sub * 8));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) of[u] += (float)r8[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = fmaf(of[u], (float)g8[u], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < rows && sub == 0) {
+    // row = (b*n + i)*H + h  ->  D[(b*H + h)*n + i]
+    const int h = (int)(row % a.H);
+    const long bi = row / a.H;
+    const int i = (int)(bi % a.n);
+    const int b = (int)(bi / a.n);
+    a.dbuf[((long)b * a.H + h) * a.n + i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// kbar[b,g,kt,:] = mean of K over the valid keys of tile kt (fp32).  Used by the
+// G_Q pass to compensate the bf16 rounding of G_S (see dq_kernel).  One
+// workgroup per (b, g, kt); thread t sums rows t/(D/8) + 256/(D/8)*i of the
+// 8-column chunk t%(D/8), then the partial sums meet in LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void kmean_kernel(BwdArgs a) {
+  constexpr int CH = D / 8;
+  constexpr int RSTEP = 256 / CH;
+  __shared__ float part[RSTEP][D];
+  const int T = a.T, n = a.n;
+  const int kt = blockIdx.x % T;
+  const int bg = blockIdx.x / T;
+  const int g = bg % a.Hk, b = bg / a.Hk;
+  const int tid = threadIdx.x, ch = tid % CH, r0 = tid / CH;
+  const long stride = (long)a.Hk * D;
+  const uint16_t* kp = a.k + ((long)b * n + (long)kt * TILE) * stride + (long)g * D + ch * 8;
+  const int nv = min(TILE, n - kt * TILE);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = r0; r < nv; r += RSTEP) {
+    const bf16x8 v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + (long)r * stride));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += (float)v[u];
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) part[r0][ch * 8 + u] = acc[u];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < RSTEP; ++i) s += part[i][tid];
+    a.kbar[((long)bg * T + kt) * D + tid] = s / (float)nv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// G_K, G_V
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
+  constexpr int NT = 256;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Gs[TILE * D];
+  __shared__ __attribute__((aligned(16))) float Ls[TILE];  // LSE in scaled log2 units
+  __shared__ __attribute__((aligned(16))) float Ds[TILE];
+
+  const int T = a.T, n = a.n;
+  const int total = a.B * a.Hk * T;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int kt = L % T;
+  const int bg = L / T;
+  const int g = bg % a.Hk, b = bg / a.Hk;
+  const int G = a.H / a.Hk;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int key = kt * TILE + wave * 32 + l32;  // this lane's key (B-operand column)
+
+  const long kvstride = (long)a.Hk * D;
+  bf16x8 kf[NKS], vf[NKS];
+  {
+    const long base = ((long)b * n) * kvstride + (long)g * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (key < n) {
+        kv = *reinterpret_cast<const u32x4*>(a.k + base + (long)key * kvstride + ks * 16 + h32 * 8);
+        vv = *reinterpret_cast<const u32x4*>(a.v + base + (long)key * kvstride + ks * 16 + h32 * 8);
+      }
+      kf[ks] = __builtin_bit_cast(bf16x8, kv);
+      vf[ks] = __builtin_bit_cast(bf16x8, vv);
+    }
+  }
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+  const float c = a.scale_log2;
+  const long qstride = (long)a.H * D;
+
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    const long bh = (long)b * a.H + h;
+    const int cnt = a.kcnt[bh * T + kt];
+    const uint16_t* list = a.kidx + (bh * T + kt) * T;
+    const uint16_t* qbase = a.q + ((long)b * n) * qstride + (long)h * D;
+    const uint16_t* gbase = a.dout + ((long)b * n) * qstride + (long)h * D;
+    for (int it = 0; it < cnt; ++it) {
+      const int qt = list[it];
+      const int q0 = qt * TILE;
+      __syncthreads();
+      load_tile<D, NT>(Qs, qbase + (long)q0 * qstride, qstride, n - q0, tid);
+      load_tile<D, NT>(Gs, gbase + (long)q0 * qstride, qstride, n - q0, tid);
+      if (tid < TILE) {
+        const int i = q0 + tid;
+        Ls[tid] = (i < n) ? a.lse[bh * n + i] * LOG2E : INFINITY;
+        Ds[tid] = (i < n) ? a.dbuf[bh * n + i] : 0.f;
+      }
+      __syncthreads();
+      const bool diag = CAUSAL && (qt == kt);
+#pragma unroll
+      for (int qc = 0; qc < 4; ++qc) {
+        // S and G_P for queries 32qc + (C rows), keys of this wave (C column)
+        f32x16 s = f32x16{}, gp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          s = mfma32(lds_row8<D>(Qs, qc * 32 + l32, 2 * ks + h32), kf[ks], s);
+          gp = mfma32(lds_row8<D>(Gs, qc * 32 + l32, 2 * ks + h32), vf[ks], gp);
+        }
+        f32x16 p, ds;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qr = qc * 32 + 8 * j + 4 * h32;  // local query row of registers 4j..4j+3
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qr);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qr);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = 4 * j + t;
+            float pv = exp2f(fmaf(s[r], c, -l4[t]));
+            if (diag && key > q0 + qr + t) pv = 0.f;
+            p[r] = pv;
+            ds[r] = pv * (gp[r] - d4[t]);
+          }
+        }
+        // G_V += P^T G_O and G_K += G_S^T Q; step st covers queries
+        // 32qc + 16st + 4*h32 + 0..3 and 32qc + 16st + 8 + 4*h32 + 0..3
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 pa = pack8(p, st);
+          const bf16x8 sa = pack8(ds, st);
+          const int k0 = qc * 32 + st * 16 + 4 * h32;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
+            const bf16x8 gb = cat8(lds_tr4<D>(Gs, k0, n0, lane), lds_tr4<D>(Gs, k0 + 8, n0, lane));
+            dv[db] = mfma32(pa, gb, dv[db]);
+            const bf16x8 qb = cat8(lds_tr4<D>(Qs, k0, n0, lane), lds_tr4<D>(Qs, k0 + 8, n0, lane));
+            dk[db] = mfma32(sa, qb, dk[db]);
+          }
+        }
+      }
+    }
+  }
+
+  // epilogue: C layout is [key = 8(r/4) + 4*h32 + r%4 of the wave][dim = 32db + l32];
+  // stage through LDS as [key][dim] and store coalesced rows.
+  __syncthreads();
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = wave * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      const int dim = db * 32 + l32;
+      const int off = tile_off<D>(kr, dim >> 3) + (dim & 7);
+      Qs[off] = (bf16)(dk[db][r] * a.scale);
+      Gs[off] = (bf16)dv[db][r];
+    }
+  __syncthreads();
+  {
+    constexpr int CH = D / 8;
+    const long base = ((long)b * n + (long)kt * TILE) * kvstride + (long)g * D;
+#pragma unroll
+    for (int it = 0; it < TILE * CH / NT; ++it) {
+      const int cc = tid + it * NT;
+      const int row = cc / CH, ch = cc % CH;
+      if (kt * TILE + row < n) {
+        *reinterpret_cast<u32x4*>(a.dk + base + (long)row * kvstride + ch * 8) =
+            *reinterpret_cast<const u32x4*>(Qs + tile_off<D>(row, ch));
+        *reinterpret_cast<u32x4*>(a.dv + base + (long)row * kvstride + ch * 8) =
+            *reinterpret_cast<const u32x4*>(Gs + tile_off<D>(row, ch));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// G_Q
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
+  constexpr int NT = 256;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[TILE * D];
+  __shared__ __attribute__((aligned(16))) float Kb[D];
+
+  const int T = a.T, n = a.n;
+  const int total = a.B * a.H * T;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int qt = L % T;
+  const int bh = L / T;
+  const int h = bh % a.H, b = bh / a.H;
+  const int g = h / (a.H / a.Hk);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int qrow = qt * TILE + wave * 32 + l32;
+
+  const long qstride = (long)a.H * D;
+  bf16x8 qf[NKS], gf[NKS];
+  {
+    const long base = ((long)b * n) * qstride + (long)h * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
+      if (qrow < n) {
+        qv = *reinterpret_cast<const u32x4*>(a.q + base + (long)qrow * qstride + ks * 16 + h32 * 8);
+        gv = *reinterpret_cast<const u32x4*>(a.dout + base + (long)qrow * qstride + ks * 16 + h32 * 8);
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8, qv);
+      gf[ks] = __builtin_bit_cast(bf16x8, gv);
+    }
+  }
+  const float lse2 = (qrow < n) ? a.lse[(long)bh * n + qrow] * LOG2E : INFINITY;
+  const float dl = (qrow < n) ? a.dbuf[(long)bh * n + qrow] : 0.f;
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
+  const float c = a.scale_log2;
+  const long kvstride = (long)a.Hk * D;
+  const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
+  const uint16_t* vbase = a.v + ((long)b * n) * kvstride + (long)g * D;
+  const int cnt = a.qcnt[(long)bh * T + qt];
+  const uint16_t* list = a.qidx + ((long)bh * T + qt) * T;
+
+  for (int it = 0; it < cnt; ++it) {
+    const int kt = list[it];
+    const int key0 = kt * TILE;
+    __syncthreads();
+    load_tile<D, NT>(Ks, kbase + (long)key0 * kvstride, kvstride, n - key0, tid);
+    load_tile<D, NT>(Vs, vbase + (long)key0 * kvstride, kvstride, n - key0, tid);
+    if (tid < D) Kb[tid] = a.kbar[((long)(b * a.Hk + g) * T + kt) * D + tid];
+    __syncthreads();
+    const bool diag = CAUSAL && (qt == kt);
+    const bool edge = key0 + TILE > n;
+    float losum = 0.f;  // sum over this tile's keys of (G_S - bf16(G_S)) for this row
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x16 s = f32x16{}, gp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = mfma32(lds_row8<D>(Ks, kb * 32 + l32, 2 * ks + h32), qf[ks], s);
+        gp = mfma32(lds_row8<D>(Vs, kb * 32 + l32, 2 * ks + h32), gf[ks], gp);
+      }
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2f(fmaf(s[r], c, -lse2));
+        if (diag || edge) {
+          const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          if (kk >= n || (diag && kk > qrow)) pv = 0.f;
+        }
+        ds[r] = pv * (gp[r] - dl);
+      }
+      // G_Q^T += K^T G_S^T; step st covers keys 32kb + 16st + 4*h32 + 0..3 and +8
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 sb = pack8_lo(ds, st, losum);
+        const int k0 = kb * 32 + st * 16 + 4 * h32;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
+          const bf16x8 ka = cat8(lds_tr4<D>(Ks, k0, n0, lane), lds_tr4<D>(Ks, k0 + 8, n0, lane));
+          dq[db] = mfma32(ka, sb, dq[db]);
+        }
+      }
+    }
+    // Rounding compensation.  The MFMA used bf16(G_S); the residual
+    // lo = G_S - bf16(G_S) contributes sum_j lo_ij K_j, whose dominant part when
+    // the tile's keys share a large common vector is (sum_j lo_ij) * kbar.  Rows
+    // of G_S nearly sum to zero, so without this term that common vector would
+    // multiply the rounding error.  Exact algebra: the leftover error is
+    // sum_j lo_ij (K_j - kbar).
+    losum += __shfl_xor(losum, 32);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 kb4 = *reinterpret_cast<const f32x4*>(Kb + db * 32 + 8 * j + 4 * h32);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dq[db][4 * j + t] = fmaf(losum, kb4[t], dq[db][4 * j + t]);
+      }
+  }
+
+  // epilogue: dq C layout is [dim = 32db + 8(r/4) + 4*h32 + r%4][query l32]
+  __syncthreads();
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dim = db * 32 + 8 * j + 4 * h32;
+      const int row = wave * 32 + l32;
+      bf16x4 w4 = {(bf16)(dq[db][4 * j] * a.scale), (bf16)(dq[db][4 * j + 1] * a.scale),
+                   (bf16)(dq[db][4 * j + 2] * a.scale), (bf16)(dq[db][4 * j + 3] * a.scale)};
+      *reinterpret_cast<bf16x4*>(Ks + tile_off<D>(row, dim >> 3) + (dim & 7)) = w4;
+    }
+  __syncthreads();
+  {
+    constexpr int CH = D / 8;
+    uint16_t* op = a.dq + ((long)b * n + (long)qt * TILE) * qstride + (long)h * D;
+#pragma unroll
+    for (int it = 0; it < TILE * CH / NT; ++it) {
+      const int cc = tid + it * NT;
+      const int row = cc / CH, ch = cc % CH;
+      if (qt * TILE + row < n)
+        *reinterpret_cast<u32x4*>(op + (long)row * qstride + ch * 8) =
+            *reinterpret_cast<const u32x4*>(Ks + tile_off<D>(row, ch));
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  {
+    const long rows = (long)a.B * a.n * a.H;
+    const long rpb = 256 / (D / 8);
+    hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((kmean_kernel<D>), dim3(a.B * a.Hk * a.T), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(a.B * a.Hk * a.T), dim3(256), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(a.B * a.H * a.T), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                      const uint16_t* olo, const uint16_t* dout, const float* lse, const int32_t* qcnt,
+                      const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
+                      int H, int Hk, int d, float scale, int causal, uint16_t* dq, uint16_t* dk,
+                      uint16_t* dv, float* dbuf, float* kbar, hipStream_t st) {
+  BwdArgs a{q,  k,  v,    o,    olo, dout, lse, qcnt, qidx, kcnt, kidx, dq,
+            dk, dv, dbuf, kbar, B,   n,    H,   Hk,   (n + TILE - 1) / TILE, scale, scale * LOG2E};
+  if (d == 64) return causal ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
+  return causal ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
+}
+
+}  // namespace backlite

@@ -1,0 +1,216 @@
+// Attention forward with per-(query row, key tile) log-sum-exp statistics.
+//
+// What it computes ("Introducing BackLite", "Backpropagation for attention";
+// BackLite README, "How It Works", phase 1): S = scale * Q K^T with the causal
+// rule j <= i when requested, P = row softmax(S), O = P V, the row LSE, and for
+// every (row i, key tile kt) the LSE of row i restricted to tile kt.
+//
+// Method: single pass over key tiles with the online (running-max) softmax of
+// the FlashAttention tutorial ("Online Softmax", "Flash Attention"), in base 2
+// with scale*log2(e) folded into the exponent.  The tile statistic reuses the
+// tile's rescaled row sum: LSE_tile = m_run + log2(sum_j 2^(s_j - m_run)), with
+// m_run the running maximum after the tile, so it costs one log per row per
+// tile.
+//
+// Work decomposition (gfx950): one workgroup of 4 waves per (b, h, query tile);
+// wave w owns 32 query rows.  S^T = K Q^T is formed with 32x32x16 bf16 MFMA
+// (K from LDS as the A operand, the wave's Q fragment resident in registers as
+// B), so each lane holds one query row and the row reductions stay in-lane
+// plus one exchange between the two lane halves.  O^T += V^T P^T takes P^T
+// straight from the S^T accumulators and V^T from the row-major V tile with the
+// LDS transpose read.
+#include "bl_device.h"
+
+namespace backlite {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  uint16_t* olo;  // optional: bf16 rounding residual of O
+  float* lse;
+  float* tlse;
+  int B, n, H, Hk, T;
+  float scale_log2;  // scale * log2(e)
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+  constexpr int NT = 256;
+  constexpr int NKS = D / 16;  // MFMA k-steps over the head dimension
+  constexpr int NDB = D / 32;  // 32-wide blocks of the head dimension
+  __shared__ __attribute__((aligned(16))) bf16 Ks[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[TILE * D];
+
+  const int total = a.B * a.H * a.T;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int T = a.T;
+  int qt = L % T;
+  if (CAUSAL) qt = T - 1 - qt;  // heaviest query tiles first
+  const int bh = L / T;
+  const int h = bh % a.H, b = bh / a.H;
+  const int g = h / (a.H / a.Hk);
+  const int n = a.n;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int qrow = qt * TILE + wave * 32 + l32;  // this lane's query row
+
+  // Q fragment (B operand of S^T = K Q^T): dims 16ks + 8*h32 + 0..7 of row qrow
+  bf16x8 qf[NKS];
+  {
+    const long qstride = (long)a.H * D;
+    const uint16_t* qp = a.q + ((long)b * n) * qstride + (long)h * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qrow < n) v = *reinterpret_cast<const u32x4*>(qp + (long)qrow * qstride + ks * 16 + h32 * 8);
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY;  // running max, in scaled log2 units
+  float l_run = 0.f;
+
+  const long kvstride = (long)a.Hk * D;
+  const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
+  const uint16_t* vbase = a.v + ((long)b * n) * kvstride + (long)g * D;
+  const int nkt = CAUSAL ? qt + 1 : T;
+  float* tl_row = nullptr;
+  if (a.tlse) {
+    const long pairs = CAUSAL ? (long)T * (T + 1) / 2 : (long)T * T;
+    tl_row = a.tlse + (long)bh * pairs * TILE;
+  }
+  const float c = a.scale_log2;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int key0 = kt * TILE;
+    __syncthreads();
+    load_tile<D, NT>(Ks, kbase + (long)key0 * kvstride, kvstride, n - key0, tid);
+    load_tile<D, NT>(Vs, vbase + (long)key0 * kvstride, kvstride, n - key0, tid);
+    __syncthreads();
+
+    // S^T for the 4 key blocks of 32
+    f32x16 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        s[kb] = mfma32(lds_row8<D>(Ks, kb * 32 + l32, 2 * ks + h32), qf[ks], s[kb]);
+    }
+    // mask padded keys (last tile) and, on the diagonal tile, keys after the row
+    const bool need_mask = (key0 + TILE > n) || (CAUSAL && kt == qt);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          const bool bad = (key >= n) || (CAUSAL && key > qrow);
+          s[kb][r] = bad ? -INFINITY : s[kb][r];
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt * c);
+    const float alpha = exp2f(m_run - m_new);
+    float ts = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(fmaf(s[kb][r], c, -m_new));
+        s[kb][r] = p;
+        ts += p;
+      }
+    ts += __shfl_xor(ts, 32);
+    l_run = l_run * alpha + ts;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    if (tl_row && h32 == 0) {
+      const float t = (qrow < n) ? (m_new + __log2f(ts)) * LN2 : -INFINITY;
+      tl_row[pair_index(qt, kt, T, CAUSAL) * TILE + wave * 32 + l32] = t;
+    }
+    // O^T += V^T P^T.  Step s of key block kb covers keys 32kb + 16s + 4*h32 + 0..3
+    // and 32kb + 16s + 8 + 4*h32 + 0..3, i.e. C registers 8s .. 8s+7.
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 pb = pack8(s[kb], st);
+        const int k0 = kb * 32 + st * 16 + 4 * h32;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
+          const bf16x8 va = cat8(lds_tr4<D>(Vs, k0, n0, lane), lds_tr4<D>(Vs, k0 + 8, n0, lane));
+          oacc[db] = mfma32(va, pb, oacc[db]);
+        }
+      }
+  }
+
+  // epilogue: normalise, stage O through LDS as [row][dim], store coalesced
+  const float inv = 1.f / l_run;
+  __syncthreads();
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dim = db * 32 + 8 * j + 4 * h32;
+      const int row = wave * 32 + l32;
+      bf16x4 w4, r4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float f = oacc[db][4 * j + t] * inv;
+        w4[t] = (bf16)f;
+        r4[t] = (bf16)(f - (float)w4[t]);
+      }
+      *reinterpret_cast<bf16x4*>(Ks + tile_off<D>(row, dim >> 3) + (dim & 7)) = w4;
+      *reinterpret_cast<bf16x4*>(Vs + tile_off<D>(row, dim >> 3) + (dim & 7)) = r4;
+    }
+  if (h32 == 0 && qrow < n) a.lse[(long)bh * n + qrow] = (m_run + __log2f(l_run)) * LN2;
+  __syncthreads();
+  {
+    constexpr int CH = D / 8;
+    const long ostride = (long)a.H * D;
+    const long obase = ((long)b * n + (long)qt * TILE) * ostride + (long)h * D;
+#pragma unroll
+    for (int it = 0; it < TILE * CH / NT; ++it) {
+      const int cc = tid + it * NT;
+      const int row = cc / CH, ch = cc % CH;
+      if (qt * TILE + row < n) {
+        *reinterpret_cast<u32x4*>(a.o + obase + (long)row * ostride + ch * 8) =
+            *reinterpret_cast<const u32x4*>(Ks + tile_off<D>(row, ch));
+        if (a.olo)
+          *reinterpret_cast<u32x4*>(a.olo + obase + (long)row * ostride + ch * 8) =
+              *reinterpret_cast<const u32x4*>(Vs + tile_off<D>(row, ch));
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  const int total = a.B * a.H * a.T;
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int n, int H,
+                      int Hk, int d, float scale, int causal, uint16_t* o, uint16_t* olo, float* lse,
+                      float* tlse, hipStream_t st) {
+  FwdArgs a{q, k, v, o, olo, lse, tlse, B, n, H, Hk, (n + TILE - 1) / TILE, scale * LOG2E};
+  if (d == 64) return causal ? launch_fwd_t<64, true>(a, st) : launch_fwd_t<64, false>(a, st);
+  return causal ? launch_fwd_t<128, true>(a, st) : launch_fwd_t<128, false>(a, st);
+}
+
+}  // namespace backlite

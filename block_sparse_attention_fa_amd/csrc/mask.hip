@@ -1,0 +1,215 @@
+// Mask from tile statistics: tile weights -> smallest-first cumulative cut ->
+// keep bitmap and compacted work lists.
+//
+// What it computes (BackLite README, "How It Works", phase 2, and "Overview";
+// "Introducing BackLite", "Using Sparsity"): for each query tile, the tile
+// probability p_tile = exp(LSE_tile - LSE_row) of each candidate key tile,
+// aggregated over the query tile's rows by the maximum; the candidates with the
+// smallest weights are skipped while their cumulative weight stays below
+// negl_prob.
+//
+// select_kernel: one workgroup per (b, h, qt).
+//   1. a[kt] = max_r (tile_lse[qt,kt,r] - lse_row[r]) in fp64: eight 32-lane
+//      groups each take one key tile at a time, a lane reads 4 rows (one
+//      16-byte load per lane, 512 contiguous bytes per tile).
+//   2. bitonic sort of (a, kt) in LDS, ascending, ties by kt.
+//   3. one lane walks the sorted list adding exp(a) in fp64 left to right and
+//      stops at the first running sum >= negl_prob; everything before is
+//      skipped (the walk visits only the skipped prefix plus one).
+//   4. keep row and the ascending q-list (block-wide prefix count).
+// transpose_kernel: one workgroup per (b, h, kt) turns column kt of the keep
+// bitmap into the ascending k-list.
+#include "bl_device.h"
+
+namespace backlite {
+
+constexpr int MASK_NT = 256;
+constexpr int MAX_T = 1024;  // n <= 131072
+
+// Exclusive prefix sum of one int per thread over the 256-thread block.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < MASK_NT / 64; ++w) {
+    const int r = red[w];
+    if (w < wave) base += r;
+    total += r;
+  }
+  __syncthreads();
+  return base + x - v;
+}
+
+struct MaskArgs {
+  const float* tlse;
+  const float* lse;
+  uint8_t* keep;
+  int32_t* qcnt;
+  uint16_t* qidx;
+  int32_t* kcnt;
+  uint16_t* kidx;
+  unsigned long long* stats;
+  int B, H, n, T, causal;
+  double negl;
+};
+
+__global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
+  __shared__ double sa[MAX_T];
+  __shared__ int sk[MAX_T];
+  __shared__ uint8_t flag[MAX_T];
+  __shared__ int red[MASK_NT / 64];
+  __shared__ int s_skip;
+
+  const int T = a.T;
+  const int total = a.B * a.H * T;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int qt = L % T;
+  const int bh = L / T;
+  const int tid = threadIdx.x;
+  const int nc = a.causal ? qt + 1 : T;  // candidates are kt = 0 .. nc-1
+  int P2 = 1;
+  while (P2 < nc) P2 <<= 1;
+
+  for (int i = tid; i < T; i += MASK_NT) flag[i] = 0;
+
+  if (a.tlse != nullptr) {
+    // ---- 1. log-weights
+    const int grp = tid >> 5, gl = tid & 31;
+    const int r0 = qt * TILE + gl * 4;
+    double ls[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ls[u] = (r0 + u < a.n) ? (double)a.lse[(long)bh * a.n + r0 + u] : 0.0;
+    const long pairs = a.causal ? (long)T * (T + 1) / 2 : (long)T * T;
+    const float* tl = a.tlse + (long)bh * pairs * TILE;
+    for (int kt = grp; kt < nc; kt += MASK_NT / 32) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(tl + pair_index(qt, kt, T, a.causal) * TILE + gl * 4);
+      double m = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (r0 + u < a.n) m = fmax(m, (double)v[u] - ls[u]);
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 32));
+      if (gl == 0) {
+        sa[kt] = m;
+        sk[kt] = kt;
+      }
+    }
+    for (int i = nc + tid; i < P2; i += MASK_NT) {
+      sa[i] = INFINITY;
+      sk[i] = 0x7fffffff;
+    }
+    __syncthreads();
+    // ---- 2. bitonic sort ascending by (a, kt)
+    for (int kk = 2; kk <= P2; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P2 / 2; i += MASK_NT) {
+          const int lo = 2 * j * (i / j) + (i % j);
+          const int hi = lo + j;
+          const bool up = ((lo & kk) == 0);
+          const double alo = sa[lo], ahi = sa[hi];
+          const int klo = sk[lo], khi = sk[hi];
+          const bool gt = (alo > ahi) || (alo == ahi && klo > khi);
+          if (gt == up) {
+            sa[lo] = ahi;
+            sa[hi] = alo;
+            sk[lo] = khi;
+            sk[hi] = klo;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // ---- 3. sequential fp64 prefix, stop at the first sum >= negl_prob
+    if (tid == 0) {
+      double acc = 0.0;
+      int r = 0;
+      for (; r < nc; ++r) {
+        acc += exp(sa[r]);
+        if (!(acc < a.negl)) break;
+      }
+      s_skip = r;
+    }
+    __syncthreads();
+    const int skip = s_skip;
+    for (int r = skip + tid; r < nc; r += MASK_NT) flag[sk[r]] = 1;
+  } else {
+    for (int i = tid; i < nc; i += MASK_NT) flag[i] = 1;
+  }
+  __syncthreads();
+
+  // ---- 4. keep row + ascending q-list
+  uint8_t* keep_row = a.keep + ((long)bh * T + qt) * T;
+  for (int i = tid; i < T; i += MASK_NT) keep_row[i] = flag[i];
+  constexpr int PER = MAX_T / MASK_NT;  // 4 consecutive kt per thread
+  int f[PER], cnt = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int kt = tid * PER + u;
+    f[u] = (kt < T) ? flag[kt] : 0;
+    cnt += f[u];
+  }
+  int tot;
+  int pos = block_exclusive_scan(cnt, red, tot);
+  uint16_t* qrow = a.qidx + ((long)bh * T + qt) * T;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (f[u]) qrow[pos++] = (uint16_t)(tid * PER + u);
+  if (tid == 0) {
+    a.qcnt[(long)bh * T + qt] = tot;
+    if (a.stats) {
+      atomicAdd(&a.stats[0], (unsigned long long)nc);
+      atomicAdd(&a.stats[1], (unsigned long long)tot);
+    }
+  }
+}
+
+__global__ __launch_bounds__(MASK_NT) void mask_transpose_kernel(MaskArgs a) {
+  __shared__ int red[MASK_NT / 64];
+  const int T = a.T;
+  const int total = a.B * a.H * T;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int kt = L % T;
+  const int bh = L / T;
+  const int tid = threadIdx.x;
+  constexpr int PER = MAX_T / MASK_NT;
+  const uint8_t* col = a.keep + (long)bh * T * T + kt;
+  int f[PER], cnt = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int qt = tid * PER + u;
+    f[u] = (qt < T) ? col[(long)qt * T] : 0;
+    cnt += f[u];
+  }
+  int tot;
+  int pos = block_exclusive_scan(cnt, red, tot);
+  uint16_t* krow = a.kidx + ((long)bh * T + kt) * T;
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (f[u]) krow[pos++] = (uint16_t)(tid * PER + u);
+  if (tid == 0) a.kcnt[(long)bh * T + kt] = tot;
+}
+
+hipError_t launch_mask(const float* tlse, const float* lse, int B, int H, int n, int causal,
+                       double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
+                       uint16_t* kidx, int64_t* stats, hipStream_t st) {
+  const int T = (n + TILE - 1) / TILE;
+  MaskArgs a{tlse, lse, keep, qcnt, qidx, kcnt, kidx, reinterpret_cast<unsigned long long*>(stats),
+             B, H, n, T, causal, negl};
+  const int total = B * H * T;
+  hipLaunchKernelGGL(mask_select_kernel, dim3(total), dim3(MASK_NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mask_transpose_kernel, dim3(total), dim3(MASK_NT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace backlite

@@ -1,0 +1,158 @@
+/*
+ * backlite.h — C ABI of the BackLite attention hot path for AMD MI355X (gfx950).
+ *
+ * BackLite ("Introducing BackLite: Attention Backpropagation Acceleration Using
+ * Dynamic Sparsity", section "Using Sparsity"; BackLite README, "How It Works /
+ * Sparse Backward Masking") runs an exact attention forward that also records
+ * softmax statistics per tile, turns those statistics into a block-sparse tile
+ * mask, and runs the attention backward over the kept tiles only.  This library
+ * exposes the three stages as separate calls:
+ *
+ *   backlite_fwd   Q,K,V            -> O, LSE_row, tile_LSE
+ *   backlite_mask  tile_LSE,LSE_row -> keep bitmap + per-tile work lists
+ *   backlite_bwd   Q,K,V,O,G_O,LSE_row, lists -> G_Q, G_K, G_V
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *    never allocates device memory and holds no state between calls; every
+ *    call is re-entrant.  Inputs are never written.
+ *  - bf16 tensors are passed as uint16_t bit patterns.  Q, O, G_O, G_Q are
+ *    [B, n, H, d] and K, V, G_K, G_V are [B, n, H_k, d], contiguous, d
+ *    fastest (the README's (batch, seq_len, heads, head_dim) layout).
+ *  - Query head h reads key/value head h / (H / H_k) (grouped-query attention,
+ *    README "Usage": key/value carry heads_k <= heads).
+ *  - Tiles are 128 query rows x 128 keys; T = ceil(n / 128).
+ *  - All launches are asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Argument validation is synchronous: a call that fails
+ *    validation returns an error code and launches nothing.
+ *  - Pointers must be non-NULL (except where stated) and 16-byte aligned.
+ *  - Return value: BACKLITE_OK or a negative backlite_status.  The detail of
+ *    the last failure on the calling thread is in backlite_last_error().
+ *  - NaN/Inf inside tensors are not checked; they propagate.
+ */
+#ifndef BACKLITE_H
+#define BACKLITE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BACKLITE_OK = 0,
+  BACKLITE_ERR_INVALID_ARG = -1, /* a size, pointer, scale or probability is out of range */
+  BACKLITE_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim not 64 or 128) */
+  BACKLITE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than backlite_bwd_workspace_bytes */
+  BACKLITE_ERR_HIP = -4          /* a HIP launch failed; hipError string in backlite_last_error() */
+} backlite_status;
+
+/* Number of float elements of the tile-LSE buffer backlite_fwd writes.
+ * Layout: for each (b, h), one block of 128 floats per candidate tile pair
+ * (qt, kt); float r of a block is the log-sum-exp of row 128*qt + r over the
+ * keys of tile kt.  Non-causal: pair index qt*T + kt (T*T pairs).  Causal:
+ * only pairs kt <= qt exist, pair index qt*(qt+1)/2 + kt (T*(T+1)/2 pairs).
+ * Returns 0 for invalid sizes. */
+size_t backlite_tile_lse_elems(int B, int H, int n, int causal);
+
+/* Number of elements of each [B, H, T, T] mask array (keep, qidx, kidx). */
+size_t backlite_mask_elems(int B, int H, int n);
+
+/* Number of int32 elements of each [B, H, T] count array (qcnt, kcnt). */
+size_t backlite_count_elems(int B, int H, int n);
+
+/* Bytes of device workspace backlite_bwd needs: the per-row D = rowsum(G_O*O)
+ * values in fp32 [B, H, n], then the per-key-tile mean of K in fp32
+ * [B, H_k, T, d], each part rounded up to 256 bytes.  0 for invalid sizes. */
+size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d);
+
+/* Forward: exact attention plus per-(row, key tile) statistics.
+ *
+ * ("Introducing BackLite", "Backpropagation for attention": S = scale*Q K^T,
+ * P = row softmax(S), O = P V; README phase 1: the forward records the
+ * log-sum-exp of every (query tile, key tile) alongside O and the full-row
+ * LSE.)  Causal: key j is visible to query i iff j <= i.
+ *
+ *   Q [B,n,H,d], K, V [B,n,H_k,d] bf16 in; scale > 0 and finite (the usual
+ *   choice is 1/sqrt(d)); causal 0/1.
+ *   O [B,n,H,d] bf16 out.
+ *   O_lo [B,n,H,d] bf16 out, optional (may be NULL): the rounding residual
+ *     bf16(O_fp32 - O) of the output, so that O + O_lo carries about 16
+ *     significant bits.  backlite_bwd uses it for D = rowsum(G_O * O): an error
+ *     in D shifts a whole row of G_S (whose row sum should vanish) and G_Q then
+ *     picks up that shift times the keys' mean vector, which bf16 O alone makes
+ *     visible (about 1% relative on keys with a large shared component).
+ *   lse_row [B,H,n] fp32 out: natural-log LSE of each row of scale*Q K^T.
+ *   tile_lse: fp32 out, backlite_tile_lse_elems() floats (layout above), the
+ *     natural-log LSE of each row over one key tile.  Rows >= n of the last
+ *     query tile are written as -inf.  May be NULL: then no statistics are
+ *     written (the negl_prob = 0 dense mode).
+ * Requires B, n, H, H_k >= 1, H % H_k == 0, d in {64, 128}. */
+int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                 int B, int n, int H, int H_k, int d, float scale, int causal,
+                 uint16_t* O, uint16_t* O_lo, float* lse_row, float* tile_lse, void* stream);
+
+/* Mask from statistics (README phase 2; "Using Sparsity").
+ *
+ * For every (b, h, query tile qt) and candidate key tile kt (all kt, or
+ * kt <= qt when causal):
+ *   a(qt,kt) = max over valid rows i of tile qt of (tile_lse[i,kt] - lse_row[i]),
+ *              computed in fp64 from the fp32 inputs; the tile weight is
+ *              w = exp(a) = the largest p_tile = exp(LSE_tile - LSE_row) of the
+ *              tile's rows;
+ *   candidates are ordered by (a ascending, kt ascending); w is summed in fp64
+ *   in that order, left to right; every tile whose running sum is still
+ *   < negl_prob is skipped, every other candidate is kept.
+ * Outputs (all written in full for every (b, h, tile)):
+ *   keep [B,H,T,T] uint8: 1 = tile (qt, kt) is computed by the backward.
+ *   qcnt [B,H,T] int32, qidx [B,H,T,T] uint16: for query tile qt, its kept key
+ *     tiles in ascending order in qidx[..., qt, 0:qcnt]; the rest of the row is
+ *     left unspecified.
+ *   kcnt, kidx: the same per key tile kt (kept query tiles, ascending).
+ *   stats: optional (may be NULL) int64[2], ACCUMULATED into (not cleared):
+ *     [0] += candidate tile pairs, [1] += kept tile pairs.
+ * tile_lse may be NULL only with negl_prob == 0 (every candidate is kept).
+ * negl_prob must be finite and in [0, 1); with negl_prob <= 1 every query tile
+ * keeps at least one key tile. */
+int backlite_mask(const float* tile_lse, const float* lse_row,
+                  int B, int H, int n, int causal, float negl_prob,
+                  uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
+                  int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream);
+
+/* Block-sparse backward ("Introducing BackLite", backward equations and
+ * "Using Sparsity"; README "How It Works": skipped tiles cost no loads and no
+ * FLOPs):
+ *   D = rowsum(G_O * O) over the full row, with O + O_lo when O_lo (the
+ *     forward's optional residual output) is given, else O alone;
+ *   for every kept tile pair: P = exp(scale*Q K^T - LSE_row) (causal-masked),
+ *   G_V += P^T G_O, G_P = G_O V^T, G_S = P * (G_P - D),
+ *   G_Q += scale * G_S K, G_K += scale * G_S^T Q.
+ * Tiles absent from the lists contribute nothing.  G_K / G_V of a key/value
+ * head sum over its query heads.  Every element of dQ, dK, dV is written (key
+ * rows no list reaches get zeros).
+ *   qcnt/qidx drive G_Q (per query tile); kcnt/kidx drive G_K, G_V (per key
+ *   tile); both must describe the same tile set (as backlite_mask writes them).
+ *   workspace: device buffer of at least backlite_bwd_workspace_bytes(); its
+ *   contents on entry are ignored.
+ * The result is deterministic (no atomics): repeated calls give identical bits. */
+int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                 const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
+                 const int32_t* qcnt, const uint16_t* qidx,
+                 const int32_t* kcnt, const uint16_t* kidx,
+                 int B, int n, int H, int H_k, int d, float scale, int causal,
+                 uint16_t* dQ, uint16_t* dK, uint16_t* dV,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* backlite_status_string(int status);
+
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char* backlite_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BACKLITE_H */

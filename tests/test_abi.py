@@ -1,0 +1,91 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, reports sizes, and rejects bad arguments before launching
+anything (validation never touches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "backlite.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_sparse_attention_fa_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libbacklite.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(backlite_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for nm in names:
+        assert hasattr(L, nm), f"{nm} not exported"
+
+
+def test_sizes(L):
+    assert L.backlite_tile_lse_elems(1, 2, 1024, 0) == 2 * 64 * 128
+    assert L.backlite_tile_lse_elems(1, 1, 300, 1) == 6 * 128          # T = 3 -> 6 pairs
+    assert L.backlite_tile_lse_elems(1, 40, 75600, 0) == 40 * 591 * 591 * 128
+    assert L.backlite_mask_elems(2, 3, 129) == 2 * 3 * 4
+    assert L.backlite_count_elems(2, 3, 129) == 2 * 3 * 2
+    # D: 1*2*100 floats = 800 B -> 1024; kbar: 1*2*1*64 floats = 512 B
+    assert L.backlite_bwd_workspace_bytes(1, 2, 2, 100, 64) == 1024 + 512
+    assert L.backlite_tile_lse_elems(0, 1, 1, 0) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced
+MIS = ctypes.c_void_p((1 << 20) + 2)     # misaligned
+
+
+def _fwd(L, B=1, n=128, H=2, Hk=2, d=64, scale=0.125, q=FAKE, tl=FAKE):
+    return L.backlite_fwd(q, FAKE, FAKE, B, n, H, Hk, d, scale, 0, FAKE, None, FAKE, tl, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=3, Hk=2), -1), (dict(n=0), -1), (dict(B=0), -1), (dict(d=96), -2), (dict(d=256), -2),
+    (dict(n=131073), -2), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
+    (dict(scale=float("inf")), -1), (dict(q=None), -1), (dict(q=MIS), -1), (dict(tl=MIS), -1),
+])
+def test_fwd_validation(L, kw, code):
+    assert _fwd(L, **kw) == code
+    assert L.backlite_last_error()
+
+
+def _mask(L, negl=0.05, tl=FAKE, keep=FAKE, n=256):
+    return L.backlite_mask(tl, FAKE, 1, 2, n, 0, negl, keep, FAKE, FAKE, FAKE, FAKE, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(negl=-0.1), -1), (dict(negl=1.0), -1), (dict(negl=float("nan")), -1),
+    (dict(tl=None), -1), (dict(keep=None), -1), (dict(keep=MIS), -1), (dict(n=0), -1),
+])
+def test_mask_validation(L, kw, code):
+    assert _mask(L, **kw) == code
+
+
+def test_bwd_validation(L):
+    args = [FAKE] * 11 + [1, 256, 4, 2, 128, 0.1, 0, FAKE, FAKE, FAKE]
+    # workspace too small / missing
+    assert L.backlite_bwd(*args, FAKE, 16, None) == -3
+    assert L.backlite_bwd(*args, None, 1 << 20, None) == -3
+    bad = list(args)
+    bad[14] = 3                                   # H_k does not divide H
+    assert L.backlite_bwd(*bad, FAKE, 1 << 20, None) == -1
+    bad = list(args)
+    bad[15] = 80                                  # head_dim
+    assert L.backlite_bwd(*bad, FAKE, 1 << 20, None) == -2
+
+
+def test_status_strings(L):
+    for c in (0, -1, -2, -3, -4):
+        assert L.backlite_status_string(c)

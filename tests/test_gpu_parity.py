@@ -1,0 +1,201 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on small
+seeded cases that span several tiles, ragged tails, causal masking, GQA, both
+head sizes and batch > 1.  GPU only."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import (assert_close_grad, assert_close_out, check_lists, excused_mismatches,
+                     flush_print, gpu_available, lists_to_torch, packed_to_rows, rows_to_packed)
+from oracle import backlite_oracle as orc
+from workloads import TINY, make_inputs, small
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    TINY,
+    small(1000, H=4, Hk=2, d=128, causal=True, kind="blocks", seed=1),
+    small(300, H=2, Hk=1, d=64, causal=False, kind="gaussian", seed=2),
+    small(129, H=1, d=128, causal=True, kind="gaussian", seed=3),
+    small(1, H=2, Hk=1, d=64, causal=False, seed=4),
+    small(640, H=2, d=128, causal=False, kind="blocks", B=2, seed=5),
+    small(383, H=3, Hk=1, d=128, causal=False, kind="gaussian", seed=6),
+]
+IDS = [w.name for w in CASES]
+NEGL = 0.05
+
+_cache = {}
+
+
+def _setup(w):
+    if w.name in _cache:
+        return _cache[w.name]
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_fa_amd as bl
+    flush_print(f"[case] {w.name}")
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+    xg = {k: v.to(dev) for k, v in x.items()}
+    ref = orc.forward(x["q"], x["k"], x["v"], causal=w.causal)
+    o, lse, tl, olo = bl.fwd(xg["q"], xg["k"], xg["v"], causal=w.causal, with_residual=True)
+    torch.cuda.synchronize()
+    r = dict(w=w, x=x, xg=xg, ref=ref, o=o, olo=olo, lse=lse, tl=tl, bl=bl, dev=dev)
+    _cache[w.name] = r
+    return r
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_forward_outputs(w):
+    r = _setup(w)
+    assert_close_out("O", r["o"].cpu(), r["ref"]["O"])
+    assert_close_out("lse", r["lse"].cpu(), r["ref"]["lse"])
+    # O_lo is the rounding residual of the fp32 output: at most half a bf16 ulp
+    # of O, and O + O_lo is closer to the exact output than O alone
+    o1 = orc.to_f64(r["o"].cpu())
+    lo = orc.to_f64(r["olo"].cpu())
+    half_ulp = np.where(o1 != 0, 2.0 ** (np.floor(np.log2(np.abs(np.where(o1 != 0, o1, 1.0)))) - 8), 2.0 ** -133)
+    assert (np.abs(lo) <= half_ulp).all()
+    if w.n > 1:
+        assert orc.rel_l2(o1 + lo, r["ref"]["O"]) < orc.rel_l2(o1, r["ref"]["O"])
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_forward_tile_lse(w):
+    r = _setup(w)
+    B, H, n = w.B, w.H, w.n
+    got = packed_to_rows(r["tl"].cpu().numpy(), B, H, n, w.causal)
+    ref = r["ref"]["tile_lse"]
+    cand = orc.candidates(n, w.causal)
+    T = cand.shape[0]
+    # compare where the tile carries non-negligible probability (fp32 range)
+    lse = r["ref"]["lse"][..., None]
+    sel = np.isfinite(ref) & (ref - lse > -60.0)
+    assert_close_out("tile_lse", got[sel], ref[sel])
+    # every row of a candidate tile sees at least one key: no NaN anywhere
+    rows = np.arange(n)
+    for kt in range(T):
+        c = cand[rows // 128, kt]
+        assert not np.isnan(got[:, :, c, kt]).any()
+    # identity on the GPU's own output: logsumexp_kt tile_lse = lse_row
+    g = np.where(np.isfinite(got), got, -np.inf)
+    m = g.max(-1, keepdims=True)
+    lse_tiles = (m + np.log(np.exp(g - m).sum(-1, keepdims=True)))[..., 0]
+    np.testing.assert_allclose(lse_tiles, r["lse"].cpu().numpy(), atol=2e-5, rtol=0)
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_mask_same_inputs_bit_exact(w):
+    """Selection logic alone: the oracle's tile statistics, rounded to fp32, go
+    into the library's mask call; keep bitmap and lists must equal the oracle's
+    selection on those same fp32 values, bit for bit."""
+    r = _setup(w)
+    bl, dev = r["bl"], r["dev"]
+    B, H, n = w.B, w.H, w.n
+    tl32 = rows_to_packed(r["ref"]["tile_lse"], B, H, n, w.causal)
+    lse32 = r["ref"]["lse"].astype(np.float32)
+    for negl in (0.0, 0.01, NEGL, 0.3, 0.9):
+        m = bl.mask(torch.from_numpy(tl32).to(dev), torch.from_numpy(lse32).to(dev), n, w.causal, negl)
+        keep_ref = orc.mask_from_stats(packed_to_rows(tl32, B, H, n, w.causal), lse32, n, w.causal,
+                                       np.float64(np.float32(negl)))
+        check_lists(m, keep_ref)
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_mask_end_to_end(w):
+    """GPU forward statistics -> GPU mask versus the oracle's own statistics and
+    selection: equal except tiles within 1e-6 of the cut (reported)."""
+    r = _setup(w)
+    bl = r["bl"]
+    n = w.n
+    cand = orc.candidates(n, w.causal)
+    a_ref = orc.tile_log_weights(r["ref"]["tile_lse"], r["ref"]["lse"], n, w.causal)
+    for negl in (0.01, NEGL, 0.1):
+        m = bl.mask(r["tl"], r["lse"], n, w.causal, negl)
+        keep_ref = orc.select_keep(a_ref, cand, negl)
+        keep = m["keep"].cpu().numpy().astype(bool)
+        bad, exc = excused_mismatches(keep, keep_ref, a_ref, cand, negl)
+        flush_print(f"  negl={negl}: kept {keep.sum()}/{keep_ref.sum()} ref, excused {len(exc)}")
+        assert not bad, f"unexcused mask mismatches {bad[:5]}"
+        check_lists(m, keep)
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_backward_on_oracle_mask(w):
+    r = _setup(w)
+    bl, dev, x, xg = r["bl"], r["dev"], r["x"], r["xg"]
+    keep = orc.mask_from_stats(r["ref"]["tile_lse"], r["ref"]["lse"], w.n, w.causal, NEGL)
+    lists = lists_to_torch(keep, dev)
+    dq, dk, dv = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], lists, causal=w.causal,
+                        o_lo=r["olo"])
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal)
+    for name, got, ref in (("dQ", dq, g["dQ"]), ("dK", dk, g["dK"]), ("dV", dv, g["dV"])):
+        rl, cs = assert_close_grad(name, got.cpu(), ref)
+        flush_print(f"  {name}: rel-L2 {rl:.2e} cos {cs:.6f}")
+
+
+@pytest.mark.parametrize("w", CASES, ids=IDS)
+def test_backward_dense(w):
+    """negl_prob = 0 without statistics: every candidate tile, dense gradients."""
+    r = _setup(w)
+    bl, x, xg = r["bl"], r["x"], r["xg"]
+    m = bl.mask(None, r["lse"], w.n, w.causal, 0.0)
+    check_lists(m, np.broadcast_to(orc.candidates(w.n, w.causal), (w.B, w.H) + (m["keep"].shape[-1],) * 2))
+    dq, dk, dv = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=w.causal,
+                        o_lo=r["olo"])
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], causal=w.causal)
+    for name, got, ref in (("dQ", dq, g["dQ"]), ("dK", dk, g["dK"]), ("dV", dv, g["dV"])):
+        assert_close_grad(name, got.cpu(), ref)
+
+
+def test_backward_deterministic():
+    r = _setup(CASES[1])
+    bl, xg, w = r["bl"], r["xg"], r["w"]
+    m = bl.mask(r["tl"], r["lse"], w.n, w.causal, NEGL)
+    a = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=True, o_lo=r["olo"])
+    b = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=True, o_lo=r["olo"])
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+
+
+def test_module_autograd_matches_oracle():
+    """BackLite module: forward + loss.backward() against the oracle end to end."""
+    w = small(500, H=4, Hk=2, d=128, causal=True, kind="blocks", seed=7)
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_fa_amd as bl
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev).requires_grad_() for n in ("q", "k", "v"))
+    attn = bl.BackLite(negl_prob=NEGL, causal=True)
+    o, lse = attn(q, k, v, return_softmax_lse=True)
+    o.backward(x["do"].to(dev))
+    ref = orc.forward(x["q"], x["k"], x["v"], causal=True)
+    keep = orc.mask_from_stats(ref["tile_lse"], ref["lse"], w.n, True, NEGL)
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=True)
+    assert_close_out("O", o.detach().cpu(), ref["O"])
+    assert_close_out("lse", lse.cpu(), ref["lse"])
+    for name, got, rr in (("dQ", q.grad, g["dQ"]), ("dK", k.grad, g["dK"]), ("dV", v.grad, g["dV"])):
+        assert_close_grad(name, got.cpu(), rr)
+
+
+def test_backward_without_residual_gaussian():
+    """O_lo is optional: on inputs without a large shared key component the
+    bf16 O alone already meets the bound."""
+    r = _setup(CASES[2])
+    bl, x, xg, w = r["bl"], r["x"], r["xg"], r["w"]
+    keep = orc.mask_from_stats(r["ref"]["tile_lse"], r["ref"]["lse"], w.n, w.causal, NEGL)
+    dq, dk, dv = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], lists_to_torch(keep, r["dev"]),
+                        causal=w.causal)
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal)
+    for name, got, ref in (("dQ", dq, g["dQ"]), ("dK", dk, g["dK"]), ("dV", dv, g["dV"])):
+        assert_close_grad(name, got.cpu(), ref)
+
+
+def test_stats_counters():
+    r = _setup(CASES[0])
+    bl, w = r["bl"], r["w"]
+    st = torch.zeros(2, dtype=torch.int64, device=r["dev"])
+    m = bl.mask(r["tl"], r["lse"], w.n, w.causal, NEGL, stats=st)
+    s = st.cpu().tolist()
+    assert s[0] == w.B * w.H * 64 and s[1] == int(m["keep"].sum().item())
