@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the BackLite hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input resident in HBM:
+forward with tile statistics -> mask from statistics -> block-sparse backward.
+Default workload: the 32k-token video-DiT shape (B=1, H=40, n=32760 = 21x30x52
+latent grid, d=128, bf16, non-causal, negl_prob=0.05).
+
+Printed JSON line (rank 0): value = dense-equivalent backward throughput,
+10*d*B*H*n^2 FLOP / sparse-backward time, in TFLOP/s; plus forward, mask and
+backward ms, sparsity, the executed-tile MFMA fraction of the bf16 dense peak,
+the backward speedup over the same library's dense (negl_prob = 0) backward,
+the roofline of the dominant kernel from per-launch HIP events, and the fp64
+oracle timed on the host on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload dit-480p-32k]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse attn bwd ms + dense-equiv TFLOP/s & MFMA % peak, 32k DiT, negl_prob=0.05"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TILE = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dit-480p-32k")
+    ap.add_argument("--negl", type=float, default=None, help="negl_prob (default: the workload's first)")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-rows", type=int, default=12288,
+                    help="query rows of head 0 in the oracle's timed sample")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-backward comparison")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, x_h0, negl, rows):
+    """fp64 oracle on head 0, query rows [0, rows): forward, mask and backward of
+    those rows against all keys.  Rate = dense-equivalent backward FLOP of the
+    sample / the oracle's backward seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import backlite_oracle as orc
+    q, k, v, do = (orc.to_f64(x_h0[nm]) for nm in ("q", "k", "v", "do"))
+    n, d = w.n, w.d
+    rows = min(rows, n)
+    rr = np.arange(rows)
+    t0 = time.perf_counter()
+    f = orc.forward(q, k, v, causal=w.causal, rows=rr)
+    t1 = time.perf_counter()
+    # tile weights / selection on the sampled query tiles only
+    nt = (rows + TILE - 1) // TILE
+    tl = np.full((1, 1, n, f["tile_lse"].shape[-1]), -np.inf)
+    ls = np.zeros((1, 1, n))
+    tl[:, :, :rows] = f["tile_lse"]
+    ls[:, :, :rows] = f["lse"]
+    a = orc.tile_log_weights(tl, ls, n, w.causal)
+    cand = orc.candidates(n, w.causal).copy()
+    cand[nt:] = False                       # only the sampled query tiles
+    keep = orc.select_keep(a, cand, negl)
+    t2 = time.perf_counter()
+    orc.backward(q, k, v, do, keep=keep, causal=w.causal, q_rows=rr)
+    t3 = time.perf_counter()
+    # dense-equivalent: every (row, key) pair the causal rule allows
+    flops = 10.0 * d * (rows * (rows + 1) / 2 if w.causal else rows * n)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {
+        "value": flops / (t3 - t2) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent backward)",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"head 0, query rows 0-{rows - 1} of the {w.name} problem against all {n} keys, fp64 numpy: "
+                   f"forward {t1 - t0:.2f} s, mask {t2 - t1:.2f} s, backward {t3 - t2:.2f} s"),
+        "bwd_s": t3 - t2,
+        "fwd_s": t1 - t0,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the hot path shards by (batch, kv-head group) with no exchange, so multi-GPU runs are not "
+              "part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_fa_amd as bl
+    from block_sparse_attention_fa_amd import _lib
+    from workloads import ALL, make_inputs
+
+    w = ALL[args.workload]
+    negl = w.negl_probs[0] if args.negl is None else args.negl
+    B, H, Hk, n, d, causal = w.B, w.H, w.Hk, w.n, w.d, w.causal
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: B={B} H={H} H_k={Hk} n={n} d={d} causal={causal} negl_prob={negl}")
+    t = time.time()
+    x = make_inputs(w)
+    log(f"[bench] inputs generated in {time.time() - t:.1f} s")
+    x_h0 = {nm: x[nm][:, :, :1].contiguous() for nm in ("q", "do")}
+    x_h0.update({nm: x[nm][:, :, :1].contiguous() for nm in ("k", "v")})
+    q, k, v, do = (x[nm].to(dev) for nm in ("q", "k", "v", "do"))
+    del x
+    T = (n + TILE - 1) // TILE
+
+    # every buffer allocated once, outside the timed region
+    tl = torch.empty(_lib.tile_lse_elems(B, H, n, causal), dtype=torch.float32, device=dev)
+    stats = torch.zeros(2, dtype=torch.int64, device=dev)
+    ws = torch.empty(_lib.bwd_workspace_bytes(B, H, Hk, n, d), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(rec=None):
+        o, lse, _, olo = bl.fwd(q, k, v, causal=causal, tile_lse=tl, with_residual=True)
+        if rec is not None:
+            rec[0].record()
+        m = bl.mask(tl, lse, n, causal, negl, stats=stats)
+        if rec is not None:
+            rec[1].record()
+        bl.bwd(q, k, v, o, do, lse, m, causal=causal, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+        return o, lse, olo
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stats.zero_()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    _lib.profile_reset()
+    _lib.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(rec=(ev[i][1], ev[i][2]))
+        ev[i][3].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    prof = _lib.profile_read()
+    total_ms = start.elapsed_time(stop)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    mask_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    bwd_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    st = stats.cpu().tolist()
+    cand, kept = st[0] / args.steps, st[1] / args.steps
+    sparsity = 1.0 - kept / cand if cand else 0.0
+
+    # the same library's dense backward (negl_prob = 0: every candidate tile)
+    dense_ms = None
+    if not args.no_dense:
+        o, lse, olo = step()
+        md = bl.mask(None, lse, n, causal, 0.0)
+        for _ in range(max(1, args.warmup)):
+            bl.bwd(q, k, v, o, do, lse, md, causal=causal, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            bl.bwd(q, k, v, o, do, lse, md, causal=causal, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.steps
+
+    pairs_dense = (n * (n + 1) / 2) if causal else float(n) * n
+    f_dense_bwd = 10.0 * d * B * H * pairs_dense
+    f_fwd = 4.0 * d * B * H * pairs_dense
+    tile_bwd_flop = 10.0 * TILE * TILE * d
+    dense_equiv_tflops = f_dense_bwd / (bwd_ms * 1e-3) / 1e12
+    mfma_frac = kept * tile_bwd_flop / (bwd_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+
+    kms = {k_: (v_[0] / v_[1] if v_[1] else None) for k_, v_ in prof.items()}
+    # dominant kernel: dK/dV pass; algorithmic work = 4 of the 5 backward GEMMs
+    # (S, G_P, G_V, G_K) per executed tile = 8*128*128*d FLOP
+    dkdv_ms = kms.get("dkdv")
+    dkdv_flop = kept * 8.0 * TILE * TILE * d
+    achieved = dkdv_flop / (dkdv_ms * 1e-3) / 1e12 if dkdv_ms else None
+    roofline = {"kernel": "dkdv", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS if achieved else None, "traffic": None}
+
+    # mask algorithmic bytes: tile-LSE of every candidate pair (512 B), the row LSE
+    # and D-like row data of each query tile, bitmap + list entries written
+    mask_bytes = cand * 512 + B * H * n * 4 + B * H * T * T * 1 + kept * 2 * 2 + 2 * B * H * T * 4
+    delta_bytes = B * H * n * (4 * d + 4 + 2 * d)  # O, G_O, O_lo read; D written
+
+    out = {
+        "metric": METRIC,
+        "value": dense_equiv_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "H_k": Hk, "n": n, "d": d, "causal": causal,
+                   "negl_prob": negl, "tile": TILE},
+        "bwd_ms": bwd_ms,
+        "fwd_ms": fwd_ms,
+        "mask_ms": mask_ms,
+        "dense_bwd_ms": dense_ms,
+        "bwd_speedup_vs_dense": (dense_ms / bwd_ms) if dense_ms else None,
+        "sparsity": sparsity,
+        "executed_tiles_per_step": kept,
+        "candidate_tiles_per_step": cand,
+        "executed_tile_mfma_frac": mfma_frac,
+        "fwd_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
+        "fwd_mfma_frac": f_fwd / (fwd_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "kernel_avg_ms": kms,
+        "mask_gbs": (mask_bytes / ((kms["mask_select"] + kms["mask_transpose"]) * 1e-3) / 1e9)
+        if kms.get("mask_select") and kms.get("mask_transpose") else None,
+        "delta_gbs": delta_bytes / (kms["delta"] * 1e-3) / 1e9 if kms.get("delta") else None,
+        "wall_s_timed": wall,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    log(f"[bench] fwd {fwd_ms:.3f} ms  mask {mask_ms:.3f} ms  bwd {bwd_ms:.3f} ms  dense bwd "
+        f"{dense_ms if dense_ms is None else round(dense_ms, 3)} ms  sparsity {sparsity:.3f}  "
+        f"dense-equiv {dense_equiv_tflops:.1f} TFLOP/s  exec-tile MFMA {100 * mfma_frac:.1f}%")
+    if args.cpu_baseline == "on":
+        del q, k, v, do, tl, ws, dq, dk, dv
+        log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows of head 0 ...")
+        out["cpu_baseline"] = cpu_baseline(w, x_h0, negl, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -48,6 +48,13 @@ def _load():
     lib.backlite_mask.restype = I
     lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, P, P, P, Z, P]
     lib.backlite_bwd.restype = I
+    lib.backlite_profile_enable.argtypes = [I]
+    lib.backlite_profile_enable.restype = I
+    lib.backlite_profile_reset.argtypes = []
+    lib.backlite_profile_reset.restype = I
+    lib.backlite_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int64)]
+    lib.backlite_profile_read.restype = I
     lib.backlite_status_string.argtypes = [I]
     lib.backlite_status_string.restype = ctypes.c_char_p
     lib.backlite_last_error.argtypes = []
@@ -178,3 +185,25 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
                               _stream(q.device))
     _check(rc, "backlite_bwd")
     return dq, dk, dv
+
+
+PROFILE_KERNELS = ("fwd", "mask_select", "mask_transpose", "delta", "kmean", "dkdv", "dq")
+
+
+def profile_enable(on: bool = True):
+    _check(_load().backlite_profile_enable(1 if on else 0), "backlite_profile_enable")
+
+
+def profile_reset():
+    _check(_load().backlite_profile_reset(), "backlite_profile_reset")
+
+
+def profile_read() -> dict:
+    """{kernel: (total_ms, launches)} accumulated since the last reset."""
+    out = {}
+    L = _load()
+    for k in PROFILE_KERNELS:
+        ms, cnt = ctypes.c_double(0.0), ctypes.c_int64(0)
+        _check(L.backlite_profile_read(k.encode(), ctypes.byref(ms), ctypes.byref(cnt)), "backlite_profile_read")
+        out[k] = (ms.value, cnt.value)
+    return out

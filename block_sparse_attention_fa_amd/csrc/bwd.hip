@@ -19,6 +19,7 @@
 //   tile's list of kept key tiles with K, V row-major in LDS.
 // Both passes are free of atomics, so results are bit-reproducible.
 #include "bl_device.h"
+#include "prof.h"
 
 namespace backlite {
 
@@ -408,17 +409,27 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   {
     const long rows = (long)a.B * a.n * a.H;
     const long rpb = 256 / (D / 8);
+    ProfScope ps(PK_DELTA, st);
     hipLaunchKernelGGL((delta_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((kmean_kernel<D>), dim3(a.B * a.Hk * a.T), dim3(256), 0, st, a);
+  {
+    ProfScope ps(PK_KMEAN, st);
+    hipLaunchKernelGGL((kmean_kernel<D>), dim3(a.B * a.Hk * a.T), dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(a.B * a.Hk * a.T), dim3(256), 0, st, a);
+  {
+    ProfScope ps(PK_DKDV, st);
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(a.B * a.Hk * a.T), dim3(256), 0, st, a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(a.B * a.H * a.T), dim3(256), 0, st, a);
+  {
+    ProfScope ps(PK_DQ, st);
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(a.B * a.H * a.T), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

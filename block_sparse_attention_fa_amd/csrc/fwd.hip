@@ -20,6 +20,7 @@
 // straight from the S^T accumulators and V^T from the row-major V tile with the
 // LDS transpose read.
 #include "bl_device.h"
+#include "prof.h"
 
 namespace backlite {
 
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   const int total = a.B * a.H * a.T;
+  ProfScope ps(PK_FWD, st);
   hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -20,6 +20,7 @@
 // transpose_kernel: one workgroup per (b, h, kt) turns column kt of the keep
 // bitmap into the ascending k-list.
 #include "bl_device.h"
+#include "prof.h"
 
 namespace backlite {
 
@@ -205,10 +206,16 @@ hipError_t launch_mask(const float* tlse, const float* lse, int B, int H, int n,
   MaskArgs a{tlse, lse, keep, qcnt, qidx, kcnt, kidx, reinterpret_cast<unsigned long long*>(stats),
              B, H, n, T, causal, negl};
   const int total = B * H * T;
-  hipLaunchKernelGGL(mask_select_kernel, dim3(total), dim3(MASK_NT), 0, st, a);
+  {
+    ProfScope ps(PK_MASK_SELECT, st);
+    hipLaunchKernelGGL(mask_select_kernel, dim3(total), dim3(MASK_NT), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mask_transpose_kernel, dim3(total), dim3(MASK_NT), 0, st, a);
+  {
+    ProfScope ps(PK_MASK_TRANSPOSE, st);
+    hipLaunchKernelGGL(mask_transpose_kernel, dim3(total), dim3(MASK_NT), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -145,6 +145,18 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  uint16_t* dQ, uint16_t* dK, uint16_t* dV,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Per-kernel timing (opt-in).  While enabled, every kernel the library
+ * launches is bracketed by two hipEvents recorded on its launch stream.
+ * backlite_profile_read waits for the outstanding events and returns, for the
+ * named kernel, the accumulated elapsed time and the number of launches since
+ * the last reset.  Kernel names: "fwd", "mask_select", "mask_transpose",
+ * "delta", "kmean", "dkdv", "dq".  Process-wide state, thread-safe; enabling
+ * adds two event records per launch.  read returns BACKLITE_ERR_INVALID_ARG
+ * for an unknown name or NULL outputs, BACKLITE_ERR_HIP if an event failed. */
+int backlite_profile_enable(int on);
+int backlite_profile_reset(void);
+int backlite_profile_read(const char* kernel, double* total_ms, int64_t* launches);
+
 /* Static text for a status code. */
 const char* backlite_status_string(int status);
 
