@@ -102,6 +102,38 @@ __device__ __forceinline__ void load_tile(bf16* tile, const uint16_t* src, long 
   }
 }
 
+// Asynchronous copy of a full [128 x D] bf16 tile (every row valid) from global
+// memory into a swizzled LDS tile with global_load_lds_dwordx4: each wave
+// instruction fills 64 consecutive 16-byte LDS slots (slot = lane), so lane l
+// fetches the global chunk that belongs at its slot, i.e. the inverse swizzle.
+// Completion: s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
+template <int D, int NT>
+__device__ __forceinline__ void dma_tile(bf16* tile, const uint16_t* src, long stride, int tid) {
+  constexpr int CH = D / 8;
+  constexpr int NW = NT / 64;
+  constexpr int NI = TILE * CH / NT;  // instructions per thread
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot0 = (i * NW + wave) * 64;  // first slot of this wave instruction
+    const int s = slot0 + lane;
+    const int row = s / CH, pch = s % CH;
+    const uint16_t* g = src + (long)row * stride + ((pch ^ swz(row)) << 3);
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                     (__attribute__((address_space(3))) void*)(tile + slot0 * 8), 16, 0, 0);
+  }
+}
+
+// Asynchronous copy of n32 4-byte words (n32 a multiple of 64) into LDS by one
+// wave: lane l of instruction i lands word 64i + l.
+__device__ __forceinline__ void dma_words(float* lds, const float* src, int n32, int lane) {
+  for (int i = 0; i < n32 / 64; ++i)
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 64 * i + lane),
+                                     (__attribute__((address_space(3))) void*)(lds + 64 * i), 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // Map a hardware workgroup id to a logical work index so that consecutive
 // logical indices run on the same XCD (workgroups are dealt round-robin over
 // the 8 XCDs; each XCD has its own L2).

@@ -8,15 +8,12 @@
 //   G_K += scale * G_S^T Q,  G_Q += scale * G_S K
 // over the kept tile pairs only; skipped tiles are never loaded.
 //
-// dkdv_kernel: one workgroup per (b, kv head g, key tile kt); wave w owns keys
-//   32w .. 32w+31 and keeps their K, V fragments and G_K, G_V accumulators in
-//   registers while it walks, for every query head of the group, that head's
-//   list of kept query tiles.  Per query tile, Q and G_O sit row-major in LDS;
-//   S = Q K^T and G_P = G_O V^T read them as row operands, G_V and G_K read them
-//   through the LDS transpose read.
-// dq_kernel: one workgroup per (b, h, query tile qt); wave w owns 32 query rows
-//   (Q, G_O fragments and the G_Q^T accumulator in registers) and walks the
-//   tile's list of kept key tiles with K, V row-major in LDS.
+// dkdv_kernel: one workgroup per (b, kv head g, key tile kt) walks, for every
+//   query head of the group, that head's list of kept query tiles.  Per query
+//   tile, Q and G_O sit row-major in LDS; S = Q K^T and G_P = G_O V^T read them
+//   as row operands, G_V and G_K read them through the LDS transpose read.
+// dq_kernel: one workgroup per (b, h, query tile qt) walks the tile's list of
+//   kept key tiles with K, V row-major in LDS.
 // Both passes are free of atomics, so results are bit-reproducible.
 #include "bl_device.h"
 #include "prof.h"
@@ -126,15 +123,57 @@ __global__ __launch_bounds__(256) void kmean_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // G_K, G_V
 // ---------------------------------------------------------------------------
+// Work items of a (b, g, kt) workgroup: for each query head h of the group, the
+// kept query tiles of key tile kt in that head's k-list.
+struct KItems {
+  int hh, it, cnt;  // current head of the group, position in its list, list length
+};
+
+// Stage Q, G_O, LSE and D of query tile qt of head bh into LDS; asynchronously
+// for full tiles, synchronously (zero / +inf padding) for the ragged last one.
+template <int D, int NT>
+__device__ __forceinline__ void stage_qg(bf16* Qd, bf16* Gd, float* Ld, float* Dd, const BwdArgs& a,
+                                         long bh, int b, int h, int qt, int tid) {
+  const int n = a.n;
+  const long qstride = (long)a.H * D;
+  const int q0 = qt * TILE;
+  const uint16_t* qsrc = a.q + ((long)b * n + q0) * qstride + (long)h * D;
+  const uint16_t* gsrc = a.dout + ((long)b * n + q0) * qstride + (long)h * D;
+  if (q0 + TILE <= n) {
+    dma_tile<D, NT>(Qd, qsrc, qstride, tid);
+    dma_tile<D, NT>(Gd, gsrc, qstride, tid);
+    const int wave = tid >> 6, lane = tid & 63;
+    if (wave == 0) dma_words(Ld, a.lse + bh * n + q0, TILE, lane);
+    if (wave == 1) dma_words(Dd, a.dbuf + bh * n + q0, TILE, lane);
+  } else {
+    load_tile<D, NT>(Qd, qsrc, qstride, n - q0, tid);
+    load_tile<D, NT>(Gd, gsrc, qstride, n - q0, tid);
+    if (tid < TILE) {
+      const int i = q0 + tid;
+      Ld[tid] = (i < n) ? a.lse[bh * n + i] : INFINITY;
+      Dd[tid] = (i < n) ? a.dbuf[bh * n + i] : 0.f;
+    }
+  }
+}
+
+// One workgroup of 4 waves (one per SIMD, so each wave may hold up to 512
+// registers) per (b, kv head g, key tile kt).  Wave w owns keys 32w .. +31 of
+// the tile; their K, V fragments and G_K, G_V accumulators stay in registers.
+// The next listed query tile is copied into the other LDS stage while the
+// current one is consumed.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int NT = 256;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[TILE * D];
-  __shared__ __attribute__((aligned(16))) bf16 Gs[TILE * D];
-  __shared__ __attribute__((aligned(16))) float Ls[TILE];  // LSE in scaled log2 units
-  __shared__ __attribute__((aligned(16))) float Ds[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Qs0[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Gs0[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Qs1[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Gs1[TILE * D];
+  __shared__ __attribute__((aligned(16))) float Ls0[TILE];  // natural-log row LSE
+  __shared__ __attribute__((aligned(16))) float Ds0[TILE];
+  __shared__ __attribute__((aligned(16))) float Ls1[TILE];
+  __shared__ __attribute__((aligned(16))) float Ds1[TILE];
 
   const int T = a.T, n = a.n;
   const int total = a.B * a.Hk * T;
@@ -146,7 +185,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
-  const int key = kt * TILE + wave * 32 + l32;  // this lane's key (B-operand column)
+  const int kw = wave;
+  const int key = kt * TILE + kw * 32 + l32;  // this lane's key (B-operand column)
 
   const long kvstride = (long)a.Hk * D;
   bf16x8 kf[NKS], vf[NKS];
@@ -170,84 +210,100 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
   const float c = a.scale_log2;
-  const long qstride = (long)a.H * D;
 
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    const long bh = (long)b * a.H + h;
-    const int cnt = a.kcnt[bh * T + kt];
-    const uint16_t* list = a.kidx + (bh * T + kt) * T;
-    const uint16_t* qbase = a.q + ((long)b * n) * qstride + (long)h * D;
-    const uint16_t* gbase = a.dout + ((long)b * n) * qstride + (long)h * D;
-    for (int it = 0; it < cnt; ++it) {
-      const int qt = list[it];
-      const int q0 = qt * TILE;
-      __syncthreads();
-      load_tile<D, NT>(Qs, qbase + (long)q0 * qstride, qstride, n - q0, tid);
-      load_tile<D, NT>(Gs, gbase + (long)q0 * qstride, qstride, n - q0, tid);
-      if (tid < TILE) {
-        const int i = q0 + tid;
-        Ls[tid] = (i < n) ? a.lse[bh * n + i] * LOG2E : INFINITY;
-        Ds[tid] = (i < n) ? a.dbuf[bh * n + i] : 0.f;
+  // flattened work list over the group's heads
+  const long bh0 = (long)b * a.H + (long)g * G;
+  int nitems = 0;
+  for (int hh = 0; hh < G; ++hh) nitems += a.kcnt[(bh0 + hh) * T + kt];
+  KItems cur{0, 0, a.kcnt[bh0 * T + kt]};
+  auto skip_empty = [&](KItems& s) {
+    while (s.it >= s.cnt && s.hh + 1 < G) {
+      ++s.hh;
+      s.it = 0;
+      s.cnt = a.kcnt[(bh0 + s.hh) * T + kt];
+    }
+  };
+  skip_empty(cur);
+  KItems nxt = cur;
+  auto qt_of = [&](const KItems& s) { return (int)a.kidx[((bh0 + s.hh) * T + kt) * T + s.it]; };
+  auto advance = [&](KItems& s) {
+    ++s.it;
+    skip_empty(s);
+  };
+
+  auto visit = [&](int j, const bf16* Qc, const bf16* Gc, const float* Lc, const float* Dc, bf16* Qn,
+                   bf16* Gn, float* Ln, float* Dn) {
+    const int qt = qt_of(cur);
+    wait_vmem();
+    __syncthreads();  // item j staged in (Qc, Gc, Lc, Dc); stage n is free
+    if (j + 1 < nitems) {
+      advance(nxt);
+      stage_qg<D, NT>(Qn, Gn, Ln, Dn, a, bh0 + nxt.hh, b, (int)(g * G + nxt.hh), qt_of(nxt), tid);
+    }
+    const int q0 = qt * TILE;
+    const bool diag = CAUSAL && (qt == kt);
+#pragma unroll 1
+    for (int qc = 0; qc < 4; ++qc) {
+      // S and G_P for queries 32qc + (C rows), keys of this wave (C column)
+      f32x16 s = f32x16{}, gp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = mfma32(lds_row8<D>(Qc, qc * 32 + l32, 2 * ks + h32), kf[ks], s);
+        gp = mfma32(lds_row8<D>(Gc, qc * 32 + l32, 2 * ks + h32), vf[ks], gp);
       }
-      __syncthreads();
-      const bool diag = CAUSAL && (qt == kt);
 #pragma unroll
-      for (int qc = 0; qc < 4; ++qc) {
-        // S and G_P for queries 32qc + (C rows), keys of this wave (C column)
-        f32x16 s = f32x16{}, gp = f32x16{};
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int qr = qc * 32 + 8 * j4 + 4 * h32;  // local query row of registers 4j4..4j4+3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lc + qr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dc + qr);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          s = mfma32(lds_row8<D>(Qs, qc * 32 + l32, 2 * ks + h32), kf[ks], s);
-          gp = mfma32(lds_row8<D>(Gs, qc * 32 + l32, 2 * ks + h32), vf[ks], gp);
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * j4 + t;
+          float pv = exp2f(fmaf(s[r], c, -l4[t] * LOG2E));
+          if (diag && key > q0 + qr + t) pv = 0.f;
+          s[r] = pv;
+          gp[r] = pv * (gp[r] - d4[t]);
         }
-        f32x16 p, ds;
+      }
+      // G_V += P^T G_O and G_K += G_S^T Q; step st covers queries
+      // 32qc + 16st + 4*h32 + 0..3 and 32qc + 16st + 8 + 4*h32 + 0..3
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int qr = qc * 32 + 8 * j + 4 * h32;  // local query row of registers 4j..4j+3
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + qr);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + qr);
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 pa = pack8(s, st);
+        const bf16x8 sa = pack8(gp, st);
+        const int k0 = qc * 32 + st * 16 + 4 * h32;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int r = 4 * j + t;
-            float pv = exp2f(fmaf(s[r], c, -l4[t]));
-            if (diag && key > q0 + qr + t) pv = 0.f;
-            p[r] = pv;
-            ds[r] = pv * (gp[r] - d4[t]);
-          }
-        }
-        // G_V += P^T G_O and G_K += G_S^T Q; step st covers queries
-        // 32qc + 16st + 4*h32 + 0..3 and 32qc + 16st + 8 + 4*h32 + 0..3
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16x8 pa = pack8(p, st);
-          const bf16x8 sa = pack8(ds, st);
-          const int k0 = qc * 32 + st * 16 + 4 * h32;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
-            const bf16x8 gb = cat8(lds_tr4<D>(Gs, k0, n0, lane), lds_tr4<D>(Gs, k0 + 8, n0, lane));
-            dv[db] = mfma32(pa, gb, dv[db]);
-            const bf16x8 qb = cat8(lds_tr4<D>(Qs, k0, n0, lane), lds_tr4<D>(Qs, k0 + 8, n0, lane));
-            dk[db] = mfma32(sa, qb, dk[db]);
-          }
+        for (int db = 0; db < NDB; ++db) {
+          const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
+          const bf16x8 gb = cat8(lds_tr4<D>(Gc, k0, n0, lane), lds_tr4<D>(Gc, k0 + 8, n0, lane));
+          dv[db] = mfma32(pa, gb, dv[db]);
+          const bf16x8 qb = cat8(lds_tr4<D>(Qc, k0, n0, lane), lds_tr4<D>(Qc, k0 + 8, n0, lane));
+          dk[db] = mfma32(sa, qb, dk[db]);
         }
       }
     }
+    advance(cur);
+  };
+
+  if (nitems > 0) stage_qg<D, NT>(Qs0, Gs0, Ls0, Ds0, a, bh0 + cur.hh, b, (int)(g * G + cur.hh), qt_of(cur), tid);
+  for (int j = 0; j < nitems; j += 2) {
+    visit(j, Qs0, Gs0, Ls0, Ds0, Qs1, Gs1, Ls1, Ds1);
+    if (j + 1 < nitems) visit(j + 1, Qs1, Gs1, Ls1, Ds1, Qs0, Gs0, Ls0, Ds0);
   }
 
-  // epilogue: C layout is [key = 8(r/4) + 4*h32 + r%4 of the wave][dim = 32db + l32];
-  // stage through LDS as [key][dim] and store coalesced rows.
+  // epilogue: stage as [key][dim] bf16 and store coalesced rows.
+  // C layout: [key = 8(r/4) + 4*h32 + r%4 of block kw][dim = 32db + l32].
+  wait_vmem();
   __syncthreads();
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kr = wave * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      const int kr = kw * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
       const int dim = db * 32 + l32;
       const int off = tile_off<D>(kr, dim >> 3) + (dim & 7);
-      Qs[off] = (bf16)(dk[db][r] * a.scale);
-      Gs[off] = (bf16)dv[db][r];
+      Qs0[off] = (bf16)(dk[db][r] * a.scale);
+      Gs0[off] = (bf16)dv[db][r];
     }
   __syncthreads();
   {
@@ -259,9 +315,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       const int row = cc / CH, ch = cc % CH;
       if (kt * TILE + row < n) {
         *reinterpret_cast<u32x4*>(a.dk + base + (long)row * kvstride + ch * 8) =
-            *reinterpret_cast<const u32x4*>(Qs + tile_off<D>(row, ch));
+            *reinterpret_cast<const u32x4*>(Qs0 + tile_off<D>(row, ch));
         *reinterpret_cast<u32x4*>(a.dv + base + (long)row * kvstride + ch * 8) =
-            *reinterpret_cast<const u32x4*>(Gs + tile_off<D>(row, ch));
+            *reinterpret_cast<const u32x4*>(Gs0 + tile_off<D>(row, ch));
       }
     }
   }
@@ -270,14 +326,38 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // G_Q
 // ---------------------------------------------------------------------------
+// Stage K, V and the key mean of key tile kt into LDS.
+template <int D, int NT>
+__device__ __forceinline__ void stage_kvb(bf16* Kd, bf16* Vd, float* Bd, const BwdArgs& a, const uint16_t* kbase,
+                                          const uint16_t* vbase, const float* kbar, int kt, int tid) {
+  const int n = a.n;
+  const long stride = (long)a.Hk * D;
+  const int key0 = kt * TILE;
+  if (key0 + TILE <= n) {
+    dma_tile<D, NT>(Kd, kbase + (long)key0 * stride, stride, tid);
+    dma_tile<D, NT>(Vd, vbase + (long)key0 * stride, stride, tid);
+  } else {
+    load_tile<D, NT>(Kd, kbase + (long)key0 * stride, stride, n - key0, tid);
+    load_tile<D, NT>(Vd, vbase + (long)key0 * stride, stride, n - key0, tid);
+  }
+  if ((tid >> 6) == 0) dma_words(Bd, kbar + (long)kt * D, D, tid & 63);
+}
+
+// One workgroup of 4 waves (one per SIMD) per (b, h, query tile qt).  Wave w
+// owns query rows 32w .. +31: their Q, G_O fragments and the G_Q^T accumulator
+// stay in registers.  The next listed key tile is copied into the other LDS
+// stage while the current one is consumed.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   constexpr int NT = 256;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[TILE * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[TILE * D];
-  __shared__ __attribute__((aligned(16))) float Kb[D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE * D];
+  __shared__ __attribute__((aligned(16))) float Kb0[D];
+  __shared__ __attribute__((aligned(16))) float Kb1[D];
 
   const int T = a.T, n = a.n;
   const int total = a.B * a.H * T;
@@ -289,7 +369,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
-  const int qrow = qt * TILE + wave * 32 + l32;
+  const int lrow = wave * 32 + l32;
+  const int qrow = qt * TILE + lrow;
 
   const long qstride = (long)a.H * D;
   bf16x8 qf[NKS], gf[NKS];
@@ -315,47 +396,45 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
   const long kvstride = (long)a.Hk * D;
   const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
   const uint16_t* vbase = a.v + ((long)b * n) * kvstride + (long)g * D;
+  const float* kbar = a.kbar + (long)(b * a.Hk + g) * T * D;
   const int cnt = a.qcnt[(long)bh * T + qt];
   const uint16_t* list = a.qidx + ((long)bh * T + qt) * T;
 
-  for (int it = 0; it < cnt; ++it) {
+  auto visit = [&](int it, const bf16* Kc, const bf16* Vc, const float* Bc, bf16* Kn, bf16* Vn, float* Bn) {
     const int kt = list[it];
+    wait_vmem();
+    __syncthreads();  // key tile kt staged in (Kc, Vc, Bc); stage n is free
+    if (it + 1 < cnt) stage_kvb<D, NT>(Kn, Vn, Bn, a, kbase, vbase, kbar, list[it + 1], tid);
     const int key0 = kt * TILE;
-    __syncthreads();
-    load_tile<D, NT>(Ks, kbase + (long)key0 * kvstride, kvstride, n - key0, tid);
-    load_tile<D, NT>(Vs, vbase + (long)key0 * kvstride, kvstride, n - key0, tid);
-    if (tid < D) Kb[tid] = a.kbar[((long)(b * a.Hk + g) * T + kt) * D + tid];
-    __syncthreads();
     const bool diag = CAUSAL && (qt == kt);
     const bool edge = key0 + TILE > n;
-    float losum = 0.f;  // sum over this tile's keys of (G_S - bf16(G_S)) for this row
-#pragma unroll
+    float losum = 0.f;  // sum over this wave's keys of (G_S - bf16(G_S)) for this row
+#pragma unroll 1
     for (int kb = 0; kb < 4; ++kb) {
       f32x16 s = f32x16{}, gp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s = mfma32(lds_row8<D>(Ks, kb * 32 + l32, 2 * ks + h32), qf[ks], s);
-        gp = mfma32(lds_row8<D>(Vs, kb * 32 + l32, 2 * ks + h32), gf[ks], gp);
+        s = mfma32(lds_row8<D>(Kc, kb * 32 + l32, 2 * ks + h32), qf[ks], s);
+        gp = mfma32(lds_row8<D>(Vc, kb * 32 + l32, 2 * ks + h32), gf[ks], gp);
       }
-      f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = exp2f(fmaf(s[r], c, -lse2));
         if (diag || edge) {
-          const int kk = key0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          if (kk >= n || (diag && kk > qrow)) pv = 0.f;
+          const int kk2 = key0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          if (kk2 >= n || (diag && kk2 > qrow)) pv = 0.f;
         }
-        ds[r] = pv * (gp[r] - dl);
+        gp[r] = pv * (gp[r] - dl);
       }
       // G_Q^T += K^T G_S^T; step st covers keys 32kb + 16st + 4*h32 + 0..3 and +8
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8 sb = pack8_lo(ds, st, losum);
+        const bf16x8 sb = pack8_lo(gp, st, losum);
         const int k0 = kb * 32 + st * 16 + 4 * h32;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
-          const bf16x8 ka = cat8(lds_tr4<D>(Ks, k0, n0, lane), lds_tr4<D>(Ks, k0 + 8, n0, lane));
+          const bf16x8 ka = cat8(lds_tr4<D>(Kc, k0, n0, lane), lds_tr4<D>(Kc, k0 + 8, n0, lane));
           dq[db] = mfma32(ka, sb, dq[db]);
         }
       }
@@ -371,23 +450,29 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 kb4 = *reinterpret_cast<const f32x4*>(Kb + db * 32 + 8 * j + 4 * h32);
+        const f32x4 kb4 = *reinterpret_cast<const f32x4*>(Bc + db * 32 + 8 * j + 4 * h32);
 #pragma unroll
         for (int t = 0; t < 4; ++t) dq[db][4 * j + t] = fmaf(losum, kb4[t], dq[db][4 * j + t]);
       }
+  };
+
+  if (cnt > 0) stage_kvb<D, NT>(Ks0, Vs0, Kb0, a, kbase, vbase, kbar, list[0], tid);
+  for (int it = 0; it < cnt; it += 2) {
+    visit(it, Ks0, Vs0, Kb0, Ks1, Vs1, Kb1);
+    if (it + 1 < cnt) visit(it + 1, Ks1, Vs1, Kb1, Ks0, Vs0, Kb0);
   }
 
   // epilogue: dq C layout is [dim = 32db + 8(r/4) + 4*h32 + r%4][query l32]
+  wait_vmem();
   __syncthreads();
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int dim = db * 32 + 8 * j + 4 * h32;
-      const int row = wave * 32 + l32;
       bf16x4 w4 = {(bf16)(dq[db][4 * j] * a.scale), (bf16)(dq[db][4 * j + 1] * a.scale),
                    (bf16)(dq[db][4 * j + 2] * a.scale), (bf16)(dq[db][4 * j + 3] * a.scale)};
-      *reinterpret_cast<bf16x4*>(Ks + tile_off<D>(row, dim >> 3) + (dim & 7)) = w4;
+      *reinterpret_cast<bf16x4*>(Vs0 + tile_off<D>(lrow, dim >> 3) + (dim & 7)) = w4;
     }
   __syncthreads();
   {
@@ -399,7 +484,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a) {
       const int row = cc / CH, ch = cc % CH;
       if (qt * TILE + row < n)
         *reinterpret_cast<u32x4*>(op + (long)row * qstride + ch * 8) =
-            *reinterpret_cast<const u32x4*>(Ks + tile_off<D>(row, ch));
+            *reinterpret_cast<const u32x4*>(Vs0 + tile_off<D>(row, ch));
     }
   }
 }

@@ -12,8 +12,8 @@
 // m_run the running maximum after the tile, so it costs one log per row per
 // tile.
 //
-// Work decomposition (gfx950): one workgroup of 4 waves per (b, h, query tile);
-// wave w owns 32 query rows.  S^T = K Q^T is formed with 32x32x16 bf16 MFMA
+// Work decomposition (gfx950): one workgroup of 8 waves (2 per SIMD) per
+// (b, h, pair of query tiles); wave w owns 32 query rows.  S^T = K Q^T is formed with 32x32x16 bf16 MFMA
 // (K from LDS as the A operand, the wave's Q fragment resident in registers as
 // B), so each lane holds one query row and the row reductions stay in-lane
 // plus one exchange between the two lane halves.  O^T += V^T P^T takes P^T
@@ -36,27 +36,50 @@ struct FwdArgs {
   float scale_log2;  // scale * log2(e)
 };
 
+// Stage one K and one V tile of keys key0 .. key0+127 into LDS: asynchronously
+// when the tile is full, else synchronously with zero-filled padding rows.
+template <int D, int NT>
+__device__ __forceinline__ void stage_kv(bf16* Ks, bf16* Vs, const uint16_t* kbase, const uint16_t* vbase,
+                                         long stride, int key0, int n, int tid) {
+  if (key0 + TILE <= n) {
+    dma_tile<D, NT>(Ks, kbase + (long)key0 * stride, stride, tid);
+    dma_tile<D, NT>(Vs, vbase + (long)key0 * stride, stride, tid);
+  } else {
+    load_tile<D, NT>(Ks, kbase + (long)key0 * stride, stride, n - key0, tid);
+    load_tile<D, NT>(Vs, vbase + (long)key0 * stride, stride, n - key0, tid);
+  }
+}
+
+// One workgroup of 8 waves per (b, h, pair of query tiles 2p, 2p+1); wave w owns
+// rows 32(w%4) .. +31 of query tile 2p + w/4.  K/V tiles are double-buffered in
+// LDS: the copy of tile kt+1 is in flight while tile kt is consumed.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  constexpr int NT = 256;
+__global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
+  constexpr int NT = 512;
   constexpr int NKS = D / 16;  // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;  // 32-wide blocks of the head dimension
-  __shared__ __attribute__((aligned(16))) bf16 Ks[TILE * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE * D];
 
-  const int total = a.B * a.H * a.T;
-  const int L = xcd_remap(blockIdx.x, total);
   const int T = a.T;
-  int qt = L % T;
-  if (CAUSAL) qt = T - 1 - qt;  // heaviest query tiles first
-  const int bh = L / T;
+  const int T2 = (T + 1) / 2;
+  const int total = a.B * a.H * T2;
+  const int L = xcd_remap(blockIdx.x, total);
+  int p = L % T2;
+  if (CAUSAL) p = T2 - 1 - p;  // heaviest query tiles first
+  const int bh = L / T2;
   const int h = bh % a.H, b = bh / a.H;
   const int g = h / (a.H / a.Hk);
   const int n = a.n;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
-  const int qrow = qt * TILE + wave * 32 + l32;  // this lane's query row
+  const int qt = 2 * p + (wave >> 2);            // this wave's query tile
+  const bool active = qt < T;                     // odd T: the last pair has one tile
+  const int lrow = (wave & 3) * 32 + l32;         // row within the query tile
+  const int qrow = qt * TILE + lrow;              // this lane's query row
 
   // Q fragment (B operand of S^T = K Q^T): dims 16ks + 8*h32 + 0..7 of row qrow
   bf16x8 qf[NKS];
@@ -80,7 +103,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const long kvstride = (long)a.Hk * D;
   const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
   const uint16_t* vbase = a.v + ((long)b * n) * kvstride + (long)g * D;
-  const int nkt = CAUSAL ? qt + 1 : T;
+  const int qt_hi = min(2 * p + 1, T - 1);
+  const int nkt = CAUSAL ? qt_hi + 1 : T;        // key tiles the workgroup visits
   float* tl_row = nullptr;
   if (a.tlse) {
     const long pairs = CAUSAL ? (long)T * (T + 1) / 2 : (long)T * T;
@@ -88,22 +112,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
   const float c = a.scale_log2;
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  // one visit of key tile kt: prefetch tile kt+1 into the other stage, then
+  // consume tile kt from (Kc, Vc).  Called with static stage arrays so that the
+  // compiler sees the prefetch target and the operands as distinct objects.
+  auto visit = [&](int kt, const bf16* Kc, const bf16* Vc, bf16* Kn, bf16* Vn) {
+    wait_vmem();
+    __syncthreads();  // tile kt is in (Kc, Vc); nobody reads (Kn, Vn) any more
+    if (kt + 1 < nkt) stage_kv<D, NT>(Kn, Vn, kbase, vbase, kvstride, (kt + 1) * TILE, n, tid);
+    if (!active || (CAUSAL && kt > qt)) return;  // wave-uniform
     const int key0 = kt * TILE;
-    __syncthreads();
-    load_tile<D, NT>(Ks, kbase + (long)key0 * kvstride, kvstride, n - key0, tid);
-    load_tile<D, NT>(Vs, vbase + (long)key0 * kvstride, kvstride, n - key0, tid);
-    __syncthreads();
 
     // S^T for the 4 key blocks of 32
     f32x16 s[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x16{};
+    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        s[kb] = mfma32(lds_row8<D>(Ks, kb * 32 + l32, 2 * ks + h32), qf[ks], s[kb]);
-    }
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)  // four independent accumulators back to back
+        s[kb] = mfma32(lds_row8<D>(Kc, kb * 32 + l32, 2 * ks + h32), qf[ks], s[kb]);
     // mask padded keys (last tile) and, on the diagonal tile, keys after the row
     const bool need_mask = (key0 + TILE > n) || (CAUSAL && kt == qt);
     if (need_mask) {
@@ -129,9 +156,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(s[kb][r], c, -m_new));
-        s[kb][r] = p;
-        ts += p;
+        const float pv = exp2f(fmaf(s[kb][r], c, -m_new));
+        s[kb][r] = pv;
+        ts += pv;
       }
     ts += __shfl_xor(ts, 32);
     l_run = l_run * alpha + ts;
@@ -140,10 +167,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     if (tl_row && h32 == 0) {
       const float t = (qrow < n) ? (m_new + __log2f(ts)) * LN2 : -INFINITY;
-      tl_row[pair_index(qt, kt, T, CAUSAL) * TILE + wave * 32 + l32] = t;
+      tl_row[pair_index(qt, kt, T, CAUSAL) * TILE + lrow] = t;
     }
-    // O^T += V^T P^T.  Step s of key block kb covers keys 32kb + 16s + 4*h32 + 0..3
-    // and 32kb + 16s + 8 + 4*h32 + 0..3, i.e. C registers 8s .. 8s+7.
+    // O^T += V^T P^T.  Step st of key block kb covers keys 32kb + 16st + 4*h32 + 0..3
+    // and 32kb + 16st + 8 + 4*h32 + 0..3, i.e. C registers 8st .. 8st+7.
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -153,47 +180,59 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
-          const bf16x8 va = cat8(lds_tr4<D>(Vs, k0, n0, lane), lds_tr4<D>(Vs, k0 + 8, n0, lane));
+          const bf16x8 va = cat8(lds_tr4<D>(Vc, k0, n0, lane), lds_tr4<D>(Vc, k0 + 8, n0, lane));
           oacc[db] = mfma32(va, pb, oacc[db]);
         }
       }
+  };
+
+  stage_kv<D, NT>(Ks0, Vs0, kbase, vbase, kvstride, 0, n, tid);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    visit(kt, Ks0, Vs0, Ks1, Vs1);
+    if (kt + 1 < nkt) visit(kt + 1, Ks1, Vs1, Ks0, Vs0);
   }
 
-  // epilogue: normalise, stage O through LDS as [row][dim], store coalesced
-  const float inv = 1.f / l_run;
+  // epilogue: normalise, stage O (and its residual) through LDS as [row][dim],
+  // store coalesced.  Query tile 2p + j uses Ks[j] / Vs[j].
   __syncthreads();
+  bf16* Os = (wave >> 2) ? Ks1 : Ks0;
+  bf16* Rs = (wave >> 2) ? Vs1 : Vs0;
+  if (active) {
+    const float inv = 1.f / l_run;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int dim = db * 32 + 8 * j + 4 * h32;
-      const int row = wave * 32 + l32;
-      bf16x4 w4, r4;
+      for (int j = 0; j < 4; ++j) {
+        const int dim = db * 32 + 8 * j + 4 * h32;
+        bf16x4 w4, r4;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float f = oacc[db][4 * j + t] * inv;
-        w4[t] = (bf16)f;
-        r4[t] = (bf16)(f - (float)w4[t]);
+        for (int t = 0; t < 4; ++t) {
+          const float f = oacc[db][4 * j + t] * inv;
+          w4[t] = (bf16)f;
+          r4[t] = (bf16)(f - (float)w4[t]);
+        }
+        *reinterpret_cast<bf16x4*>(Os + tile_off<D>(lrow, dim >> 3) + (dim & 7)) = w4;
+        *reinterpret_cast<bf16x4*>(Rs + tile_off<D>(lrow, dim >> 3) + (dim & 7)) = r4;
       }
-      *reinterpret_cast<bf16x4*>(Ks + tile_off<D>(row, dim >> 3) + (dim & 7)) = w4;
-      *reinterpret_cast<bf16x4*>(Vs + tile_off<D>(row, dim >> 3) + (dim & 7)) = r4;
-    }
-  if (h32 == 0 && qrow < n) a.lse[(long)bh * n + qrow] = (m_run + __log2f(l_run)) * LN2;
+    if (h32 == 0 && qrow < n) a.lse[(long)bh * n + qrow] = (m_run + __log2f(l_run)) * LN2;
+  }
   __syncthreads();
   {
     constexpr int CH = D / 8;
     const long ostride = (long)a.H * D;
-    const long obase = ((long)b * n + (long)qt * TILE) * ostride + (long)h * D;
 #pragma unroll
-    for (int it = 0; it < TILE * CH / NT; ++it) {
+    for (int it = 0; it < 2 * TILE * CH / NT; ++it) {
       const int cc = tid + it * NT;
-      const int row = cc / CH, ch = cc % CH;
-      if (qt * TILE + row < n) {
-        *reinterpret_cast<u32x4*>(a.o + obase + (long)row * ostride + ch * 8) =
-            *reinterpret_cast<const u32x4*>(Ks + tile_off<D>(row, ch));
+      const int r2 = cc / CH, ch = cc % CH;  // r2: row within the 256-row pair
+      const int j = r2 / TILE, row = r2 % TILE;
+      const int gi = (2 * p + j) * TILE + row;
+      if (gi < n) {
+        const long off = ((long)b * n + gi) * ostride + (long)h * D + ch * 8;
+        *reinterpret_cast<u32x4*>(a.o + off) =
+            *reinterpret_cast<const u32x4*>((j ? Ks1 : Ks0) + tile_off<D>(row, ch));
         if (a.olo)
-          *reinterpret_cast<u32x4*>(a.olo + obase + (long)row * ostride + ch * 8) =
-              *reinterpret_cast<const u32x4*>(Vs + tile_off<D>(row, ch));
+          *reinterpret_cast<u32x4*>(a.olo + off) =
+              *reinterpret_cast<const u32x4*>((j ? Vs1 : Vs0) + tile_off<D>(row, ch));
       }
     }
   }
@@ -201,9 +240,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  const int total = a.B * a.H * a.T;
+  const int total = a.B * a.H * ((a.T + 1) / 2);
   ProfScope ps(PK_FWD, st);
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3(total), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
