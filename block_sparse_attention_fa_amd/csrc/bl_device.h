@@ -6,10 +6,13 @@
 //   C (32x32):      lane holds C[m = 8(r/4) + 4h + r%4][n = l % 32], r = 0..15
 //
 // LDS tiles hold 128 rows x D bf16, row-major, in 16-byte chunks.  Chunk c of
-// row r is stored at chunk position c ^ swz(r) with swz(r) = 2(r%4) + (r/4)%2,
-// so that eight consecutive rows read at the same chunk, and four consecutive
-// rows read as two adjacent chunks by ds_read_b64_tr_b16, fall in distinct
-// bank groups.
+// row r is stored at chunk position c ^ swz<D>(r).  For D = 128 swz(r) =
+// 8(r%2) + (r/2)%8; for D = 64 (8 chunks per row) swz(r) = 2(r%4) + (r/4)%2.
+// Measured on MI355X, these keep both access patterns below near the LDS peak:
+// 32 lanes reading one chunk of 32 consecutive rows (ds_read_b128), and 16-lane
+// groups reading 4 consecutive rows x 32 bytes (ds_read_b64_tr_b16).  swz depends
+// on r % 16 only, so shifting a read by a multiple of 16 rows is a constant
+// offset.
 //
 // ds_read_b64_tr_b16 (transpose read, per 16-lane group): lane i of the group
 // supplies the address of 4 bf16 at (row k0 + i/4, col n0 + 4(i%4)); lane j of
@@ -36,13 +39,60 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 1) << 3) | ((r >> 1) & 7);
+  else return ((r & 3) << 1) | ((r >> 2) & 1);
+}
 
 // element offset of (row, chunk) in a swizzled tile with D columns
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * D + ((chunk ^ swz(row)) << 3);
+  return row * D + ((chunk ^ swz<D>(row)) << 3);
 }
+
+// Per-lane byte offsets of the two MFMA operand read patterns on a tile, so that
+// every read in the inner loops is "lane offset + compile-time immediate".
+//   row pattern: lane reads row blk*32 + l32, chunk 2ks + h32 (A rows of S/dP,
+//                8 consecutive elements along the head dimension)
+//   tr pattern:  16-lane group g reads rows 32kb + 16st + 4*h32 + 8*half + i/4,
+//                columns 32db + 16(g%2) + 4(i%4) (ds_read_b64_tr_b16)
+template <int D>
+struct LdsOffsets {
+  int row[D / 16];
+  int tr[2][D / 32];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, h32 = lane >> 5, i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) row[ks] = 2 * tile_off<D>(l32, 2 * ks + h32);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int r = 4 * h32 + 8 * half + (i >> 2);
+        const int col = 32 * db + 16 * (g & 1) + 4 * (i & 3);
+        tr[half][db] = 2 * (tile_off<D>(r, col >> 3) + (col & 7));
+      }
+  }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 rd_row(const bf16* tile, const LdsOffsets<D>& o, int blk, int ks) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + o.row[ks] + blk * 32 * D * 2);
+}
+
+// bf16x8 operand over rows 32kb + 16st + 4*h32 + {0..3, 8..11} of column block db
+template <int D>
+__device__ __forceinline__ bf16x8 rd_tr(const bf16* tile, const LdsOffsets<D>& o, int kb, int st, int db) {
+  const char* base = reinterpret_cast<const char*>(tile) + (32 * kb + 16 * st) * D * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(base + o.tr[0][db]));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(base + o.tr[1][db]));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 16-byte row read: 8 consecutive columns of one row
 template <int D>
@@ -106,20 +156,33 @@ __device__ __forceinline__ void load_tile(bf16* tile, const uint16_t* src, long 
 // memory into a swizzled LDS tile with global_load_lds_dwordx4: each wave
 // instruction fills 64 consecutive 16-byte LDS slots (slot = lane), so lane l
 // fetches the global chunk that belongs at its slot, i.e. the inverse swizzle.
-// Completion: s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
+// The per-thread source offsets depend only on the row stride and are computed
+// once.  Completion: s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
 template <int D, int NT>
-__device__ __forceinline__ void dma_tile(bf16* tile, const uint16_t* src, long stride, int tid) {
-  constexpr int CH = D / 8;
-  constexpr int NW = NT / 64;
-  constexpr int NI = TILE * CH / NT;  // instructions per thread
-  const int lane = tid & 63, wave = tid >> 6;
+struct DmaOffsets {
+  static constexpr int NI = TILE * (D / 8) / NT;  // instructions per thread per tile
+  uint32_t off[NI];                               // element offsets within the source tile
+  __device__ __forceinline__ void init(long stride, int tid) {
+    constexpr int CH = D / 8;
+    constexpr int NW = NT / 64;
+    const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < NI; ++i) {
+      const int s = (i * NW + wave) * 64 + lane;
+      const int row = s / CH, pch = s % CH;
+      off[i] = (uint32_t)(row * stride + ((pch ^ swz<D>(row)) << 3));
+    }
+  }
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void dma_tile(bf16* tile, const uint16_t* src, const DmaOffsets<D, NT>& o, int tid) {
+  constexpr int NW = NT / 64;
+  const int wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < DmaOffsets<D, NT>::NI; ++i) {
     const int slot0 = (i * NW + wave) * 64;  // first slot of this wave instruction
-    const int s = slot0 + lane;
-    const int row = s / CH, pch = s % CH;
-    const uint16_t* g = src + (long)row * stride + ((pch ^ swz(row)) << 3);
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + o.off[i]),
                                      (__attribute__((address_space(3))) void*)(tile + slot0 * 8), 16, 0, 0);
   }
 }
@@ -130,6 +193,22 @@ __device__ __forceinline__ void dma_words(float* lds, const float* src, int n32,
   for (int i = 0; i < n32 / 64; ++i)
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 64 * i + lane),
                                      (__attribute__((address_space(3))) void*)(lds + 64 * i), 4, 0, 0);
+}
+
+// Scheduling hints (instruction classes of __builtin_amdgcn_sched_group_barrier).
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
+
+// Ask the scheduler for: `ahead` LDS reads, then `steps` x [m MFMA, r LDS reads],
+// then the remaining MFMAs `tail`.  Keeps operand loads a few MFMAs ahead of use.
+template <int AHEAD, int STEPS, int M, int R, int TAIL>
+__device__ __forceinline__ void sched_interleave() {
+  __builtin_amdgcn_sched_group_barrier(SG_DS_READ, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(SG_MFMA, M, 0);
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(SG_MFMA, TAIL, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)

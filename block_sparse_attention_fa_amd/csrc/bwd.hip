@@ -133,15 +133,15 @@ struct KItems {
 // for full tiles, synchronously (zero / +inf padding) for the ragged last one.
 template <int D, int NT>
 __device__ __forceinline__ void stage_qg(bf16* Qd, bf16* Gd, float* Ld, float* Dd, const BwdArgs& a,
-                                         long bh, int b, int h, int qt, int tid) {
+                                         const DmaOffsets<D, NT>& dmo, long bh, int b, int h, int qt, int tid) {
   const int n = a.n;
   const long qstride = (long)a.H * D;
   const int q0 = qt * TILE;
   const uint16_t* qsrc = a.q + ((long)b * n + q0) * qstride + (long)h * D;
   const uint16_t* gsrc = a.dout + ((long)b * n + q0) * qstride + (long)h * D;
   if (q0 + TILE <= n) {
-    dma_tile<D, NT>(Qd, qsrc, qstride, tid);
-    dma_tile<D, NT>(Gd, gsrc, qstride, tid);
+    dma_tile<D, NT>(Qd, qsrc, dmo, tid);
+    dma_tile<D, NT>(Gd, gsrc, dmo, tid);
     const int wave = tid >> 6, lane = tid & 63;
     if (wave == 0) dma_words(Ld, a.lse + bh * n + q0, TILE, lane);
     if (wave == 1) dma_words(Dd, a.dbuf + bh * n + q0, TILE, lane);
@@ -210,6 +210,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
   }
   const float c = a.scale_log2;
+  LdsOffsets<D> lo;
+  lo.init(lane);
+  DmaOffsets<D, NT> dmo;
+  dmo.init((long)a.H * D, tid);
 
   // flattened work list over the group's heads
   const long bh0 = (long)b * a.H + (long)g * G;
@@ -238,19 +242,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     __syncthreads();  // item j staged in (Qc, Gc, Lc, Dc); stage n is free
     if (j + 1 < nitems) {
       advance(nxt);
-      stage_qg<D, NT>(Qn, Gn, Ln, Dn, a, bh0 + nxt.hh, b, (int)(g * G + nxt.hh), qt_of(nxt), tid);
+      stage_qg<D, NT>(Qn, Gn, Ln, Dn, a, dmo, bh0 + nxt.hh, b, (int)(g * G + nxt.hh), qt_of(nxt), tid);
     }
     const int q0 = qt * TILE;
     const bool diag = CAUSAL && (qt == kt);
-#pragma unroll 1
-    for (int qc = 0; qc < 4; ++qc) {
-      // S and G_P for queries 32qc + (C rows), keys of this wave (C column)
-      f32x16 s = f32x16{}, gp = f32x16{};
+    // Per 32-query chunk qc: [S, G_P MFMAs] -> [P, G_S on the VALU] -> [G_V, G_K
+    // MFMAs].  The chunks are software-pipelined: chunk qc+1's S and G_P MFMAs
+    // are issued before chunk qc's VALU work, so the matrix pipe stays busy
+    // while the wave computes exponentials.
+    auto mm_sdp = [&](int qc, f32x16& sv, f32x16& gv) {
+      sv = f32x16{};
+      gv = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s = mfma32(lds_row8<D>(Qc, qc * 32 + l32, 2 * ks + h32), kf[ks], s);
-        gp = mfma32(lds_row8<D>(Gc, qc * 32 + l32, 2 * ks + h32), vf[ks], gp);
+        sv = mfma32(rd_row<D>(Qc, lo, qc, ks), kf[ks], sv);
+        gv = mfma32(rd_row<D>(Gc, lo, qc, ks), vf[ks], gv);
       }
+    };
+    auto soft = [&](int qc, f32x16& sv, f32x16& gv) {
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         const int qr = qc * 32 + 8 * j4 + 4 * h32;  // local query row of registers 4j4..4j4+3
@@ -259,33 +268,45 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * j4 + t;
-          float pv = exp2f(fmaf(s[r], c, -l4[t] * LOG2E));
+          float pv = fast_exp2(fmaf(sv[r], c, -l4[t] * LOG2E));
           if (diag && key > q0 + qr + t) pv = 0.f;
-          s[r] = pv;
-          gp[r] = pv * (gp[r] - d4[t]);
+          sv[r] = pv;
+          gv[r] = pv * (gv[r] - d4[t]);
         }
       }
-      // G_V += P^T G_O and G_K += G_S^T Q; step st covers queries
-      // 32qc + 16st + 4*h32 + 0..3 and 32qc + 16st + 8 + 4*h32 + 0..3
+    };
+    // G_V += P^T G_O and G_K += G_S^T Q; step st covers queries
+    // 32qc + 16st + 4*h32 + 0..3 and 32qc + 16st + 8 + 4*h32 + 0..3
+    auto mm_dvdk = [&](int qc, const f32x16& pv, const f32x16& sv) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8 pa = pack8(s, st);
-        const bf16x8 sa = pack8(gp, st);
-        const int k0 = qc * 32 + st * 16 + 4 * h32;
+        const bf16x8 pa = pack8(pv, st);
+        const bf16x8 sa = pack8(sv, st);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
-          const bf16x8 gb = cat8(lds_tr4<D>(Gc, k0, n0, lane), lds_tr4<D>(Gc, k0 + 8, n0, lane));
-          dv[db] = mfma32(pa, gb, dv[db]);
-          const bf16x8 qb = cat8(lds_tr4<D>(Qc, k0, n0, lane), lds_tr4<D>(Qc, k0 + 8, n0, lane));
-          dk[db] = mfma32(sa, qb, dk[db]);
+          dv[db] = mfma32(pa, rd_tr<D>(Gc, lo, qc, st, db), dv[db]);
+          dk[db] = mfma32(sa, rd_tr<D>(Qc, lo, qc, st, db), dk[db]);
         }
       }
-    }
+    };
+    f32x16 sA, gA, sB, gB;
+    mm_sdp(0, sA, gA);
+    mm_sdp(1, sB, gB);
+    soft(0, sA, gA);
+    mm_dvdk(0, sA, gA);
+    mm_sdp(2, sA, gA);
+    soft(1, sB, gB);
+    mm_dvdk(1, sB, gB);
+    mm_sdp(3, sB, gB);
+    soft(2, sA, gA);
+    mm_dvdk(2, sA, gA);
+    soft(3, sB, gB);
+    mm_dvdk(3, sB, gB);
     advance(cur);
   };
 
-  if (nitems > 0) stage_qg<D, NT>(Qs0, Gs0, Ls0, Ds0, a, bh0 + cur.hh, b, (int)(g * G + cur.hh), qt_of(cur), tid);
+  if (nitems > 0)
+    stage_qg<D, NT>(Qs0, Gs0, Ls0, Ds0, a, dmo, bh0 + cur.hh, b, (int)(g * G + cur.hh), qt_of(cur), tid);
   for (int j = 0; j < nitems; j += 2) {
     visit(j, Qs0, Gs0, Ls0, Ds0, Qs1, Gs1, Ls1, Ds1);
     if (j + 1 < nitems) visit(j + 1, Qs1, Gs1, Ls1, Ds1, Qs0, Gs0, Ls0, Ds0);
@@ -328,14 +349,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Stage K, V and the key mean of key tile kt into LDS.
 template <int D, int NT>
-__device__ __forceinline__ void stage_kvb(bf16* Kd, bf16* Vd, float* Bd, const BwdArgs& a, const uint16_t* kbase,
-                                          const uint16_t* vbase, const float* kbar, int kt, int tid) {
+__device__ __forceinline__ void stage_kvb(bf16* Kd, bf16* Vd, float* Bd, const BwdArgs& a, const DmaOffsets<D, NT>& dmo,
+                                          const uint16_t* kbase, const uint16_t* vbase, const float* kbar, int kt,
+                                          int tid) {
   const int n = a.n;
   const long stride = (long)a.Hk * D;
   const int key0 = kt * TILE;
   if (key0 + TILE <= n) {
-    dma_tile<D, NT>(Kd, kbase + (long)key0 * stride, stride, tid);
-    dma_tile<D, NT>(Vd, vbase + (long)key0 * stride, stride, tid);
+    dma_tile<D, NT>(Kd, kbase + (long)key0 * stride, dmo, tid);
+    dma_tile<D, NT>(Vd, vbase + (long)key0 * stride, dmo, tid);
   } else {
     load_tile<D, NT>(Kd, kbase + (long)key0 * stride, stride, n - key0, tid);
     load_tile<D, NT>(Vd, vbase + (long)key0 * stride, stride, n - key0, tid);
@@ -399,46 +421,64 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   const float* kbar = a.kbar + (long)(b * a.Hk + g) * T * D;
   const int cnt = a.qcnt[(long)bh * T + qt];
   const uint16_t* list = a.qidx + ((long)bh * T + qt) * T;
+  LdsOffsets<D> lo;
+  lo.init(lane);
+  DmaOffsets<D, NT> dmo;
+  dmo.init(kvstride, tid);
 
   auto visit = [&](int it, const bf16* Kc, const bf16* Vc, const float* Bc, bf16* Kn, bf16* Vn, float* Bn) {
     const int kt = list[it];
     wait_vmem();
     __syncthreads();  // key tile kt staged in (Kc, Vc, Bc); stage n is free
-    if (it + 1 < cnt) stage_kvb<D, NT>(Kn, Vn, Bn, a, kbase, vbase, kbar, list[it + 1], tid);
+    if (it + 1 < cnt) stage_kvb<D, NT>(Kn, Vn, Bn, a, dmo, kbase, vbase, kbar, list[it + 1], tid);
     const int key0 = kt * TILE;
     const bool diag = CAUSAL && (qt == kt);
     const bool edge = key0 + TILE > n;
-    float losum = 0.f;  // sum over this wave's keys of (G_S - bf16(G_S)) for this row
-#pragma unroll 1
-    for (int kb = 0; kb < 4; ++kb) {
-      f32x16 s = f32x16{}, gp = f32x16{};
+    float losum = 0.f;  // sum over this tile's keys of (G_S - bf16(G_S)) for this row
+    // Per 32-key block kb: [S^T, G_P^T MFMAs] -> [G_S on the VALU] -> [G_Q MFMAs],
+    // software-pipelined over kb like the G_K/G_V pass.
+    auto mm_sdp = [&](int kb, f32x16& sv, f32x16& gv) {
+      sv = f32x16{};
+      gv = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        s = mfma32(lds_row8<D>(Kc, kb * 32 + l32, 2 * ks + h32), qf[ks], s);
-        gp = mfma32(lds_row8<D>(Vc, kb * 32 + l32, 2 * ks + h32), gf[ks], gp);
+        sv = mfma32(rd_row<D>(Kc, lo, kb, ks), qf[ks], sv);
+        gv = mfma32(rd_row<D>(Vc, lo, kb, ks), gf[ks], gv);
       }
+    };
+    auto soft = [&](int kb, const f32x16& sv, f32x16& gv) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = exp2f(fmaf(s[r], c, -lse2));
+        float pv = fast_exp2(fmaf(sv[r], c, -lse2));
         if (diag || edge) {
           const int kk2 = key0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
           if (kk2 >= n || (diag && kk2 > qrow)) pv = 0.f;
         }
-        gp[r] = pv * (gp[r] - dl);
+        gv[r] = pv * (gv[r] - dl);
       }
-      // G_Q^T += K^T G_S^T; step st covers keys 32kb + 16st + 4*h32 + 0..3 and +8
+    };
+    // G_Q^T += K^T G_S^T; step st covers keys 32kb + 16st + 4*h32 + 0..3 and +8
+    auto mm_dq = [&](int kb, const f32x16& gv) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8 sb = pack8_lo(gp, st, losum);
-        const int k0 = kb * 32 + st * 16 + 4 * h32;
+        const bf16x8 sb = pack8_lo(gv, st, losum);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
-          const bf16x8 ka = cat8(lds_tr4<D>(Kc, k0, n0, lane), lds_tr4<D>(Kc, k0 + 8, n0, lane));
-          dq[db] = mfma32(ka, sb, dq[db]);
-        }
+        for (int db = 0; db < NDB; ++db) dq[db] = mfma32(rd_tr<D>(Kc, lo, kb, st, db), sb, dq[db]);
       }
-    }
+    };
+    f32x16 sA, gA, sB, gB;
+    mm_sdp(0, sA, gA);
+    mm_sdp(1, sB, gB);
+    soft(0, sA, gA);
+    mm_dq(0, gA);
+    mm_sdp(2, sA, gA);
+    soft(1, sB, gB);
+    mm_dq(1, gB);
+    mm_sdp(3, sB, gB);
+    soft(2, sA, gA);
+    mm_dq(2, gA);
+    soft(3, sB, gB);
+    mm_dq(3, gB);
     // Rounding compensation.  The MFMA used bf16(G_S); the residual
     // lo = G_S - bf16(G_S) contributes sum_j lo_ij K_j, whose dominant part when
     // the tile's keys share a large common vector is (sum_j lo_ij) * kbar.  Rows
@@ -456,7 +496,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
       }
   };
 
-  if (cnt > 0) stage_kvb<D, NT>(Ks0, Vs0, Kb0, a, kbase, vbase, kbar, list[0], tid);
+  if (cnt > 0) stage_kvb<D, NT>(Ks0, Vs0, Kb0, a, dmo, kbase, vbase, kbar, list[0], tid);
   for (int it = 0; it < cnt; it += 2) {
     visit(it, Ks0, Vs0, Kb0, Ks1, Vs1, Kb1);
     if (it + 1 < cnt) visit(it + 1, Ks1, Vs1, Kb1, Ks0, Vs0, Kb0);

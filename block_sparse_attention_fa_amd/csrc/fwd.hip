@@ -40,10 +40,10 @@ struct FwdArgs {
 // when the tile is full, else synchronously with zero-filled padding rows.
 template <int D, int NT>
 __device__ __forceinline__ void stage_kv(bf16* Ks, bf16* Vs, const uint16_t* kbase, const uint16_t* vbase,
-                                         long stride, int key0, int n, int tid) {
+                                         long stride, const DmaOffsets<D, NT>& dmo, int key0, int n, int tid) {
   if (key0 + TILE <= n) {
-    dma_tile<D, NT>(Ks, kbase + (long)key0 * stride, stride, tid);
-    dma_tile<D, NT>(Vs, vbase + (long)key0 * stride, stride, tid);
+    dma_tile<D, NT>(Ks, kbase + (long)key0 * stride, dmo, tid);
+    dma_tile<D, NT>(Vs, vbase + (long)key0 * stride, dmo, tid);
   } else {
     load_tile<D, NT>(Ks, kbase + (long)key0 * stride, stride, n - key0, tid);
     load_tile<D, NT>(Vs, vbase + (long)key0 * stride, stride, n - key0, tid);
@@ -111,6 +111,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     tl_row = a.tlse + (long)bh * pairs * TILE;
   }
   const float c = a.scale_log2;
+  LdsOffsets<D> lo;
+  lo.init(lane);
+  DmaOffsets<D, NT> dmo;
+  dmo.init(kvstride, tid);
 
   // one visit of key tile kt: prefetch tile kt+1 into the other stage, then
   // consume tile kt from (Kc, Vc).  Called with static stage arrays so that the
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   auto visit = [&](int kt, const bf16* Kc, const bf16* Vc, bf16* Kn, bf16* Vn) {
     wait_vmem();
     __syncthreads();  // tile kt is in (Kc, Vc); nobody reads (Kn, Vn) any more
-    if (kt + 1 < nkt) stage_kv<D, NT>(Kn, Vn, kbase, vbase, kvstride, (kt + 1) * TILE, n, tid);
+    if (kt + 1 < nkt) stage_kv<D, NT>(Kn, Vn, kbase, vbase, kvstride, dmo, (kt + 1) * TILE, n, tid);
     if (!active || (CAUSAL && kt > qt)) return;  // wave-uniform
     const int key0 = kt * TILE;
 
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)  // four independent accumulators back to back
-        s[kb] = mfma32(lds_row8<D>(Kc, kb * 32 + l32, 2 * ks + h32), qf[ks], s[kb]);
+        s[kb] = mfma32(rd_row<D>(Kc, lo, kb, ks), qf[ks], s[kb]);
     // mask padded keys (last tile) and, on the diagonal tile, keys after the row
     const bool need_mask = (key0 + TILE > n) || (CAUSAL && kt == qt);
     if (need_mask) {
@@ -150,13 +154,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt * c);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = fast_exp2(m_run - m_new);
     float ts = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = exp2f(fmaf(s[kb][r], c, -m_new));
+        const float pv = fast_exp2(fmaf(s[kb][r], c, -m_new));
         s[kb][r] = pv;
         ts += pv;
       }
@@ -176,17 +180,12 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const bf16x8 pb = pack8(s[kb], st);
-        const int k0 = kb * 32 + st * 16 + 4 * h32;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int n0 = db * 32 + 16 * ((lane >> 4) & 1);
-          const bf16x8 va = cat8(lds_tr4<D>(Vc, k0, n0, lane), lds_tr4<D>(Vc, k0 + 8, n0, lane));
-          oacc[db] = mfma32(va, pb, oacc[db]);
-        }
+        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(rd_tr<D>(Vc, lo, kb, st, db), pb, oacc[db]);
       }
   };
 
-  stage_kv<D, NT>(Ks0, Vs0, kbase, vbase, kvstride, 0, n, tid);
+  stage_kv<D, NT>(Ks0, Vs0, kbase, vbase, kvstride, dmo, 0, n, tid);
   for (int kt = 0; kt < nkt; kt += 2) {
     visit(kt, Ks0, Vs0, Ks1, Vs1);
     if (kt + 1 < nkt) visit(kt + 1, Ks1, Vs1, Ks0, Vs0);
