@@ -288,3 +288,98 @@ def cosine(a, ref):
     if na == 0 and nr == 0:
         return 1.0
     return float(a @ ref / (na * nr))
+
+
+# ----------------------------------------------------------------------------
+# sampled evaluation for long sequences
+# ----------------------------------------------------------------------------
+def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), k_tiles=(),
+                       scale=None, tile=TILE, block=TILE, all_rows=True, stats=None):
+    """The same definitions as forward / mask_from_stats / backward, evaluated
+    for one group of query heads sharing a kv head, but only for selected
+    outputs, so that long sequences stay tractable on the CPU.
+
+    For every query head h in `heads` (all must read the same kv head):
+      * pass 1, over every row when all_rows (else over the rows of q_tiles
+        only): row LSE, tile LSE and D = rowsum(G_O * O);
+      * the tile mask of the head from those statistics (rows of the query
+        tiles pass 1 did not visit stay all-False);
+      * O and G_Q of the rows of `q_tiles`;
+      * the head's contribution to G_K, G_V of the key rows of `k_tiles`
+        (requires all_rows), summed over `heads`.
+    `stats` (the "stats" entry of a previous call with the same inputs) skips
+    pass 1, e.g. to evaluate several negl_prob values.
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    assert B == 1, "sampled evaluation takes one sequence"
+    assert all_rows or not k_tiles, "key-tile gradients need every row's statistics"
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    g = kv_head(heads[0], H, Hk)
+    assert all(kv_head(h, H, Hk) == g for h in heads)
+    T = ntiles(n, tile)
+    cand = candidates(n, causal, tile)
+    kh, vh = k[0, :, g], v[0, :, g]
+    q_tiles, k_tiles = list(q_tiles), list(k_tiles)
+    out = {"keep": [], "lse": [], "tile_lse": [], "D": [], "O": [], "dQ": [], "stats": []}
+    dK = {kt: np.zeros((min(n, (kt + 1) * tile) - kt * tile, d)) for kt in k_tiles}
+    dV = {kt: np.zeros_like(dK[kt]) for kt in k_tiles}
+    p1_tiles = range(T) if all_rows else sorted(set(q_tiles))
+    for hi, h in enumerate(heads):
+        qh, doh = q[0, :, h], do[0, :, h]
+        if stats is None:
+            # pass 1: row statistics over the full key range
+            L = np.full(n, np.nan)
+            TL = np.full((n, T), -np.inf)
+            Dr = np.full(n, np.nan)
+            Oq = {}
+            for qt in p1_tiles:
+                r = np.arange(qt * tile, min(n, (qt + 1) * tile))
+                S = _score_block(qh, kh, r, scale, causal)
+                L[r] = _row_lse(S)
+                TL[r] = _tile_lse(S, n, tile)
+                O = np.exp(S - L[r][:, None]) @ vh
+                Dr[r] = (doh[r] * O).sum(axis=1)
+                if qt in q_tiles:
+                    Oq[qt] = O
+            st = {"L": L, "TL": TL, "D": Dr, "O": Oq}
+        else:
+            st = stats[hi]
+        L, TL, Dr, Oq = st["L"], st["TL"], st["D"], st["O"]
+        out["stats"].append(st)
+        # mask of the visited query tiles
+        a = tile_log_weights(np.where(np.isfinite(TL), TL, -np.inf)[None, None],
+                             np.where(np.isfinite(L), L, 0.0)[None, None], n, causal, tile)
+        cv = cand.copy()
+        visited = np.zeros(T, bool)
+        visited[list(p1_tiles)] = True
+        cv[~visited] = False
+        kp = select_keep(a, cv, negl_prob)[0, 0]
+        out["keep"].append(kp)
+        out["lse"].append(L)
+        out["tile_lse"].append(TL)
+        out["D"].append(Dr)
+        out["O"].append([Oq[qt] for qt in q_tiles])
+        # pass 2: G_Q rows of q_tiles, G_K/G_V contributions to k_tiles
+        for qt in q_tiles:
+            r = np.arange(qt * tile, min(n, (qt + 1) * tile))
+            S = _score_block(qh, kh, r, scale, causal)
+            P = np.exp(S - L[r][:, None])
+            M = kp[qt][np.arange(n) // tile][None, :]
+            dS = np.where(M, P, 0.0) * (doh[r] @ vh.T - Dr[r][:, None])
+            out["dQ"].append((h, qt, scale * (dS @ kh)))
+        for kt in k_tiles:
+            c = np.arange(kt * tile, min(n, (kt + 1) * tile))
+            for qt in np.nonzero(kp[:, kt])[0]:
+                r = np.arange(qt * tile, min(n, (qt + 1) * tile))
+                Sc = scale * (qh[r] @ kh[c].T)
+                if causal:
+                    Sc = np.where(c[None, :] <= r[:, None], Sc, -np.inf)
+                Pc = np.exp(Sc - L[r][:, None])
+                dSc = Pc * (doh[r] @ vh[c].T - Dr[r][:, None])
+                dK[kt] += scale * (dSc.T @ qh[r])
+                dV[kt] += Pc.T @ doh[r]
+    out["dK"] = dK
+    out["dV"] = dV
+    return out

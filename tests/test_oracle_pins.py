@@ -371,3 +371,46 @@ def test_metrics():
     assert orc.rel_l2(a, a) == 0.0 and orc.cosine(a, a) == pytest.approx(1.0)
     assert orc.rel_l2(2 * a, a) == pytest.approx(1.0)
     assert orc.cosine(-a, a) == pytest.approx(-1.0)
+
+
+def test_sampled_head_group_matches_full_oracle():
+    """The sampled evaluation reproduces the full oracle's rows and tiles."""
+    for causal, (H, Hk) in ((False, (2, 1)), (True, (3, 3))):
+        n, d = 300, 16
+        q, k, v, do = _rand((1, n, H, d), 60, 1.5), _rand((1, n, Hk, d), 61, 1.5), _rand((1, n, Hk, d), 62), _rand((1, n, H, d), 63)
+        heads = [0, 1] if Hk == 1 else [1]
+        f = orc.forward(q, k, v, causal=causal, tile=64)
+        keep = orc.mask_from_stats(f["tile_lse"], f["lse"], n, causal, 0.2, tile=64)
+        g = orc.backward(q, k, v, do, keep=keep, causal=causal, tile=64, heads=heads)
+        sp = orc.sampled_head_group(q, k, v, do, heads, 0.2, causal, q_tiles=[0, 2, 4], k_tiles=[0, 3, 4],
+                                    tile=64, block=64)
+        for hi, h in enumerate(heads):
+            assert (sp["keep"][hi] == keep[0, h]).all()
+            np.testing.assert_allclose(sp["lse"][hi], f["lse"][0, h], atol=1e-12)
+            np.testing.assert_allclose(sp["tile_lse"][hi], f["tile_lse"][0, h], atol=1e-12)
+            for j, qt in enumerate([0, 2, 4]):
+                r = slice(qt * 64, min(n, qt * 64 + 64))
+                np.testing.assert_allclose(sp["O"][hi][j], f["O"][0, r, h], atol=1e-12)
+        for (h, qt, dq) in sp["dQ"]:
+            r = slice(qt * 64, min(n, qt * 64 + 64))
+            np.testing.assert_allclose(dq, g["dQ"][0, r, heads.index(h)], atol=1e-11)
+        gk = orc.kv_head(heads[0], H, Hk)
+        for kt in (0, 3, 4):
+            r = slice(kt * 64, min(n, kt * 64 + 64))
+            np.testing.assert_allclose(sp["dK"][kt], g["dK"][0, r, gk], atol=1e-11)
+            np.testing.assert_allclose(sp["dV"][kt], g["dV"][0, r, gk], atol=1e-11)
+
+
+def test_sampled_rows_only_mode_and_stats_reuse():
+    n, d = 260, 8
+    q, k, v, do = _rand((1, n, 1, d), 70, 1.5), _rand((1, n, 1, d), 71, 1.5), _rand((1, n, 1, d), 72), _rand((1, n, 1, d), 73)
+    full = orc.sampled_head_group(q, k, v, do, [0], 0.1, True, q_tiles=[1, 4], k_tiles=[0], tile=64)
+    rows = orc.sampled_head_group(q, k, v, do, [0], 0.1, True, q_tiles=[1, 4], tile=64, all_rows=False)
+    for qt in (1, 4):
+        assert (rows["keep"][0][qt] == full["keep"][0][qt]).all()
+    for (h1, t1, a), (h2, t2, b) in zip(full["dQ"], rows["dQ"]):
+        assert t1 == t2
+        np.testing.assert_allclose(a, b, atol=1e-12)
+    again = orc.sampled_head_group(q, k, v, do, [0], 0.1, True, q_tiles=[1, 4], k_tiles=[0], tile=64,
+                                   stats=full["stats"])
+    np.testing.assert_allclose(again["dK"][0], full["dK"][0], atol=1e-12)
