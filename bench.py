@@ -47,7 +47,32 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=12288,
                     help="query rows of head 0 in the oracle's timed sample")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-backward comparison")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (scale for memory counters)")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("bwd.hip", "bl_device.h"):
+        with open(os.path.join(ROOT, "block_sparse_attention_fa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dK/dV kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"dkdv_{workload}_traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, x_h0, negl, rows):
@@ -121,6 +146,16 @@ def main():
     q, k, v, do = (x[nm].to(dev) for nm in ("q", "k", "v", "do"))
     del x
     T = (n + TILE - 1) // TILE
+
+    if args.copy_calibration_mib:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+        # scale between those counters and bytes moved
+        nb = args.copy_calibration_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # every buffer allocated once, outside the timed region
     tl = torch.empty(_lib.tile_lse_elems(B, H, n, causal), dtype=torch.float32, device=dev)
@@ -198,7 +233,8 @@ def main():
     dkdv_flop = kept * 8.0 * TILE * TILE * d
     achieved = dkdv_flop / (dkdv_ms * 1e-3) / 1e12 if dkdv_ms else None
     roofline = {"kernel": "dkdv", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS if achieved else None, "traffic": None}
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS if achieved else None,
+                "traffic": measured_traffic(w.name)}
 
     # mask algorithmic bytes: tile-LSE of every candidate pair (512 B), the row LSE
     # and D-like row data of each query tile, bitmap + list entries written

@@ -213,15 +213,12 @@ __device__ __forceinline__ void sched_interleave() {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// Map a hardware workgroup id to a logical work index so that consecutive
-// logical indices run on the same XCD (workgroups are dealt round-robin over
-// the 8 XCDs; each XCD has its own L2).
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
-  constexpr int NX = 8;
-  const int per = total / NX, rem = total % NX;
-  const int x = bid % NX, i = bid / NX;
-  return (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
-}
+// Work order.  Workgroups are dealt round-robin over the 8 XCDs (each with its
+// own L2); measured on MI355X, the plain order (consecutive workgroups = tiles
+// of the same head, so the whole chip works through one head's K/V or Q/G_O
+// at a time and the 256 MB Infinity Cache holds it) beats grouping each head
+// on one XCD by 20% in the backward, so no remapping is applied.
+__device__ __forceinline__ int work_index(int bid) { return bid; }
 
 __device__ __forceinline__ long pair_index(int qt, int kt, int T, bool causal) {
   return causal ? (long)qt * (qt + 1) / 2 + kt : (long)qt * T + kt;

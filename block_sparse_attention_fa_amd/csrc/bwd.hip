@@ -176,8 +176,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Ds1[TILE];
 
   const int T = a.T, n = a.n;
-  const int total = a.B * a.Hk * T;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = work_index(blockIdx.x);
   const int kt = L % T;
   const int bg = L / T;
   const int g = bg % a.Hk, b = bg / a.Hk;
@@ -251,15 +250,25 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     // are issued before chunk qc's VALU work, so the matrix pipe stays busy
     // while the wave computes exponentials.
     auto mm_sdp = [&](int qc, f32x16& sv, f32x16& gv) {
+      bf16x8 qfr[NKS], gfr[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        qfr[ks] = rd_row<D>(Qc, lo, qc, ks);
+        gfr[ks] = rd_row<D>(Gc, lo, qc, ks);
+      }
       sv = f32x16{};
       gv = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        sv = mfma32(rd_row<D>(Qc, lo, qc, ks), kf[ks], sv);
-        gv = mfma32(rd_row<D>(Gc, lo, qc, ks), vf[ks], gv);
+        sv = mfma32(qfr[ks], kf[ks], sv);
+        gv = mfma32(gfr[ks], vf[ks], gv);
       }
+      sched_interleave<6, NKS - 3, 2, 2, 6>();
     };
     auto soft = [&](int qc, f32x16& sv, f32x16& gv) {
+      // register r holds query q0 + 32qc + 4*h32 + (8(r/4) + r%4); on the
+      // diagonal tile a key after the query is dropped
+      const int lim = key - (q0 + qc * 32 + 4 * h32);  // drop offsets < lim
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
         const int qr = qc * 32 + 8 * j4 + 4 * h32;  // local query row of registers 4j4..4j4+3
@@ -269,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         for (int t = 0; t < 4; ++t) {
           const int r = 4 * j4 + t;
           float pv = fast_exp2(fmaf(sv[r], c, -l4[t] * LOG2E));
-          if (diag && key > q0 + qr + t) pv = 0.f;
+          if (diag) pv = (8 * j4 + t >= lim) ? pv : 0.f;
           sv[r] = pv;
           gv[r] = pv * (gv[r] - d4[t]);
         }
@@ -278,16 +287,25 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     // G_V += P^T G_O and G_K += G_S^T Q; step st covers queries
     // 32qc + 16st + 4*h32 + 0..3 and 32qc + 16st + 8 + 4*h32 + 0..3
     auto mm_dvdk = [&](int qc, const f32x16& pv, const f32x16& sv) {
+      bf16x8 gb[2][NDB], qb[2][NDB];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          gb[st][db] = rd_tr<D>(Gc, lo, qc, st, db);
+          qb[st][db] = rd_tr<D>(Qc, lo, qc, st, db);
+        }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const bf16x8 pa = pack8(pv, st);
         const bf16x8 sa = pack8(sv, st);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dv[db] = mfma32(pa, rd_tr<D>(Gc, lo, qc, st, db), dv[db]);
-          dk[db] = mfma32(sa, rd_tr<D>(Qc, lo, qc, st, db), dk[db]);
+          dv[db] = mfma32(pa, gb[st][db], dv[db]);
+          dk[db] = mfma32(sa, qb[st][db], dk[db]);
         }
       }
+      sched_interleave<8, 4 * NDB - 4, 1, 2, 4>();
     };
     f32x16 sA, gA, sB, gB;
     mm_sdp(0, sA, gA);
@@ -382,8 +400,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Kb1[D];
 
   const int T = a.T, n = a.n;
-  const int total = a.B * a.H * T;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = work_index(blockIdx.x);
   const int qt = L % T;
   const int bh = L / T;
   const int h = bh % a.H, b = bh / a.H;
@@ -438,33 +455,48 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
     // Per 32-key block kb: [S^T, G_P^T MFMAs] -> [G_S on the VALU] -> [G_Q MFMAs],
     // software-pipelined over kb like the G_K/G_V pass.
     auto mm_sdp = [&](int kb, f32x16& sv, f32x16& gv) {
+      bf16x8 kfr[NKS], vfr[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        kfr[ks] = rd_row<D>(Kc, lo, kb, ks);
+        vfr[ks] = rd_row<D>(Vc, lo, kb, ks);
+      }
       sv = f32x16{};
       gv = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        sv = mfma32(rd_row<D>(Kc, lo, kb, ks), qf[ks], sv);
-        gv = mfma32(rd_row<D>(Vc, lo, kb, ks), gf[ks], gv);
+        sv = mfma32(kfr[ks], qf[ks], sv);
+        gv = mfma32(vfr[ks], gf[ks], gv);
       }
+      sched_interleave<6, NKS - 3, 2, 2, 6>();
     };
     auto soft = [&](int kb, const f32x16& sv, f32x16& gv) {
+      // register r holds key key0 + 32kb + 4*h32 + (8(r/4) + r%4); a key is
+      // dropped when it is padding (>= n) or, on the diagonal, after the row
+      const int base = key0 + kb * 32 + 4 * h32;
+      const int lim = (diag ? min(n - 1, qrow) : n - 1) - base;  // keep offsets <= lim
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = fast_exp2(fmaf(sv[r], c, -lse2));
-        if (diag || edge) {
-          const int kk2 = key0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          if (kk2 >= n || (diag && kk2 > qrow)) pv = 0.f;
-        }
+        if (diag || edge) pv = (8 * (r >> 2) + (r & 3) <= lim) ? pv : 0.f;
         gv[r] = pv * (gv[r] - dl);
       }
     };
     // G_Q^T += K^T G_S^T; step st covers keys 32kb + 16st + 4*h32 + 0..3 and +8
     auto mm_dq = [&](int kb, const f32x16& gv) {
+      bf16x8 ka[2][NDB];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 sb = pack8_lo(gv, st, losum);
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) dq[db] = mfma32(rd_tr<D>(Kc, lo, kb, st, db), sb, dq[db]);
-      }
+        for (int db = 0; db < NDB; ++db) ka[st][db] = rd_tr<D>(Kc, lo, kb, st, db);
+      bf16x8 sb[2];
+      sb[0] = pack8_lo(gv, 0, losum);
+      sb[1] = pack8_lo(gv, 1, losum);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dq[db] = mfma32(ka[st][db], sb[st], dq[db]);
+      sched_interleave<6, 2 * NDB - 3, 1, 2, 3>();
     };
     f32x16 sA, gA, sB, gB;
     mm_sdp(0, sA, gA);

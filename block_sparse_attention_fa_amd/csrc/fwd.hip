@@ -65,8 +65,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
 
   const int T = a.T;
   const int T2 = (T + 1) / 2;
-  const int total = a.B * a.H * T2;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = work_index(blockIdx.x);
   int p = L % T2;
   if (CAUSAL) p = T2 - 1 - p;  // heaviest query tiles first
   const int bh = L / T2;

@@ -71,8 +71,7 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
   __shared__ int s_skip;
 
   const int T = a.T;
-  const int total = a.B * a.H * T;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = work_index(blockIdx.x);
   const int qt = L % T;
   const int bh = L / T;
   const int tid = threadIdx.x;
@@ -176,8 +175,7 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
 __global__ __launch_bounds__(MASK_NT) void mask_transpose_kernel(MaskArgs a) {
   __shared__ int red[MASK_NT / 64];
   const int T = a.T;
-  const int total = a.B * a.H * T;
-  const int L = xcd_remap(blockIdx.x, total);
+  const int L = work_index(blockIdx.x);
   const int kt = L % T;
   const int bh = L / T;
   const int tid = threadIdx.x;
