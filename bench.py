@@ -55,7 +55,7 @@ def parse():
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("bwd.hip", "bl_device.h"):
+    for f in ("bwd.hip", "bwd_common.h", "bl_device.h"):
         with open(os.path.join(ROOT, "block_sparse_attention_fa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

@@ -89,14 +89,14 @@ extern "C" {
 
 int backlite_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!on) drain();
+  if (!on) (void)drain();
   g_on.store(on ? 1 : 0);
   return BACKLITE_OK;
 }
 
 int backlite_profile_reset(void) {
   std::lock_guard<std::mutex> lk(g_mu);
-  drain();
+  (void)drain();
   std::memset(g_ms, 0, sizeof(g_ms));
   std::memset(g_count, 0, sizeof(g_count));
   return BACKLITE_OK;
