@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace backlite {
 
 typedef __bf16 bf16;
@@ -152,16 +154,52 @@ __device__ __forceinline__ void load_tile(bf16* tile, const uint16_t* src, long 
   }
 }
 
-// Asynchronous copy of a full [128 x D] bf16 tile (every row valid) from global
-// memory into a swizzled LDS tile with global_load_lds_dwordx4: each wave
-// instruction fills 64 consecutive 16-byte LDS slots (slot = lane), so lane l
-// fetches the global chunk that belongs at its slot, i.e. the inverse swizzle.
-// The per-thread source offsets depend only on the row stride and are computed
-// once.  Completion: s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
+// Asynchronous copies global -> LDS with the load-to-LDS instructions: the
+// wave's 64 lanes fill 64 consecutive LDS slots (slot = lane).  Two encodings:
+// the buffer form (buffer_load_dword{,x4} ... lds) and the global form
+// (global_load_lds_dword{,x4}).  With the buffer form the compiler keeps
+// counting LDS reads precisely while a copy is in flight; the global form
+// makes it wait for every outstanding LDS read at each use, so kernels whose
+// LDS reads are scheduled ahead of their MFMAs take the buffer form.
+// Completion either way: s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
+// raw buffer resource: stride 0, `range` bytes (loads at or past it read 0), dword format word
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t range = 0x7FFFFFFFu) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)range, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) char lds_byte;
+__device__ __forceinline__ lds_byte* lds_ptr(const void* p) { return (lds_byte*)(p); }
+
+#define BL_LOAD_LDS(BYTES)                                                                                 \
+  if constexpr (BUF) {                                                                                     \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, BYTES, boff, 0, 0, 0);                               \
+  } else {                                                                                                 \
+    __builtin_amdgcn_global_load_lds(                                                                      \
+        (__attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(base) + boff), lds, BYTES,  \
+        0, 0);                                                                                             \
+  }
+// one lane's share of a load-to-LDS instruction: bytes at base + boff land in
+// slot `lane` of the LDS block at lds
+template <bool BUF>
+__device__ __forceinline__ void load_lds16(const __amdgpu_buffer_rsrc_t& rs, const void* base, lds_byte* lds,
+                                           uint32_t boff) {
+  BL_LOAD_LDS(16)
+}
+template <bool BUF>
+__device__ __forceinline__ void load_lds4(const __amdgpu_buffer_rsrc_t& rs, const void* base, lds_byte* lds,
+                                          uint32_t boff) {
+  BL_LOAD_LDS(4)
+}
+#undef BL_LOAD_LDS
+
+// Asynchronous copy of a full [128 x D] bf16 tile (every row valid) into a
+// swizzled LDS tile: lane l fetches the global chunk that belongs at its slot,
+// i.e. the inverse swizzle.  The per-thread source offsets depend only on the
+// row stride and are computed once.
 template <int D, int NT>
 struct DmaOffsets {
   static constexpr int NI = TILE * (D / 8) / NT;  // instructions per thread per tile
-  uint32_t off[NI];                               // element offsets within the source tile
+  uint32_t off[NI];                               // byte offsets within the source tile
   __device__ __forceinline__ void init(long stride, int tid) {
     constexpr int CH = D / 8;
     constexpr int NW = NT / 64;
@@ -170,29 +208,29 @@ struct DmaOffsets {
     for (int i = 0; i < NI; ++i) {
       const int s = (i * NW + wave) * 64 + lane;
       const int row = s / CH, pch = s % CH;
-      off[i] = (uint32_t)(row * stride + ((pch ^ swz<D>(row)) << 3));
+      off[i] = (uint32_t)(row * stride + ((pch ^ swz<D>(row)) << 3)) * 2u;
     }
   }
 };
 
-template <int D, int NT>
+template <int D, int NT, bool BUF>
 __device__ __forceinline__ void dma_tile(bf16* tile, const uint16_t* src, const DmaOffsets<D, NT>& o, int tid) {
   constexpr int NW = NT / 64;
   const int wave = tid >> 6;
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src);
 #pragma unroll
   for (int i = 0; i < DmaOffsets<D, NT>::NI; ++i) {
     const int slot0 = (i * NW + wave) * 64;  // first slot of this wave instruction
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + o.off[i]),
-                                     (__attribute__((address_space(3))) void*)(tile + slot0 * 8), 16, 0, 0);
+    load_lds16<BUF>(rs, src, lds_ptr(tile + slot0 * 8), o.off[i]);
   }
 }
 
 // Asynchronous copy of n32 4-byte words (n32 a multiple of 64) into LDS by one
 // wave: lane l of instruction i lands word 64i + l.
+template <bool BUF>
 __device__ __forceinline__ void dma_words(float* lds, const float* src, int n32, int lane) {
-  for (int i = 0; i < n32 / 64; ++i)
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 64 * i + lane),
-                                     (__attribute__((address_space(3))) void*)(lds + 64 * i), 4, 0, 0);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src);
+  for (int i = 0; i < n32 / 64; ++i) load_lds4<BUF>(rs, src, lds_ptr(lds + 64 * i), (uint32_t)(64 * i + lane) * 4u);
 }
 
 // Scheduling hints (instruction classes of __builtin_amdgcn_sched_group_barrier).
@@ -209,6 +247,17 @@ __device__ __forceinline__ void sched_interleave() {
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, R, 0);
   }
   __builtin_amdgcn_sched_group_barrier(SG_MFMA, TAIL, 0);
+}
+
+// Compile-time loop: calls f(std::integral_constant<int, I>) for I = I0 .. N-1,
+// so every index inside f is a constant expression (a plain loop of this size
+// is not always unrolled, and a rolled loop indexes registers dynamically).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)

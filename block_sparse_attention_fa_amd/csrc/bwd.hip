@@ -121,11 +121,11 @@ __device__ __forceinline__ void stage_qg(bf16* Qd, bf16* Gd, float* Ld, float* D
   const uint16_t* qsrc = a.q + ((long)b * n + q0) * qstride + (long)h * D;
   const uint16_t* gsrc = a.dout + ((long)b * n + q0) * qstride + (long)h * D;
   if (q0 + TILE <= n) {
-    dma_tile<D, NT>(Qd, qsrc, dmo, tid);
-    dma_tile<D, NT>(Gd, gsrc, dmo, tid);
+    dma_tile<D, NT, true>(Qd, qsrc, dmo, tid);
+    dma_tile<D, NT, true>(Gd, gsrc, dmo, tid);
     const int wave = tid >> 6, lane = tid & 63;
-    if (wave == 0) dma_words(Ld, a.lse + bh * n + q0, TILE, lane);
-    if (wave == 1) dma_words(Dd, a.dbuf + bh * n + q0, TILE, lane);
+    if (wave == 0) dma_words<true>(Ld, a.lse + bh * n + q0, TILE, lane);
+    if (wave == 1) dma_words<true>(Dd, a.dbuf + bh * n + q0, TILE, lane);
   } else {
     load_tile<D, NT>(Qd, qsrc, qstride, n - q0, tid);
     load_tile<D, NT>(Gd, gsrc, qstride, n - q0, tid);
@@ -142,6 +142,17 @@ __device__ __forceinline__ void stage_qg(bf16* Qd, bf16* Gd, float* Ld, float* D
 // the tile; their K, V fragments and G_K, G_V accumulators stay in registers.
 // The next listed query tile is copied into the other LDS stage while the
 // current one is consumed.
+// Issue order of one dK/dV tile: 8 phases of MFMAs, A0 A1 B0 A2 B1 A3 B2 B3,
+// where A(c) forms S and G_P of 32-query chunk c and B(c) accumulates G_V and
+// G_K from that chunk; the softmax of chunk c runs in the phase after A(c).
+__host__ __device__ constexpr bool dkdv_is_b(int ph) { return (0xD4 >> ph) & 1; }
+__host__ __device__ constexpr int dkdv_chunk(int ph) {
+  return ph == 0 ? 0 : ph == 1 ? 1 : ph == 2 ? 0 : ph == 3 ? 2 : ph == 4 ? 1 : ph == 5 ? 3 : ph == 6 ? 2 : 3;
+}
+__host__ __device__ constexpr int dkdv_soft(int ph) {  // chunk whose softmax runs in phase ph, or -1
+  return ph == 1 ? 0 : ph == 2 ? 1 : ph == 4 ? 2 : ph == 6 ? 3 : -1;
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int NT = 256;
@@ -163,7 +174,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   const int g = bg % a.Hk, b = bg / a.Hk;
   const int G = a.H / a.Hk;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index as a scalar: branches and LDS copy destinations built from it stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5;
   const int kw = wave;
   const int key = kt * TILE + kw * 32 + l32;  // this lane's key (B-operand column)
@@ -215,8 +227,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     skip_empty(s);
   };
 
-  auto visit = [&](int j, const bf16* Qc, const bf16* Gc, const float* Lc, const float* Dc, bf16* Qn,
-                   bf16* Gn, float* Ln, float* Dn) {
+  // stage S (a compile-time 0 or 1) holds item j; the other stage receives j + 1
+  auto visit = [&](int j, auto stage) {
+    constexpr int S = decltype(stage)::value;
+    const bf16* Qc = S ? Qs1 : Qs0;
+    const bf16* Gc = S ? Gs1 : Gs0;
+    const float* Lc = S ? Ls1 : Ls0;
+    const float* Dc = S ? Ds1 : Ds0;
+    bf16* Qn = S ? Qs0 : Qs1;
+    bf16* Gn = S ? Gs0 : Gs1;
+    float* Ln = S ? Ls0 : Ls1;
+    float* Dn = S ? Ds0 : Ds1;
     const int qt = qt_of(cur);
     wait_vmem();
     __syncthreads();  // item j staged in (Qc, Gc, Lc, Dc); stage n is free
@@ -225,90 +246,86 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       stage_qg<D, NT>(Qn, Gn, Ln, Dn, a, dmo, bh0 + nxt.hh, b, (int)(g * G + nxt.hh), qt_of(nxt), tid);
     }
     const int q0 = qt * TILE;
-    const bool diag = CAUSAL && (qt == kt);
-    // Per 32-query chunk qc: [S, G_P MFMAs] -> [P, G_S on the VALU] -> [G_V, G_K
-    // MFMAs].  The chunks are software-pipelined: chunk qc+1's S and G_P MFMAs
-    // are issued before chunk qc's VALU work, so the matrix pipe stays busy
-    // while the wave computes exponentials.
-    auto mm_sdp = [&](int qc, f32x16& sv, f32x16& gv) {
-      bf16x8 qfr[NKS], gfr[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        qfr[ks] = rd_row<D>(Qc, lo, qc, ks);
-        gfr[ks] = rd_row<D>(Gc, lo, qc, ks);
+    // on the diagonal tile a query row drops keys after it; elsewhere nothing
+    const int lim0 = (CAUSAL && qt == kt) ? key - (q0 + 4 * h32) : -(1 << 20);
+    // One tile = 8 phases of D/8 MFMAs: A(c) forms S and G_P of query
+    // chunk c (32 rows), B(c) accumulates G_V and G_K from chunk c's P and G_S.
+    // Issue order A0, A1, B0, A2, B1, A3, B2, B3; chunk c's softmax (exp, mask,
+    // G_S) is woven one element per MFMA into the phase after A(c), so the VALU
+    // work hides under the matrix pipe.  Operands stream through a 4-slot ring
+    // fetched 3 MFMAs ahead; sched_barrier fences keep that order.
+    constexpr int RING = 4, AHEAD = RING - 1;     // operand slots, MFMAs fetched ahead
+    constexpr int PH = D / 8;                      // MFMAs per phase (2 NKS = 4 NDB)
+    constexpr int NSTEP = 8 * PH, EPS = 16 / PH;  // softmax elements per MFMA
+    auto fetch = [&](auto kc) -> bf16x8 {
+      constexpr int k = decltype(kc)::value, ph = k / PH, st = k % PH, c4 = dkdv_chunk(ph);
+      if constexpr (dkdv_is_b(ph)) {
+        constexpr int sb = st >> 1;  // sub-step sb / NDB, head-dim block sb % NDB
+        return rd_tr<D>((st & 1) ? Qc : Gc, lo, c4, sb / NDB, sb % NDB);
+      } else {
+        return rd_row<D>((st & 1) ? Gc : Qc, lo, c4, st >> 1);
       }
-      sv = f32x16{};
-      gv = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        sv = mfma32(qfr[ks], kf[ks], sv);
-        gv = mfma32(gfr[ks], vf[ks], gv);
-      }
-      sched_interleave<6, NKS - 3, 2, 2, 6>();
     };
-    auto soft = [&](int qc, f32x16& sv, f32x16& gv) {
-      // register r holds query q0 + 32qc + 4*h32 + (8(r/4) + r%4); on the
-      // diagonal tile a key after the query is dropped
-      const int lim = key - (q0 + qc * 32 + 4 * h32);  // drop offsets < lim
+    f32x16 sacc[2], gacc[2];  // S and G_P (later P and G_S) of the two chunks in flight
+    bf16x8 pk[2][2], sk[2][2];  // packed bf16 P and G_S operands [chunk parity][sub-step]
+    f32x4 l4[4], d4[4];
+    bf16x8 ring[RING];
+    static_for<0, AHEAD>([&](auto kc) { ring[decltype(kc)::value] = fetch(kc); });
+    static_for<0, NSTEP>([&](auto kc) {
+      constexpr int k = decltype(kc)::value, ph = k / PH, st = k % PH, c4 = dkdv_chunk(ph);
+      constexpr int cs = dkdv_soft(ph);
+      if constexpr (k + AHEAD < NSTEP)
+        ring[(k + AHEAD) % RING] = fetch(std::integral_constant<int, k + AHEAD>{});
+      if constexpr (st == 0 && !dkdv_is_b(ph)) {
+        sacc[c4 & 1] = f32x16{};
+        gacc[c4 & 1] = f32x16{};
+      }
+      if constexpr (st == 0 && cs >= 0) {
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int qr = qc * 32 + 8 * j4 + 4 * h32;  // local query row of registers 4j4..4j4+3
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lc + qr);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dc + qr);
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const int qr = cs * 32 + 8 * j4 + 4 * h32;
+          l4[j4] = *reinterpret_cast<const f32x4*>(Lc + qr);
+          d4[j4] = *reinterpret_cast<const f32x4*>(Dc + qr);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (dkdv_is_b(ph)) {
+        constexpr int sb = st >> 1, s2 = sb / NDB, db = sb % NDB;
+        if constexpr (st & 1) dk[db] = mfma32(sk[c4 & 1][s2], ring[k % RING], dk[db]);
+        else dv[db] = mfma32(pk[c4 & 1][s2], ring[k % RING], dv[db]);
+      } else {
+        if constexpr (st & 1) gacc[c4 & 1] = mfma32(ring[k % RING], vf[st >> 1], gacc[c4 & 1]);
+        else sacc[c4 & 1] = mfma32(ring[k % RING], kf[st >> 1], sacc[c4 & 1]);
+      }
+      if constexpr (cs >= 0) {
+        f32x16& sv = sacc[cs & 1];
+        f32x16& gv = gacc[cs & 1];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 4 * j4 + t;
-          float pv = fast_exp2(fmaf(sv[r], c, -l4[t] * LOG2E));
-          if (diag) pv = (8 * j4 + t >= lim) ? pv : 0.f;
+        for (int e = 0; e < EPS; ++e) {
+          // register r holds query q0 + 32cs + 4*h32 + 8(r/4) + r%4
+          const int r = st * EPS + e, j4 = r >> 2, t = r & 3;
+          float pv = fast_exp2(fmaf(sv[r], c, -l4[j4][t] * LOG2E));
+          if constexpr (CAUSAL) pv = (8 * j4 + t >= lim0 - cs * 32) ? pv : 0.f;
           sv[r] = pv;
-          gv[r] = pv * (gv[r] - d4[t]);
+          gv[r] = pv * (gv[r] - d4[j4][t]);
+        }
+        if constexpr (st == PH - 1) {
+          pk[cs & 1][0] = pack8(sv, 0);
+          pk[cs & 1][1] = pack8(sv, 1);
+          sk[cs & 1][0] = pack8(gv, 0);
+          sk[cs & 1][1] = pack8(gv, 1);
         }
       }
-    };
-    // G_V += P^T G_O and G_K += G_S^T Q; step st covers queries
-    // 32qc + 16st + 4*h32 + 0..3 and 32qc + 16st + 8 + 4*h32 + 0..3
-    auto mm_dvdk = [&](int qc, const f32x16& pv, const f32x16& sv) {
-      bf16x8 gb[2][NDB], qb[2][NDB];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          gb[st][db] = rd_tr<D>(Gc, lo, qc, st, db);
-          qb[st][db] = rd_tr<D>(Qc, lo, qc, st, db);
-        }
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 pa = pack8(pv, st);
-        const bf16x8 sa = pack8(sv, st);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = mfma32(pa, gb[st][db], dv[db]);
-          dk[db] = mfma32(sa, qb[st][db], dk[db]);
-        }
-      }
-      sched_interleave<8, 4 * NDB - 4, 1, 2, 4>();
-    };
-    f32x16 sA, gA, sB, gB;
-    mm_sdp(0, sA, gA);
-    mm_sdp(1, sB, gB);
-    soft(0, sA, gA);
-    mm_dvdk(0, sA, gA);
-    mm_sdp(2, sA, gA);
-    soft(1, sB, gB);
-    mm_dvdk(1, sB, gB);
-    mm_sdp(3, sB, gB);
-    soft(2, sA, gA);
-    mm_dvdk(2, sA, gA);
-    soft(3, sB, gB);
-    mm_dvdk(3, sB, gB);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     advance(cur);
   };
 
   if (nitems > 0)
     stage_qg<D, NT>(Qs0, Gs0, Ls0, Ds0, a, dmo, bh0 + cur.hh, b, (int)(g * G + cur.hh), qt_of(cur), tid);
   for (int j = 0; j < nitems; j += 2) {
-    visit(j, Qs0, Gs0, Ls0, Ds0, Qs1, Gs1, Ls1, Ds1);
-    if (j + 1 < nitems) visit(j + 1, Qs1, Gs1, Ls1, Ds1, Qs0, Gs0, Ls0, Ds0);
+    visit(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nitems) visit(j + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: stage as [key][dim] bf16 and store coalesced rows.

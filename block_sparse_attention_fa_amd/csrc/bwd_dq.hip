@@ -21,13 +21,13 @@ __device__ __forceinline__ void stage_kvb(bf16* Kd, bf16* Vd, float* Bd, const B
   const long stride = (long)a.Hk * D;
   const int key0 = kt * TILE;
   if (key0 + TILE <= n) {
-    dma_tile<D, NT>(Kd, kbase + (long)key0 * stride, dmo, tid);
-    dma_tile<D, NT>(Vd, vbase + (long)key0 * stride, dmo, tid);
+    dma_tile<D, NT, false>(Kd, kbase + (long)key0 * stride, dmo, tid);
+    dma_tile<D, NT, false>(Vd, vbase + (long)key0 * stride, dmo, tid);
   } else {
     load_tile<D, NT>(Kd, kbase + (long)key0 * stride, stride, n - key0, tid);
     load_tile<D, NT>(Vd, vbase + (long)key0 * stride, stride, n - key0, tid);
   }
-  if ((tid >> 6) == 0) dma_words(Bd, kbar + (long)kt * D, D, tid & 63);
+  if ((tid >> 6) == 0) dma_words<false>(Bd, kbar + (long)kt * D, D, tid & 63);
 }
 
 // One workgroup of 4 waves (one per SIMD) per (b, h, query tile qt).  Wave w

@@ -42,8 +42,8 @@ template <int D, int NT>
 __device__ __forceinline__ void stage_kv(bf16* Ks, bf16* Vs, const uint16_t* kbase, const uint16_t* vbase,
                                          long stride, const DmaOffsets<D, NT>& dmo, int key0, int n, int tid) {
   if (key0 + TILE <= n) {
-    dma_tile<D, NT>(Ks, kbase + (long)key0 * stride, dmo, tid);
-    dma_tile<D, NT>(Vs, vbase + (long)key0 * stride, dmo, tid);
+    dma_tile<D, NT, false>(Ks, kbase + (long)key0 * stride, dmo, tid);
+    dma_tile<D, NT, false>(Vs, vbase + (long)key0 * stride, dmo, tid);
   } else {
     load_tile<D, NT>(Ks, kbase + (long)key0 * stride, stride, n - key0, tid);
     load_tile<D, NT>(Vs, vbase + (long)key0 * stride, stride, n - key0, tid);
