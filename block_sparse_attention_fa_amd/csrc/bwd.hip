@@ -104,37 +104,42 @@ __global__ __launch_bounds__(256) void kmean_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // G_K, G_V
 // ---------------------------------------------------------------------------
-// Work items of a (b, g, kt) workgroup: for each query head h of the group, the
-// kept query tiles of key tile kt in that head's k-list.
-struct KItems {
-  int hh, it, cnt;  // current head of the group, position in its list, list length
+// Sources of query tile qt of head h (Q, G_O rows; LSE, D words) as buffer
+// resources whose range ends after the last valid row: the rows of the ragged
+// last tile, and every row when `valid` is false, read as zero.  Zero rows
+// contribute nothing to G_K and G_V (their G_O and D are zero), so no other
+// padding is needed.
+struct QgSrc {
+  __amdgpu_buffer_rsrc_t q, g, l, d;
 };
-
-// Stage Q, G_O, LSE and D of query tile qt of head bh into LDS; asynchronously
-// for full tiles, synchronously (zero / +inf padding) for the ragged last one.
-template <int D, int NT>
-__device__ __forceinline__ void stage_qg(bf16* Qd, bf16* Gd, float* Ld, float* Dd, const BwdArgs& a,
-                                         const DmaOffsets<D, NT>& dmo, long bh, int b, int h, int qt, int tid) {
+template <int D>
+__device__ __forceinline__ QgSrc qg_src(const BwdArgs& a, long bh, int b, int h, int qt, bool valid) {
   const int n = a.n;
   const long qstride = (long)a.H * D;
   const int q0 = qt * TILE;
-  const uint16_t* qsrc = a.q + ((long)b * n + q0) * qstride + (long)h * D;
-  const uint16_t* gsrc = a.dout + ((long)b * n + q0) * qstride + (long)h * D;
-  if (q0 + TILE <= n) {
-    dma_tile<D, NT, true>(Qd, qsrc, dmo, tid);
-    dma_tile<D, NT, true>(Gd, gsrc, dmo, tid);
-    const int wave = tid >> 6, lane = tid & 63;
-    if (wave == 0) dma_words<true>(Ld, a.lse + bh * n + q0, TILE, lane);
-    if (wave == 1) dma_words<true>(Dd, a.dbuf + bh * n + q0, TILE, lane);
-  } else {
-    load_tile<D, NT>(Qd, qsrc, qstride, n - q0, tid);
-    load_tile<D, NT>(Gd, gsrc, qstride, n - q0, tid);
-    if (tid < TILE) {
-      const int i = q0 + tid;
-      Ld[tid] = (i < n) ? a.lse[bh * n + i] : INFINITY;
-      Dd[tid] = (i < n) ? a.dbuf[bh * n + i] : 0.f;
-    }
+  const uint32_t rows = valid ? (uint32_t)min(TILE, n - q0) : 0u;
+  const long off = ((long)b * n + q0) * qstride + (long)h * D;
+  const uint32_t bytes = rows * (uint32_t)qstride * 2u;
+  return QgSrc{buffer_rsrc(a.q + off, bytes), buffer_rsrc(a.dout + off, bytes),
+               buffer_rsrc(a.lse + bh * n + q0, rows * 4u), buffer_rsrc(a.dbuf + bh * n + q0, rows * 4u)};
+}
+
+// LSE and D words of a staged query tile: one instruction each, waves 0 and 1
+__device__ __forceinline__ void stage_ld(float* Ld, float* Dd, const QgSrc& s, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < TILE / 64; ++i) {
+    if (wave == 0) load_lds4<true>(s.l, nullptr, lds_ptr(Ld + 64 * i), (uint32_t)(64 * i + lane) * 4u);
+    if (wave == 1) load_lds4<true>(s.d, nullptr, lds_ptr(Dd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
   }
+}
+
+// Copy instruction i (of 2 NI) of a staged query tile: Q rows, then G_O rows.
+template <int D, int NT, int I>
+__device__ __forceinline__ void stage_qg_part(bf16* Qd, bf16* Gd, const QgSrc& s, const DmaOffsets<D, NT>& dmo,
+                                              int wave) {
+  constexpr int NI = DmaOffsets<D, NT>::NI, II = I % NI;
+  lds_byte* dst = lds_ptr((I < NI ? Qd : Gd) + ((II * (NT / 64) + wave) * 64) * 8);
+  load_lds16<true>(I < NI ? s.q : s.g, nullptr, dst, dmo.off[II]);
 }
 
 // One workgroup of 4 waves (one per SIMD, so each wave may hold up to 512
@@ -166,6 +171,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Ds0[TILE];
   __shared__ __attribute__((aligned(16))) float Ls1[TILE];
   __shared__ __attribute__((aligned(16))) float Ds1[TILE];
+  constexpr int ITAB = 2048;  // work-list window held in LDS
+  __shared__ uint32_t itab[ITAB];
 
   const int T = a.T, n = a.n;
   const int L = work_index(blockIdx.x);
@@ -207,26 +214,35 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   DmaOffsets<D, NT> dmo;
   dmo.init((long)a.H * D, tid);
 
-  // flattened work list over the group's heads
+  // Flattened work list over the group's heads: item p is (head hh of the
+  // group, query tile qt), heads in order, each head's k-list in order.  A
+  // window of ITAB items is kept in LDS as (hh << 16 | qt), so reading the next
+  // item is an LDS read, not a global load whose latency would stall the wave
+  // between a tile's barrier and the copy of the next tile.
   const long bh0 = (long)b * a.H + (long)g * G;
   int nitems = 0;
   for (int hh = 0; hh < G; ++hh) nitems += a.kcnt[(bh0 + hh) * T + kt];
-  KItems cur{0, 0, a.kcnt[bh0 * T + kt]};
-  auto skip_empty = [&](KItems& s) {
-    while (s.it >= s.cnt && s.hh + 1 < G) {
-      ++s.hh;
-      s.it = 0;
-      s.cnt = a.kcnt[(bh0 + s.hh) * T + kt];
+  auto fill_items = [&](int base) {  // items [base, base + ITAB) of the list, all threads
+    int p0 = 0;
+    for (int hh = 0; hh < G && p0 < base + ITAB; ++hh) {
+      const long row = ((bh0 + hh) * T + kt);
+      const int c = a.kcnt[row];
+      const int lo_p = max(base, p0), hi_p = min(base + ITAB, p0 + c);
+      for (int p = lo_p + tid; p < hi_p; p += NT) itab[p - base] = ((uint32_t)hh << 16) | a.kidx[row * T + (p - p0)];
+      p0 += c;
     }
   };
-  skip_empty(cur);
-  KItems nxt = cur;
-  auto qt_of = [&](const KItems& s) { return (int)a.kidx[((bh0 + s.hh) * T + kt) * T + s.it]; };
-  auto advance = [&](KItems& s) {
-    ++s.it;
-    skip_empty(s);
+  int ibase = 0;
+  fill_items(0);
+  __syncthreads();
+  struct Item {
+    int hh, qt;
   };
-
+  auto item_at = [&](int p) -> Item {  // p in [ibase, ibase + ITAB)
+    const uint32_t e = __builtin_amdgcn_readfirstlane(itab[p - ibase]);
+    return Item{(int)(e >> 16), (int)(e & 0xFFFFu)};
+  };
+  Item it_cur = item_at(0);
   // stage S (a compile-time 0 or 1) holds item j; the other stage receives j + 1
   auto visit = [&](int j, auto stage) {
     constexpr int S = decltype(stage)::value;
@@ -238,13 +254,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     bf16* Gn = S ? Gs0 : Gs1;
     float* Ln = S ? Ls0 : Ls1;
     float* Dn = S ? Ds0 : Ds1;
-    const int qt = qt_of(cur);
+    const int qt = it_cur.qt;
     wait_vmem();
     __syncthreads();  // item j staged in (Qc, Gc, Lc, Dc); stage n is free
-    if (j + 1 < nitems) {
-      advance(nxt);
-      stage_qg<D, NT>(Qn, Gn, Ln, Dn, a, dmo, bh0 + nxt.hh, b, (int)(g * G + nxt.hh), qt_of(nxt), tid);
+    if (j + 1 >= ibase + ITAB && j + 1 < nitems) {  // slide the item window
+      ibase += ITAB;
+      fill_items(ibase);
+      __syncthreads();
     }
+    const Item it_nxt = (j + 1 < nitems) ? item_at(j + 1) : it_cur;
+    // Stage item j + 1 into the free stage: its LSE and D words now, its Q and
+    // G_O rows one copy instruction every few MFMAs in the first part of this
+    // tile's stream (issued back to back they would stall the wave: the copy
+    // pipeline holds few requests while rows stream in from HBM).  Without a
+    // next item the copies read nothing and land zeros in the free stage.
+    const QgSrc nsrc = qg_src<D>(a, bh0 + it_nxt.hh, b, (int)(g * G + it_nxt.hh), it_nxt.qt, j + 1 < nitems);
+    stage_ld(Ln, Dn, nsrc, wave, lane);
     const int q0 = qt * TILE;
     // on the diagonal tile a query row drops keys after it; elsewhere nothing
     const int lim0 = (CAUSAL && qt == kt) ? key - (q0 + 4 * h32) : -(1 << 20);
@@ -257,6 +282,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     constexpr int RING = 4, AHEAD = RING - 1;     // operand slots, MFMAs fetched ahead
     constexpr int PH = D / 8;                      // MFMAs per phase (2 NKS = 4 NDB)
     constexpr int NSTEP = 8 * PH, EPS = 16 / PH;  // softmax elements per MFMA
+    constexpr int NI = DmaOffsets<D, NT>::NI;
+    constexpr int DSTEP = NSTEP / (2 * 2 * NI);   // the 2 NI copies span the first half
     auto fetch = [&](auto kc) -> bf16x8 {
       constexpr int k = decltype(kc)::value, ph = k / PH, st = k % PH, c4 = dkdv_chunk(ph);
       if constexpr (dkdv_is_b(ph)) {
@@ -276,6 +303,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       constexpr int cs = dkdv_soft(ph);
       if constexpr (k + AHEAD < NSTEP)
         ring[(k + AHEAD) % RING] = fetch(std::integral_constant<int, k + AHEAD>{});
+      if constexpr (k % DSTEP == 0 && k / DSTEP < 2 * NI) stage_qg_part<D, NT, k / DSTEP>(Qn, Gn, nsrc, dmo, wave);
       if constexpr (st == 0 && !dkdv_is_b(ph)) {
         sacc[c4 & 1] = f32x16{};
         gacc[c4 & 1] = f32x16{};
@@ -318,15 +346,23 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    advance(cur);
+    it_cur = it_nxt;
   };
 
-  if (nitems > 0)
-    stage_qg<D, NT>(Qs0, Gs0, Ls0, Ds0, a, dmo, bh0 + cur.hh, b, (int)(g * G + cur.hh), qt_of(cur), tid);
-  for (int j = 0; j < nitems; j += 2) {
-    visit(j, std::integral_constant<int, 0>{});
-    if (j + 1 < nitems) visit(j + 1, std::integral_constant<int, 1>{});
+  {
+    const QgSrc s0 = qg_src<D>(a, bh0 + it_cur.hh, b, (int)(g * G + it_cur.hh), it_cur.qt, nitems > 0);
+    stage_ld(Ls0, Ds0, s0, wave, lane);
+    static_for<0, 2 * DmaOffsets<D, NT>::NI>([&](auto ic) { stage_qg_part<D, NT, decltype(ic)::value>(Qs0, Gs0, s0, dmo, wave); });
   }
+  // pairs of items (stage 0, then stage 1), then the odd one out: no branch
+  // between the two visits of an iteration, so the accumulators keep one
+  // register assignment around the loop
+  int j = 0;
+  for (; j + 1 < nitems; j += 2) {
+    visit(j, std::integral_constant<int, 0>{});
+    visit(j + 1, std::integral_constant<int, 1>{});
+  }
+  if (j < nitems) visit(j, std::integral_constant<int, 0>{});
 
   // epilogue: stage as [key][dim] bf16 and store coalesced rows.
   // C layout: [key = 8(r/4) + 4*h32 + r%4 of block kw][dim = 32db + l32].
