@@ -12,23 +12,69 @@ namespace backlite {
 // ---------------------------------------------------------------------------
 // G_Q
 // ---------------------------------------------------------------------------
-// Stage K, V and the key mean of key tile kt into LDS.
-template <int D, int NT>
-__device__ __forceinline__ void stage_kvb(bf16* Kd, bf16* Vd, float* Bd, const BwdArgs& a, const DmaOffsets<D, NT>& dmo,
-                                          const uint16_t* kbase, const uint16_t* vbase, const float* kbar, int kt,
-                                          int tid) {
-  const int n = a.n;
-  const long stride = (long)a.Hk * D;
+// Sources of key tile kt (K, V rows; the key mean) as buffer resources whose
+// range ends after the last valid row: the rows of the ragged last tile, and
+// everything when `valid` is false, read as zero.  Keys past the end are also
+// masked out of P, so their zero rows never matter.
+struct KvSrc {
+  __amdgpu_buffer_rsrc_t k, v, m;
+};
+template <int D>
+__device__ __forceinline__ KvSrc kv_src(const uint16_t* kbase, const uint16_t* vbase, const float* kbar, long stride,
+                                        int n, int kt, bool valid) {
   const int key0 = kt * TILE;
-  if (key0 + TILE <= n) {
-    dma_tile<D, NT, false>(Kd, kbase + (long)key0 * stride, dmo, tid);
-    dma_tile<D, NT, false>(Vd, vbase + (long)key0 * stride, dmo, tid);
-  } else {
-    load_tile<D, NT>(Kd, kbase + (long)key0 * stride, stride, n - key0, tid);
-    load_tile<D, NT>(Vd, vbase + (long)key0 * stride, stride, n - key0, tid);
-  }
-  if ((tid >> 6) == 0) dma_words<false>(Bd, kbar + (long)kt * D, D, tid & 63);
+  const uint32_t rows = valid ? (uint32_t)min(TILE, n - key0) : 0u;
+  const uint32_t bytes = rows * (uint32_t)stride * 2u;
+  return KvSrc{buffer_rsrc(kbase + (long)key0 * stride, bytes), buffer_rsrc(vbase + (long)key0 * stride, bytes),
+               buffer_rsrc(kbar + (long)kt * D, valid ? (uint32_t)D * 4u : 0u)};
 }
+
+// copy instruction I (of 2 NI) of a staged key tile: K rows, then V rows
+template <int D, int NT, int I>
+__device__ __forceinline__ void stage_kv_part(bf16* Kd, bf16* Vd, const KvSrc& s, const DmaOffsets<D, NT>& dmo,
+                                              int wave) {
+  constexpr int NI = DmaOffsets<D, NT>::NI, II = I % NI;
+  lds_byte* dst = lds_ptr((I < NI ? Kd : Vd) + ((II * (NT / 64) + wave) * 64) * 8);
+  load_lds16<true>(I < NI ? s.k : s.v, nullptr, dst, dmo.off[II]);
+}
+
+// the key mean of a staged key tile: wave 0, D / 64 instructions
+template <int D>
+__device__ __forceinline__ void stage_kbar(float* Bd, const KvSrc& s, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i)
+    if (wave == 0) load_lds4<true>(s.m, nullptr, lds_ptr(Bd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
+}
+
+// Issue order of one key tile: 8 phases, A0 A1 B0 A2 B1 A3 B2 B3, where A(c)
+// (LA MFMAs) forms S^T and G_P^T of 32-key chunk c and B(c) (LB MFMAs)
+// accumulates G_Q^T from that chunk's G_S.  The softmax of chunk c runs
+// between the end of A(c) and the start of B(c), its 16 elements spread evenly
+// over the MFMAs issued there.
+template <int LA, int LB>
+struct DqSched {
+  static constexpr bool is_b(int ph) { return (0xD4 >> ph) & 1; }
+  static constexpr int chunk(int ph) {
+    return ph == 0 ? 0 : ph == 1 ? 1 : ph == 2 ? 0 : ph == 3 ? 2 : ph == 4 ? 1 : ph == 5 ? 3 : ph == 6 ? 2 : 3;
+  }
+  static constexpr int len(int ph) { return is_b(ph) ? LB : LA; }
+  static constexpr int start(int ph) {
+    int s = 0;
+    for (int i = 0; i < ph; ++i) s += len(i);
+    return s;
+  }
+  static constexpr int total = 4 * (LA + LB);
+  static constexpr int phase_of(int k) {
+    int ph = 0;
+    while (ph < 7 && start(ph + 1) <= k) ++ph;
+    return ph;
+  }
+  static constexpr int a_phase(int c) { return c == 0 ? 0 : c == 1 ? 1 : c == 2 ? 3 : 5; }
+  static constexpr int b_phase(int c) { return c == 0 ? 2 : c == 1 ? 4 : c == 2 ? 6 : 7; }
+  static constexpr int soft_begin(int c) { return start(a_phase(c)) + LA; }
+  static constexpr int soft_end(int c) { return start(b_phase(c)); }
+  static constexpr int elem_step(int c, int e) { return soft_begin(c) + e * (soft_end(c) - soft_begin(c)) / 16; }
+};
 
 // One workgroup of 4 waves (one per SIMD) per (b, h, query tile qt).  Wave w
 // owns query rows 32w .. +31: their Q, G_O fragments and the G_Q^T accumulator
@@ -45,6 +91,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE * D];
   __shared__ __attribute__((aligned(16))) float Kb0[D];
   __shared__ __attribute__((aligned(16))) float Kb1[D];
+  __shared__ uint16_t itab[MAX_TILES];  // this query tile's q-list
 
   const int T = a.T, n = a.n;
   const int L = work_index(blockIdx.x);
@@ -53,7 +100,8 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   const int h = bh % a.H, b = bh / a.H;
   const int g = h / (a.H / a.Hk);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index as a scalar: branches and LDS copy destinations built from it stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5;
   const int lrow = wave * 32 + l32;
   const int qrow = qt * TILE + lrow;
@@ -84,80 +132,107 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   const uint16_t* vbase = a.v + ((long)b * n) * kvstride + (long)g * D;
   const float* kbar = a.kbar + (long)(b * a.Hk + g) * T * D;
   const int cnt = a.qcnt[(long)bh * T + qt];
-  const uint16_t* list = a.qidx + ((long)bh * T + qt) * T;
+  {
+    // the q-list in LDS: reading the next key tile is then an LDS read, not a
+    // global load whose latency would stall the wave before the next copy
+    const uint16_t* list = a.qidx + ((long)bh * T + qt) * T;
+    for (int i = tid; i < cnt; i += NT) itab[i] = list[i];
+  }
   LdsOffsets<D> lo;
   lo.init(lane);
   DmaOffsets<D, NT> dmo;
   dmo.init(kvstride, tid);
+  __syncthreads();
+  int kt_cur = (cnt > 0) ? (int)__builtin_amdgcn_readfirstlane(itab[0]) : 0;
 
-  auto visit = [&](int it, const bf16* Kc, const bf16* Vc, const float* Bc, bf16* Kn, bf16* Vn, float* Bn) {
-    const int kt = list[it];
+  using SC = DqSched<2 * NKS, 2 * NDB>;
+  constexpr int NSTEP = SC::total;
+  constexpr int NI = DmaOffsets<D, NT>::NI;
+  constexpr int DSTEP = NSTEP / (2 * 2 * NI);  // the 2 NI copies span the first half
+  constexpr int RING = 4, AHEAD = RING - 1;    // operand slots, MFMAs fetched ahead
+
+  // stage S (a compile-time 0 or 1) holds item j; the other stage receives j + 1
+  auto visit = [&](int j, auto stage) {
+    constexpr int S = decltype(stage)::value;
+    const bf16* Kc = S ? Ks1 : Ks0;
+    const bf16* Vc = S ? Vs1 : Vs0;
+    const float* Bc = S ? Kb1 : Kb0;
+    bf16* Kn = S ? Ks0 : Ks1;
+    bf16* Vn = S ? Vs0 : Vs1;
+    float* Bn = S ? Kb0 : Kb1;
+    const int kt = kt_cur;
     wait_vmem();
     __syncthreads();  // key tile kt staged in (Kc, Vc, Bc); stage n is free
-    if (it + 1 < cnt) stage_kvb<D, NT>(Kn, Vn, Bn, a, dmo, kbase, vbase, kbar, list[it + 1], tid);
+    // Stage item j + 1: its key mean now, its K and V rows one copy instruction
+    // every few MFMAs in the first half of this tile's stream (issued back to
+    // back they would stall the wave).  Without a next item the copies read
+    // nothing and land zeros in the free stage.
+    const bool more = j + 1 < cnt;
+    const int kt_nxt = more ? (int)__builtin_amdgcn_readfirstlane(itab[j + 1]) : kt;
+    const KvSrc nsrc = kv_src<D>(kbase, vbase, kbar, kvstride, n, kt_nxt, more);
+    stage_kbar<D>(Bn, nsrc, wave, lane);
+
     const int key0 = kt * TILE;
+    // register r of chunk kb holds key key0 + 32kb + 4*h32 + 8(r/4) + r%4; a key
+    // is dropped when it is padding (>= n) or, on the diagonal, after the row
     const bool diag = CAUSAL && (qt == kt);
     const bool edge = key0 + TILE > n;
-    float losum = 0.f;  // sum over this tile's keys of (G_S - bf16(G_S)) for this row
-    // Per 32-key block kb: [S^T, G_P^T MFMAs] -> [G_S on the VALU] -> [G_Q MFMAs],
-    // software-pipelined over kb like the G_K/G_V pass.
-    auto mm_sdp = [&](int kb, f32x16& sv, f32x16& gv) {
-      bf16x8 kfr[NKS], vfr[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        kfr[ks] = rd_row<D>(Kc, lo, kb, ks);
-        vfr[ks] = rd_row<D>(Vc, lo, kb, ks);
-      }
-      sv = f32x16{};
-      gv = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        sv = mfma32(kfr[ks], qf[ks], sv);
-        gv = mfma32(vfr[ks], gf[ks], gv);
-      }
-      sched_interleave<6, NKS - 3, 2, 2, 6>();
+    const int lim0 = (diag ? min(n - 1, qrow) : n - 1) - (key0 + 4 * h32);  // keep offsets <= lim0 - 32kb
+    auto fetch = [&](auto kc) -> bf16x8 {
+      constexpr int k = decltype(kc)::value, ph = SC::phase_of(k), st = k - SC::start(ph), cb = SC::chunk(ph);
+      if constexpr (SC::is_b(ph)) return rd_tr<D>(Kc, lo, cb, st / NDB, st % NDB);
+      else return rd_row<D>((st & 1) ? Vc : Kc, lo, cb, st >> 1);
     };
-    auto soft = [&](int kb, const f32x16& sv, f32x16& gv) {
-      // register r holds key key0 + 32kb + 4*h32 + (8(r/4) + r%4); a key is
-      // dropped when it is padding (>= n) or, on the diagonal, after the row
-      const int base = key0 + kb * 32 + 4 * h32;
-      const int lim = (diag ? min(n - 1, qrow) : n - 1) - base;  // keep offsets <= lim
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(sv[r], c, -lse2));
-        if (diag || edge) pv = (8 * (r >> 2) + (r & 3) <= lim) ? pv : 0.f;
-        gv[r] = pv * (gv[r] - dl);
+    f32x16 sacc[2], gacc[2];  // S^T and G_P^T (later P and G_S) of the two chunks in flight
+    bf16x8 sb[2][2];          // packed bf16 G_S^T operands [chunk parity][sub-step]
+    float csum = 0.f, bsum = 0.f;  // this row's sums over the tile's keys of G_S and of bf16(G_S)
+    bf16x8 ring[RING];
+    static_for<0, AHEAD>([&](auto kc) { ring[decltype(kc)::value] = fetch(kc); });
+    static_for<0, NSTEP>([&](auto kc) {
+      constexpr int k = decltype(kc)::value, ph = SC::phase_of(k), st = k - SC::start(ph), cb = SC::chunk(ph);
+      if constexpr (k + AHEAD < NSTEP)
+        ring[(k + AHEAD) % RING] = fetch(std::integral_constant<int, k + AHEAD>{});
+      if constexpr (k % DSTEP == 0 && k / DSTEP < 2 * NI) stage_kv_part<D, NT, k / DSTEP>(Kn, Vn, nsrc, dmo, wave);
+      if constexpr (st == 0 && !SC::is_b(ph)) {
+        sacc[cb & 1] = f32x16{};
+        gacc[cb & 1] = f32x16{};
       }
-    };
-    // G_Q^T += K^T G_S^T; step st covers keys 32kb + 16st + 4*h32 + 0..3 and +8
-    auto mm_dq = [&](int kb, const f32x16& gv) {
-      bf16x8 ka[2][NDB];
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SC::is_b(ph)) {
+        dq[st % NDB] = mfma32(ring[k % RING], sb[cb & 1][st / NDB], dq[st % NDB]);
+      } else {
+        if constexpr (st & 1) gacc[cb & 1] = mfma32(ring[k % RING], gf[st >> 1], gacc[cb & 1]);
+        else sacc[cb & 1] = mfma32(ring[k % RING], qf[st >> 1], sacc[cb & 1]);
+      }
+      // softmax elements whose turn is this MFMA
+      static_for<0, 4>([&](auto cc) {
+        constexpr int c4 = decltype(cc)::value;
+        static_for<0, 16>([&](auto ec) {
+          constexpr int r = decltype(ec)::value;
+          if constexpr (SC::elem_step(c4, r) == k) {
+            float pv = fast_exp2(fmaf(sacc[c4 & 1][r], c, -lse2));
+            if (diag || edge) pv = (8 * (r >> 2) + (r & 3) <= lim0 - 32 * c4) ? pv : 0.f;
+            const float gs = pv * (gacc[c4 & 1][r] - dl);
+            gacc[c4 & 1][r] = gs;
+            csum += gs;
+          }
+        });
+        if constexpr (SC::soft_end(c4) - 1 == k) {
+          sb[c4 & 1][0] = pack8(gacc[c4 & 1], 0);
+          sb[c4 & 1][1] = pack8(gacc[c4 & 1], 1);
+          // sum of the bf16 operands: pairs of bf16 dotted with (1, 1)
+          const bf16x2 one = {(bf16)1.f, (bf16)1.f};
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+          for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) ka[st][db] = rd_tr<D>(Kc, lo, kb, st, db);
-      bf16x8 sb[2];
-      sb[0] = pack8_lo(gv, 0, losum);
-      sb[1] = pack8_lo(gv, 1, losum);
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) dq[db] = mfma32(ka[st][db], sb[st], dq[db]);
-      sched_interleave<6, 2 * NDB - 3, 1, 2, 3>();
-    };
-    f32x16 sA, gA, sB, gB;
-    mm_sdp(0, sA, gA);
-    mm_sdp(1, sB, gB);
-    soft(0, sA, gA);
-    mm_dq(0, gA);
-    mm_sdp(2, sA, gA);
-    soft(1, sB, gB);
-    mm_dq(1, gB);
-    mm_sdp(3, sB, gB);
-    soft(2, sA, gA);
-    mm_dq(2, gA);
-    soft(3, sB, gB);
-    mm_dq(3, gB);
+            for (int u = 0; u < 4; ++u) {
+              const bf16x2 pr = {sb[c4 & 1][s2][2 * u], sb[c4 & 1][s2][2 * u + 1]};
+              bsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, bsum, false);
+            }
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
     // Rounding compensation.  The MFMA used bf16(G_S); the residual
     // lo = G_S - bf16(G_S) contributes sum_j lo_ij K_j, whose dominant part when
     // the tile's keys share a large common vector is (sum_j lo_ij) * kbar.  Rows
@@ -166,6 +241,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
     // sum_j lo_ij (K_j - kbar).  The rank-1 update kbar (x) losum is one MFMA per
     // 32-dim block whose A and B operands are zero except for contraction slot 0
     // (bf16 operands: the term is already a rounding-sized correction).
+    float losum = csum - bsum;
     losum += __shfl_xor(losum, 32);
     {
       bf16x8 bl = {};
@@ -177,13 +253,22 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
         dq[db] = mfma32(al, bl, dq[db]);
       }
     }
+    kt_cur = kt_nxt;
   };
 
-  if (cnt > 0) stage_kvb<D, NT>(Ks0, Vs0, Kb0, a, dmo, kbase, vbase, kbar, list[0], tid);
-  for (int it = 0; it < cnt; it += 2) {
-    visit(it, Ks0, Vs0, Kb0, Ks1, Vs1, Kb1);
-    if (it + 1 < cnt) visit(it + 1, Ks1, Vs1, Kb1, Ks0, Vs0, Kb0);
+  {
+    const KvSrc s0 = kv_src<D>(kbase, vbase, kbar, kvstride, n, kt_cur, cnt > 0);
+    stage_kbar<D>(Kb0, s0, wave, lane);
+    static_for<0, 2 * NI>([&](auto ic) { stage_kv_part<D, NT, decltype(ic)::value>(Ks0, Vs0, s0, dmo, wave); });
   }
+  // pairs of items (stage 0, then stage 1), then the odd one out: no branch
+  // between the two visits of an iteration
+  int j = 0;
+  for (; j + 1 < cnt; j += 2) {
+    visit(j, std::integral_constant<int, 0>{});
+    visit(j + 1, std::integral_constant<int, 1>{});
+  }
+  if (j < cnt) visit(j, std::integral_constant<int, 0>{});
 
   // epilogue: dq C layout is [dim = 32db + 8(r/4) + 4*h32 + r%4][query l32]
   wait_vmem();
@@ -191,10 +276,10 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int dim = db * 32 + 8 * j + 4 * h32;
-      bf16x4 w4 = {(bf16)(dq[db][4 * j] * a.scale), (bf16)(dq[db][4 * j + 1] * a.scale),
-                   (bf16)(dq[db][4 * j + 2] * a.scale), (bf16)(dq[db][4 * j + 3] * a.scale)};
+    for (int jj = 0; jj < 4; ++jj) {
+      const int dim = db * 32 + 8 * jj + 4 * h32;
+      bf16x4 w4 = {(bf16)(dq[db][4 * jj] * a.scale), (bf16)(dq[db][4 * jj + 1] * a.scale),
+                   (bf16)(dq[db][4 * jj + 2] * a.scale), (bf16)(dq[db][4 * jj + 3] * a.scale)};
       *reinterpret_cast<bf16x4*>(Vs0 + tile_off<D>(lrow, dim >> 3) + (dim & 7)) = w4;
     }
   __syncthreads();
