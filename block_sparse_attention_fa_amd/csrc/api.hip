@@ -22,7 +22,7 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       const uint16_t* olo, const uint16_t* dout, const float* lse, const int32_t* qcnt,
                       const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
                       int H, int Hk, int d, float scale, int causal, uint16_t* dq, uint16_t* dk,
-                      uint16_t* dv, float* dbuf, float* kbar, hipStream_t st);
+                      uint16_t* dv, float* dbuf, float* lse2, float* kbar, hipStream_t st);
 }  // namespace backlite
 
 namespace {
@@ -118,7 +118,7 @@ size_t delta_bytes(int B, int H, int n) { return round256((size_t)B * H * n * si
 
 size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d) {
   if (B < 1 || H < 1 || H_k < 1 || n < 1 || d < 1) return 0;
-  return delta_bytes(B, H, n) + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
+  return 2 * delta_bytes(B, H, n) + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
 }
 
 int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int n, int H,
@@ -208,6 +208,7 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
   return hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d,
                                          scale, causal ? 1 : 0, dQ, dK, dV, (float*)workspace,
                                          (float*)((char*)workspace + delta_bytes(B, H, n)),
+                                         (float*)((char*)workspace + 2 * delta_bytes(B, H, n)),
                                          (hipStream_t)stream),
                     "backlite_bwd launch");
 }

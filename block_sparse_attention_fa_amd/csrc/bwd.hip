@@ -61,7 +61,9 @@ __global__ __launch_bounds__(256) void delta_kernel(BwdArgs a) {
     const long bi = row / a.H;
     const int i = (int)(bi % a.n);
     const int b = (int)(bi / a.n);
-    a.dbuf[((long)b * a.H + h) * a.n + i] = acc;
+    const long ri = ((long)b * a.H + h) * a.n + i;
+    a.dbuf[ri] = acc;
+    a.lse2[ri] = a.lse[ri] * LOG2E;
   }
 }
 
@@ -121,7 +123,7 @@ __device__ __forceinline__ QgSrc qg_src(const BwdArgs& a, long bh, int b, int h,
   const long off = ((long)b * n + q0) * qstride + (long)h * D;
   const uint32_t bytes = rows * (uint32_t)qstride * 2u;
   return QgSrc{buffer_rsrc(a.q + off, bytes), buffer_rsrc(a.dout + off, bytes),
-               buffer_rsrc(a.lse + bh * n + q0, rows * 4u), buffer_rsrc(a.dbuf + bh * n + q0, rows * 4u)};
+               buffer_rsrc(a.lse2 + bh * n + q0, rows * 4u), buffer_rsrc(a.dbuf + bh * n + q0, rows * 4u)};
 }
 
 // LSE and D words of a staged query tile: one instruction each, waves 0 and 1
@@ -147,17 +149,6 @@ __device__ __forceinline__ void stage_qg_part(bf16* Qd, bf16* Gd, const QgSrc& s
 // the tile; their K, V fragments and G_K, G_V accumulators stay in registers.
 // The next listed query tile is copied into the other LDS stage while the
 // current one is consumed.
-// Issue order of one dK/dV tile: 8 phases of MFMAs, A0 A1 B0 A2 B1 A3 B2 B3,
-// where A(c) forms S and G_P of 32-query chunk c and B(c) accumulates G_V and
-// G_K from that chunk; the softmax of chunk c runs in the phase after A(c).
-__host__ __device__ constexpr bool dkdv_is_b(int ph) { return (0xD4 >> ph) & 1; }
-__host__ __device__ constexpr int dkdv_chunk(int ph) {
-  return ph == 0 ? 0 : ph == 1 ? 1 : ph == 2 ? 0 : ph == 3 ? 2 : ph == 4 ? 1 : ph == 5 ? 3 : ph == 6 ? 2 : 3;
-}
-__host__ __device__ constexpr int dkdv_soft(int ph) {  // chunk whose softmax runs in phase ph, or -1
-  return ph == 1 ? 0 : ph == 2 ? 1 : ph == 4 ? 2 : ph == 6 ? 3 : -1;
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int NT = 256;
@@ -273,20 +264,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     const int q0 = qt * TILE;
     // on the diagonal tile a query row drops keys after it; elsewhere nothing
     const int lim0 = (CAUSAL && qt == kt) ? key - (q0 + 4 * h32) : -(1 << 20);
-    // One tile = 8 phases of D/8 MFMAs: A(c) forms S and G_P of query
-    // chunk c (32 rows), B(c) accumulates G_V and G_K from chunk c's P and G_S.
-    // Issue order A0, A1, B0, A2, B1, A3, B2, B3; chunk c's softmax (exp, mask,
-    // G_S) is woven one element per MFMA into the phase after A(c), so the VALU
-    // work hides under the matrix pipe.  Operands stream through a 4-slot ring
-    // fetched 3 MFMAs ahead; sched_barrier fences keep that order.
+    // One tile: A(c) forms S and G_P of query chunk c (32 rows), B(c)
+    // accumulates G_V and G_K from chunk c's P and G_S, in the order of
+    // TileSched; chunk c's softmax (exp, mask, G_S) is spread over the MFMAs
+    // between A(c) and B(c) so the VALU work hides under the matrix pipe.
+    // Operands stream through a 4-slot ring fetched 3 MFMAs ahead;
+    // sched_barrier fences keep that order.
+    using SC = TileSched<2 * NKS, 4 * NDB>;
+    constexpr int NSTEP = SC::total;
     constexpr int RING = 4, AHEAD = RING - 1;     // operand slots, MFMAs fetched ahead
-    constexpr int PH = D / 8;                      // MFMAs per phase (2 NKS = 4 NDB)
-    constexpr int NSTEP = 8 * PH, EPS = 16 / PH;  // softmax elements per MFMA
     constexpr int NI = DmaOffsets<D, NT>::NI;
     constexpr int DSTEP = NSTEP / (2 * 2 * NI);   // the 2 NI copies span the first half
     auto fetch = [&](auto kc) -> bf16x8 {
-      constexpr int k = decltype(kc)::value, ph = k / PH, st = k % PH, c4 = dkdv_chunk(ph);
-      if constexpr (dkdv_is_b(ph)) {
+      constexpr int k = decltype(kc)::value, ph = SC::phase_of(k), st = k - SC::start(ph), c4 = SC::chunk(ph);
+      if constexpr (SC::is_b(ph)) {
         constexpr int sb = st >> 1;  // sub-step sb / NDB, head-dim block sb % NDB
         return rd_tr<D>((st & 1) ? Qc : Gc, lo, c4, sb / NDB, sb % NDB);
       } else {
@@ -295,29 +286,31 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     };
     f32x16 sacc[2], gacc[2];  // S and G_P (later P and G_S) of the two chunks in flight
     bf16x8 pk[2][2], sk[2][2];  // packed bf16 P and G_S operands [chunk parity][sub-step]
-    f32x4 l4[4], d4[4];
+    f32x4 l4[4], d4[4];         // LSE (log2 units) and D of the chunk in softmax
     bf16x8 ring[RING];
     static_for<0, AHEAD>([&](auto kc) { ring[decltype(kc)::value] = fetch(kc); });
     static_for<0, NSTEP>([&](auto kc) {
-      constexpr int k = decltype(kc)::value, ph = k / PH, st = k % PH, c4 = dkdv_chunk(ph);
-      constexpr int cs = dkdv_soft(ph);
+      constexpr int k = decltype(kc)::value, ph = SC::phase_of(k), st = k - SC::start(ph), c4 = SC::chunk(ph);
       if constexpr (k + AHEAD < NSTEP)
         ring[(k + AHEAD) % RING] = fetch(std::integral_constant<int, k + AHEAD>{});
       if constexpr (k % DSTEP == 0 && k / DSTEP < 2 * NI) stage_qg_part<D, NT, k / DSTEP>(Qn, Gn, nsrc, dmo, wave);
-      if constexpr (st == 0 && !dkdv_is_b(ph)) {
+      if constexpr (st == 0 && !SC::is_b(ph)) {
         sacc[c4 & 1] = f32x16{};
         gacc[c4 & 1] = f32x16{};
       }
-      if constexpr (st == 0 && cs >= 0) {
+      static_for<0, 4>([&](auto cc) {
+        constexpr int cs = decltype(cc)::value;
+        if constexpr (SC::soft_begin(cs) == k) {
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const int qr = cs * 32 + 8 * j4 + 4 * h32;
-          l4[j4] = *reinterpret_cast<const f32x4*>(Lc + qr);
-          d4[j4] = *reinterpret_cast<const f32x4*>(Dc + qr);
+          for (int j4 = 0; j4 < 4; ++j4) {
+            const int qr = cs * 32 + 8 * j4 + 4 * h32;
+            l4[j4] = *reinterpret_cast<const f32x4*>(Lc + qr);
+            d4[j4] = *reinterpret_cast<const f32x4*>(Dc + qr);
+          }
         }
-      }
+      });
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (dkdv_is_b(ph)) {
+      if constexpr (SC::is_b(ph)) {
         constexpr int sb = st >> 1, s2 = sb / NDB, db = sb % NDB;
         if constexpr (st & 1) dk[db] = mfma32(sk[c4 & 1][s2], ring[k % RING], dk[db]);
         else dv[db] = mfma32(pk[c4 & 1][s2], ring[k % RING], dv[db]);
@@ -325,25 +318,27 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         if constexpr (st & 1) gacc[c4 & 1] = mfma32(ring[k % RING], vf[st >> 1], gacc[c4 & 1]);
         else sacc[c4 & 1] = mfma32(ring[k % RING], kf[st >> 1], sacc[c4 & 1]);
       }
-      if constexpr (cs >= 0) {
+      static_for<0, 4>([&](auto cc) {
+        constexpr int cs = decltype(cc)::value;
         f32x16& sv = sacc[cs & 1];
         f32x16& gv = gacc[cs & 1];
-#pragma unroll
-        for (int e = 0; e < EPS; ++e) {
+        static_for<0, 16>([&](auto ec) {
           // register r holds query q0 + 32cs + 4*h32 + 8(r/4) + r%4
-          const int r = st * EPS + e, j4 = r >> 2, t = r & 3;
-          float pv = fast_exp2(fmaf(sv[r], c, -l4[j4][t] * LOG2E));
-          if constexpr (CAUSAL) pv = (8 * j4 + t >= lim0 - cs * 32) ? pv : 0.f;
-          sv[r] = pv;
-          gv[r] = pv * (gv[r] - d4[j4][t]);
-        }
-        if constexpr (st == PH - 1) {
+          constexpr int r = decltype(ec)::value, j4 = r >> 2, t = r & 3;
+          if constexpr (SC::elem_step(cs, r) == k) {
+            float pv = fast_exp2(fmaf(sv[r], c, -l4[j4][t]));
+            if constexpr (CAUSAL) pv = (8 * j4 + t >= lim0 - cs * 32) ? pv : 0.f;
+            sv[r] = pv;
+            gv[r] = pv * (gv[r] - d4[j4][t]);
+          }
+        });
+        if constexpr (SC::soft_end(cs) - 1 == k) {
           pk[cs & 1][0] = pack8(sv, 0);
           pk[cs & 1][1] = pack8(sv, 1);
           sk[cs & 1][0] = pack8(gv, 0);
           sk[cs & 1][1] = pack8(gv, 1);
         }
-      }
+      });
       __builtin_amdgcn_sched_barrier(0);
     });
     it_cur = it_nxt;
@@ -425,9 +420,9 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       const uint16_t* olo, const uint16_t* dout, const float* lse, const int32_t* qcnt,
                       const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
                       int H, int Hk, int d, float scale, int causal, uint16_t* dq, uint16_t* dk,
-                      uint16_t* dv, float* dbuf, float* kbar, hipStream_t st) {
-  BwdArgs a{q,  k,  v,    o,    olo, dout, lse, qcnt, qidx, kcnt, kidx, dq,
-            dk, dv, dbuf, kbar, B,   n,    H,   Hk,   (n + TILE - 1) / TILE, scale, scale * LOG2E};
+                      uint16_t* dv, float* dbuf, float* lse2, float* kbar, hipStream_t st) {
+  BwdArgs a{q,    k,    v, o, olo, dout, lse, qcnt, qidx, kcnt, kidx, dq, dk, dv, dbuf,
+            lse2, kbar, B, n, H,   Hk,   (n + TILE - 1) / TILE, scale, scale * LOG2E};
   if (d == 64) return causal ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
   return causal ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
 }

@@ -21,10 +21,42 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* dbuf;  // D, [B, H, n]
+  float* lse2;  // row LSE in log2 units (LSE * log2 e), [B, H, n]
   float* kbar;  // per key tile mean of K over its valid keys, [B, Hk, T, d]
   int B, n, H, Hk, T;
   float scale;
   float scale_log2;
+};
+
+// Issue order of the MFMAs of one tile in the backward passes: 8 phases,
+// A0 A1 B0 A2 B1 A3 B2 B3.  A(c) (LA MFMAs) forms the scores and G_P of 32-row
+// chunk c, B(c) (LB MFMAs) accumulates gradients from that chunk's P / G_S.
+// The softmax of chunk c runs between the end of A(c) and the start of B(c),
+// its 16 register elements spread evenly over the MFMAs issued there (A1 for
+// chunk 0, B0 A2 for chunk 1, B1 A3 for chunk 2, B2 for chunk 3).
+template <int LA, int LB>
+struct TileSched {
+  static constexpr bool is_b(int ph) { return (0xD4 >> ph) & 1; }
+  static constexpr int chunk(int ph) {
+    return ph == 0 ? 0 : ph == 1 ? 1 : ph == 2 ? 0 : ph == 3 ? 2 : ph == 4 ? 1 : ph == 5 ? 3 : ph == 6 ? 2 : 3;
+  }
+  static constexpr int len(int ph) { return is_b(ph) ? LB : LA; }
+  static constexpr int start(int ph) {
+    int s = 0;
+    for (int i = 0; i < ph; ++i) s += len(i);
+    return s;
+  }
+  static constexpr int total = 4 * (LA + LB);
+  static constexpr int phase_of(int k) {
+    int ph = 0;
+    while (ph < 7 && start(ph + 1) <= k) ++ph;
+    return ph;
+  }
+  static constexpr int a_phase(int c) { return c == 0 ? 0 : c == 1 ? 1 : c == 2 ? 3 : 5; }
+  static constexpr int b_phase(int c) { return c == 0 ? 2 : c == 1 ? 4 : c == 2 ? 6 : 7; }
+  static constexpr int soft_begin(int c) { return start(a_phase(c)) + LA; }
+  static constexpr int soft_end(int c) { return start(b_phase(c)); }
+  static constexpr int elem_step(int c, int e) { return soft_begin(c) + e * (soft_end(c) - soft_begin(c)) / 16; }
 };
 
 }  // namespace backlite

@@ -46,36 +46,6 @@ __device__ __forceinline__ void stage_kbar(float* Bd, const KvSrc& s, int wave, 
     if (wave == 0) load_lds4<true>(s.m, nullptr, lds_ptr(Bd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
 }
 
-// Issue order of one key tile: 8 phases, A0 A1 B0 A2 B1 A3 B2 B3, where A(c)
-// (LA MFMAs) forms S^T and G_P^T of 32-key chunk c and B(c) (LB MFMAs)
-// accumulates G_Q^T from that chunk's G_S.  The softmax of chunk c runs
-// between the end of A(c) and the start of B(c), its 16 elements spread evenly
-// over the MFMAs issued there.
-template <int LA, int LB>
-struct DqSched {
-  static constexpr bool is_b(int ph) { return (0xD4 >> ph) & 1; }
-  static constexpr int chunk(int ph) {
-    return ph == 0 ? 0 : ph == 1 ? 1 : ph == 2 ? 0 : ph == 3 ? 2 : ph == 4 ? 1 : ph == 5 ? 3 : ph == 6 ? 2 : 3;
-  }
-  static constexpr int len(int ph) { return is_b(ph) ? LB : LA; }
-  static constexpr int start(int ph) {
-    int s = 0;
-    for (int i = 0; i < ph; ++i) s += len(i);
-    return s;
-  }
-  static constexpr int total = 4 * (LA + LB);
-  static constexpr int phase_of(int k) {
-    int ph = 0;
-    while (ph < 7 && start(ph + 1) <= k) ++ph;
-    return ph;
-  }
-  static constexpr int a_phase(int c) { return c == 0 ? 0 : c == 1 ? 1 : c == 2 ? 3 : 5; }
-  static constexpr int b_phase(int c) { return c == 0 ? 2 : c == 1 ? 4 : c == 2 ? 6 : 7; }
-  static constexpr int soft_begin(int c) { return start(a_phase(c)) + LA; }
-  static constexpr int soft_end(int c) { return start(b_phase(c)); }
-  static constexpr int elem_step(int c, int e) { return soft_begin(c) + e * (soft_end(c) - soft_begin(c)) / 16; }
-};
-
 // One workgroup of 4 waves (one per SIMD) per (b, h, query tile qt).  Wave w
 // owns query rows 32w .. +31: their Q, G_O fragments and the G_Q^T accumulator
 // stay in registers.  The next listed key tile is copied into the other LDS
@@ -121,7 +91,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
       gf[ks] = __builtin_bit_cast(bf16x8, gv);
     }
   }
-  const float lse2 = (qrow < n) ? a.lse[(long)bh * n + qrow] * LOG2E : INFINITY;
+  const float lse2 = (qrow < n) ? a.lse2[(long)bh * n + qrow] : INFINITY;
   const float dl = (qrow < n) ? a.dbuf[(long)bh * n + qrow] : 0.f;
   f32x16 dq[NDB];
 #pragma unroll
@@ -145,7 +115,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   __syncthreads();
   int kt_cur = (cnt > 0) ? (int)__builtin_amdgcn_readfirstlane(itab[0]) : 0;
 
-  using SC = DqSched<2 * NKS, 2 * NDB>;
+  using SC = TileSched<2 * NKS, 2 * NDB>;  // A: S^T, G_P^T of 32 keys; B: G_Q^T
   constexpr int NSTEP = SC::total;
   constexpr int NI = DmaOffsets<D, NT>::NI;
   constexpr int DSTEP = NSTEP / (2 * 2 * NI);  // the 2 NI copies span the first half

@@ -64,8 +64,9 @@ size_t backlite_mask_elems(int B, int H, int n);
 size_t backlite_count_elems(int B, int H, int n);
 
 /* Bytes of device workspace backlite_bwd needs: the per-row D = rowsum(G_O*O)
- * values in fp32 [B, H, n], then the per-key-tile mean of K in fp32
- * [B, H_k, T, d], each part rounded up to 256 bytes.  0 for invalid sizes. */
+ * values in fp32 [B, H, n], the row LSE times log2(e) in fp32 [B, H, n], then
+ * the per-key-tile mean of K in fp32 [B, H_k, T, d], each part rounded up to
+ * 256 bytes.  0 for invalid sizes. */
 size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d);
 
 /* Forward: exact attention plus per-(row, key tile) statistics.

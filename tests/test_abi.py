@@ -38,8 +38,8 @@ def test_sizes(L):
     assert L.backlite_tile_lse_elems(1, 40, 75600, 0) == 40 * 591 * 591 * 128
     assert L.backlite_mask_elems(2, 3, 129) == 2 * 3 * 4
     assert L.backlite_count_elems(2, 3, 129) == 2 * 3 * 2
-    # D: 1*2*100 floats = 800 B -> 1024; kbar: 1*2*1*64 floats = 512 B
-    assert L.backlite_bwd_workspace_bytes(1, 2, 2, 100, 64) == 1024 + 512
+    # D and LSE*log2(e): 1*2*100 floats = 800 B -> 1024 each; kbar: 1*2*1*64 floats = 512 B
+    assert L.backlite_bwd_workspace_bytes(1, 2, 2, 100, 64) == 2 * 1024 + 512
     assert L.backlite_tile_lse_elems(0, 1, 1, 0) == 0
 
 
