@@ -262,8 +262,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     const QgSrc nsrc = qg_src<D>(a, bh0 + it_nxt.hh, b, (int)(g * G + it_nxt.hh), it_nxt.qt, j + 1 < nitems);
     stage_ld(Ln, Dn, nsrc, wave, lane);
     const int q0 = qt * TILE;
-    // on the diagonal tile a query row drops keys after it; elsewhere nothing
-    const int lim0 = (CAUSAL && qt == kt) ? key - (q0 + 4 * h32) : -(1 << 20);
+    // on the diagonal tile a query row drops keys after it
+    const bool diag = CAUSAL && qt == kt;
+    const int lim0 = key - (q0 + 4 * h32);
     // One tile: A(c) forms S and G_P of query chunk c (32 rows), B(c)
     // accumulates G_V and G_K from chunk c's P and G_S, in the order of
     // TileSched; chunk c's softmax (exp, mask, G_S) is spread over the MFMAs
@@ -322,12 +323,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         constexpr int cs = decltype(cc)::value;
         f32x16& sv = sacc[cs & 1];
         f32x16& gv = gacc[cs & 1];
+        if constexpr (CAUSAL && SC::soft_begin(cs) == k) {
+          // on the diagonal tile a query drops the keys after it: score -inf,
+          // so P = 0 there; only that tile takes this branch
+          if (diag) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[r] = (8 * (r >> 2) + (r & 3) >= lim0 - cs * 32) ? sv[r] : -INFINITY;
+          }
+        }
         static_for<0, 16>([&](auto ec) {
           // register r holds query q0 + 32cs + 4*h32 + 8(r/4) + r%4
           constexpr int r = decltype(ec)::value, j4 = r >> 2, t = r & 3;
           if constexpr (SC::elem_step(cs, r) == k) {
-            float pv = fast_exp2(fmaf(sv[r], c, -l4[j4][t]));
-            if constexpr (CAUSAL) pv = (8 * j4 + t >= lim0 - cs * 32) ? pv : 0.f;
+            const float pv = fast_exp2(fmaf(sv[r], c, -l4[j4][t]));
             sv[r] = pv;
             gv[r] = pv * (gv[r] - d4[j4][t]);
           }

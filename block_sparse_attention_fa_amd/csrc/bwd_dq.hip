@@ -177,11 +177,19 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
       // softmax elements whose turn is this MFMA
       static_for<0, 4>([&](auto cc) {
         constexpr int c4 = decltype(cc)::value;
+        if constexpr (SC::soft_begin(c4) == k) {
+          // masked keys (padding, or after the row on the diagonal) get score
+          // -inf, so P = 0 there; only diagonal and ragged tiles take this branch
+          if (diag || edge) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              sacc[c4 & 1][r] = (8 * (r >> 2) + (r & 3) <= lim0 - 32 * c4) ? sacc[c4 & 1][r] : -INFINITY;
+          }
+        }
         static_for<0, 16>([&](auto ec) {
           constexpr int r = decltype(ec)::value;
           if constexpr (SC::elem_step(c4, r) == k) {
-            float pv = fast_exp2(fmaf(sacc[c4 & 1][r], c, -lse2));
-            if (diag || edge) pv = (8 * (r >> 2) + (r & 3) <= lim0 - 32 * c4) ? pv : 0.f;
+            const float pv = fast_exp2(fmaf(sacc[c4 & 1][r], c, -lse2));
             const float gs = pv * (gacc[c4 & 1][r] - dl);
             gacc[c4 & 1][r] = gs;
             csum += gs;
