@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=12288,
                     help="query rows of head 0 in the oracle's timed sample")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-backward comparison")
+    ap.add_argument("--gq-path", choices=["stored", "recompute"], default="stored",
+                    help="G_Q from stored bf16 G_S tiles (workspace slots for every kept tile) or by recomputation")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for memory counters)")
     return ap.parse_args()
@@ -55,7 +57,7 @@ def parse():
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("bwd.hip", "bwd_common.h", "bl_device.h"):
+    for f in ("bwd.hip", "bwd_dkdv.h", "bwd_dkdv_d128_gs.hip", "bwd_gs.hip", "bwd_common.h", "bl_device.h"):
         with open(os.path.join(ROOT, "block_sparse_attention_fa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -160,8 +162,17 @@ def main():
     # every buffer allocated once, outside the timed region
     tl = torch.empty(_lib.tile_lse_elems(B, H, n, causal), dtype=torch.float32, device=dev)
     stats = torch.zeros(2, dtype=torch.int64, device=dev)
-    ws = torch.empty(_lib.bwd_workspace_bytes(B, H, Hk, n, d), dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stored = args.gq_path == "stored"
+
+    def workspace(lists):
+        # slots for every kept tile when they fit in device memory (sized once,
+        # outside the timed region: the kept count is read back here)
+        return _lib.bwd_workspace(q, k, lists, stored_tiles="auto" if stored else 0)
+
+    o0, lse0, _, _ = bl.fwd(q, k, v, causal=causal, tile_lse=tl, with_residual=True)
+    ws = workspace(bl.mask(tl, lse0, n, causal, negl))
+    del o0, lse0
 
     def step(rec=None):
         o, lse, _, olo = bl.fwd(q, k, v, causal=causal, tile_lse=tl, with_residual=True)
@@ -202,12 +213,18 @@ def main():
     st = stats.cpu().tolist()
     cand, kept = st[0] / args.steps, st[1] / args.steps
     sparsity = 1.0 - kept / cand if cand else 0.0
+    gq_stored = _lib.bwd_stored_taken(ws, B, H, Hk, n, d)[0] if ws.numel() > _lib.bwd_workspace_bytes(
+        B, H, Hk, n, d) else False
+    ws_bytes = ws.numel()
 
     # the same library's dense backward (negl_prob = 0: every candidate tile)
     dense_ms = None
+    dense_stored = None
     if not args.no_dense:
         o, lse, olo = step()
         md = bl.mask(None, lse, n, causal, 0.0)
+        del ws
+        ws = workspace(md)
         for _ in range(max(1, args.warmup)):
             bl.bwd(q, k, v, o, do, lse, md, causal=causal, workspace=ws, out=(dq, dk, dv), o_lo=olo)
         torch.cuda.synchronize()
@@ -218,6 +235,8 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / args.steps
+        dense_stored = _lib.bwd_stored_taken(ws, B, H, Hk, n, d)[0] if ws.numel() > _lib.bwd_workspace_bytes(
+            B, H, Hk, n, d) else False
 
     pairs_dense = (n * (n + 1) / 2) if causal else float(n) * n
     f_dense_bwd = 10.0 * d * B * H * pairs_dense
@@ -226,7 +245,10 @@ def main():
     dense_equiv_tflops = f_dense_bwd / (bwd_ms * 1e-3) / 1e12
     mfma_frac = kept * tile_bwd_flop / (bwd_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
 
-    kms = {k_: (v_[0] / v_[1] if v_[1] else None) for k_, v_ in prof.items()}
+    # per-step kernel time: with the stored-G_S path each backward pass launches
+    # two variants of the G_K/G_V and G_Q kernels, one of which returns at once,
+    # so the library's per-name totals are divided by the step count
+    kms = {k_: (v_[0] / args.steps if v_[1] else None) for k_, v_ in prof.items()}
     # dominant kernel: dK/dV pass; algorithmic work = 4 of the 5 backward GEMMs
     # (S, G_P, G_V, G_K) per executed tile = 8*128*128*d FLOP
     dkdv_ms = kms.get("dkdv")
@@ -235,6 +257,15 @@ def main():
     roofline = {"kernel": "dkdv", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS if achieved else None,
                 "traffic": measured_traffic(w.name)}
+
+    # the stored-G_S G_Q pass streams each kept tile's bf16 G_S (32 KB) and its
+    # row sums (2 KB) from HBM and writes G_Q once: an HBM-bound pass
+    roofline_gq = None
+    if gq_stored and kms.get("dq"):
+        gq_bytes = kept * (TILE * TILE * 2 + 4 * TILE * 4) + B * n * H * d * 2
+        gbs = gq_bytes / (kms["dq"] * 1e-3) / 1e9
+        roofline_gq = {"kernel": "dqs", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": gbs / PEAK_HBM_GBS}
 
     # mask algorithmic bytes: tile-LSE of every candidate pair (512 B), the row LSE
     # and D-like row data of each query tile, bitmap + list entries written
@@ -261,18 +292,22 @@ def main():
         "mask_ms": mask_ms,
         "dense_bwd_ms": dense_ms,
         "bwd_speedup_vs_dense": (dense_ms / bwd_ms) if dense_ms else None,
+        "gq_path": "stored" if gq_stored else "recompute",
+        "dense_gq_path": None if dense_stored is None else ("stored" if dense_stored else "recompute"),
+        "bwd_workspace_gb": ws_bytes / 1e9,
         "sparsity": sparsity,
         "executed_tiles_per_step": kept,
         "candidate_tiles_per_step": cand,
         "executed_tile_mfma_frac": mfma_frac,
         "fwd_tflops": f_fwd / (fwd_ms * 1e-3) / 1e12,
         "fwd_mfma_frac": f_fwd / (fwd_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-        "kernel_avg_ms": kms,
+        "kernel_ms_per_step": kms,
         "mask_gbs": (mask_bytes / ((kms["mask_select"] + kms["mask_transpose"]) * 1e-3) / 1e9)
         if kms.get("mask_select") and kms.get("mask_transpose") else None,
         "delta_gbs": delta_bytes / (kms["delta"] * 1e-3) / 1e9 if kms.get("delta") else None,
         "wall_s_timed": wall,
         "roofline": roofline,
+        "roofline_gq": roofline_gq,
         "cpu_baseline": None,
     }
     log(f"[bench] fwd {fwd_ms:.3f} ms  mask {mask_ms:.3f} ms  bwd {bwd_ms:.3f} ms  dense bwd "

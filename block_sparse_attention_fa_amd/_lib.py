@@ -42,6 +42,10 @@ def _load():
     lib.backlite_count_elems.restype = Z
     lib.backlite_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.backlite_bwd_workspace_bytes.restype = Z
+    lib.backlite_bwd_workspace_bytes_stored.argtypes = [I, I, I, I, I, ctypes.c_int64]
+    lib.backlite_bwd_workspace_bytes_stored.restype = Z
+    lib.backlite_bwd_state_offset.argtypes = [I, I, I, I, I]
+    lib.backlite_bwd_state_offset.restype = Z
     lib.backlite_fwd.argtypes = [P, P, P, I, I, I, I, I, F, I, P, P, P, P, P]
     lib.backlite_fwd.restype = I
     lib.backlite_mask.argtypes = [P, P, I, I, I, I, F, P, P, P, P, P, P, P]
@@ -154,9 +158,53 @@ def bwd_workspace_bytes(B, H, Hk, n, d) -> int:
     return int(_load().backlite_bwd_workspace_bytes(B, H, Hk, n, d))
 
 
-def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, out=None, o_lo=None):
+def bwd_workspace_bytes_stored(B, H, Hk, n, d, max_tiles) -> int:
+    return int(_load().backlite_bwd_workspace_bytes_stored(B, H, Hk, n, d, int(max_tiles)))
+
+
+def bwd_state_offset(B, H, Hk, n, d) -> int:
+    return int(_load().backlite_bwd_state_offset(B, H, Hk, n, d))
+
+
+def bwd_stored_taken(workspace, B, H, Hk, n, d) -> tuple:
+    """(stored path taken, kept tile pairs) from the state words of a workspace
+    the last backward used (synchronises with the device)."""
+    off = bwd_state_offset(B, H, Hk, n, d)
+    w = workspace[off:off + 8].view(torch.int32).tolist()
+    return bool(w[0]), int(w[1])
+
+
+# Device memory left free when sizing a stored-G_S workspace automatically.
+STORED_MARGIN_BYTES = 4 << 30
+
+
+def bwd_workspace(q, k, lists, stored_tiles="auto") -> torch.Tensor:
+    """A backward workspace.  stored_tiles: "auto" sizes the stored-G_S slots
+    for the tiles the lists keep (their count is read back from the device)
+    when that fits in free device memory, else no slots; an int gives that many
+    slots; 0 gives the base workspace (G_Q recomputes P and G_S)."""
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    base = bwd_workspace_bytes(B, H, Hk, n, d)
+    tiles = 0
+    if stored_tiles == "auto":
+        tiles = int(lists["qcnt"].sum().item())
+        need = bwd_workspace_bytes_stored(B, H, Hk, n, d, tiles)
+        free, _ = torch.cuda.mem_get_info(q.device)
+        if need - base > free - STORED_MARGIN_BYTES:
+            tiles = 0
+    elif stored_tiles:
+        tiles = int(stored_tiles)
+    size = bwd_workspace_bytes_stored(B, H, Hk, n, d, tiles) if tiles > 0 else base
+    return torch.empty(size, dtype=torch.uint8, device=q.device)
+
+
+def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, out=None, o_lo=None,
+        stored_tiles="auto"):
     """G_Q, G_K, G_V (bf16) for the tile set in `lists` (qcnt/qidx/kcnt/kidx).
-    o_lo: the forward's residual output (recommended; D then uses O + O_lo)."""
+    o_lo: the forward's residual output (recommended; D then uses O + O_lo).
+    workspace: reused if given (a larger one enables the stored-G_S path);
+    otherwise one is allocated by bwd_workspace(stored_tiles=...)."""
     B, n, H, d = q.shape
     Hk = k.shape[2]
     for name, t, shp in (("q", q, (B, n, H, d)), ("k", k, (B, n, Hk, d)), ("v", v, (B, n, Hk, d)),
@@ -175,9 +223,8 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
-    need = bwd_workspace_bytes(B, H, Hk, n, d)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = bwd_workspace(q, k, lists, stored_tiles)
     rc = _load().backlite_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
                               _ptr(lists["qcnt"]), _ptr(lists["qidx"]), _ptr(lists["kcnt"]),
                               _ptr(lists["kidx"]), B, n, H, Hk, d, scale, int(causal),
@@ -187,7 +234,7 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
     return dq, dk, dv
 
 
-PROFILE_KERNELS = ("fwd", "mask_select", "mask_transpose", "delta", "kmean", "dkdv", "dq")
+PROFILE_KERNELS = ("fwd", "mask_select", "mask_transpose", "delta", "kmean", "dkdv", "dq", "gs_slots")
 
 
 def profile_enable(on: bool = True):

@@ -22,7 +22,8 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       const uint16_t* olo, const uint16_t* dout, const float* lse, const int32_t* qcnt,
                       const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
                       int H, int Hk, int d, float scale, int causal, uint16_t* dq, uint16_t* dk,
-                      uint16_t* dv, float* dbuf, float* lse2, float* kbar, hipStream_t st);
+                      uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
+                      uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, hipStream_t st);
 }  // namespace backlite
 
 namespace {
@@ -121,6 +122,26 @@ size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d) {
   return 2 * delta_bytes(B, H, n) + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
 }
 
+namespace {
+constexpr size_t kSlotBytes = 128 * 128 * 2 + 4 * 128 * 4;  // bf16 G_S tile + residual sums
+constexpr size_t kStateBytes = 256;                          // gsinfo words
+// stored-path index arrays after the base workspace: state, qbase, kslot
+size_t gs_index_bytes(int B, int H, int n) {
+  const size_t T = (size_t)ntiles(n);
+  return kStateBytes + round256((size_t)B * H * T * 4) + round256((size_t)B * H * T * T * 4);
+}
+}  // namespace
+
+size_t backlite_bwd_workspace_bytes_stored(int B, int H, int H_k, int n, int d, int64_t max_tiles) {
+  const size_t base = backlite_bwd_workspace_bytes(B, H, H_k, n, d);
+  if (base == 0 || max_tiles < 1) return base;
+  return base + gs_index_bytes(B, H, n) + (size_t)max_tiles * kSlotBytes;
+}
+
+size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d) {
+  return backlite_bwd_workspace_bytes(B, H, H_k, n, d);
+}
+
 int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int n, int H,
                  int H_k, int d, float scale, int causal, uint16_t* O, uint16_t* O_lo,
                  float* lse_row, float* tile_lse, void* stream) {
@@ -205,11 +226,29 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
     return fail(BACKLITE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, workspace_bytes,
                 workspace ? "" : ", NULL");
   TRY(check_ptr(workspace, "workspace"));
+  char* ws = (char*)workspace;
+  // stored-G_S slots when the workspace holds the index arrays and at least one slot
+  int32_t* gsinfo = nullptr;
+  uint32_t *qbase = nullptr, *kslot = nullptr;
+  uint16_t* gs = nullptr;
+  float* gsl = nullptr;
+  long long cap = 0;
+  const size_t idx = gs_index_bytes(B, H, n);
+  if (workspace_bytes >= need + idx + kSlotBytes) {
+    const size_t T = (size_t)ntiles(n);
+    cap = (long long)((workspace_bytes - need - idx) / kSlotBytes);
+    if (cap > 0xffffffffLL) cap = 0xffffffffLL;  // slot indices are 32-bit
+    gsinfo = (int32_t*)(ws + need);
+    qbase = (uint32_t*)(ws + need + kStateBytes);
+    kslot = (uint32_t*)(ws + need + kStateBytes + round256((size_t)B * H * T * 4));
+    gs = (uint16_t*)(ws + need + idx);
+    gsl = (float*)(ws + need + idx + (size_t)cap * 128 * 128 * 2);
+  }
   return hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d,
-                                         scale, causal ? 1 : 0, dQ, dK, dV, (float*)workspace,
-                                         (float*)((char*)workspace + delta_bytes(B, H, n)),
-                                         (float*)((char*)workspace + 2 * delta_bytes(B, H, n)),
-                                         (hipStream_t)stream),
+                                         scale, causal ? 1 : 0, dQ, dK, dV, (float*)ws,
+                                         (float*)(ws + delta_bytes(B, H, n)),
+                                         (float*)(ws + 2 * delta_bytes(B, H, n)), gsinfo, qbase, kslot, gs, gsl,
+                                         cap, (hipStream_t)stream),
                     "backlite_bwd launch");
 }
 

@@ -1,0 +1,14 @@
+// Instances of the G_K/G_V pass for head dimension 64, stored-G_S variant (one translation
+// unit per head dimension and variant, so the kernels compile in parallel).
+#include "bwd_dkdv.h"
+
+namespace backlite {
+
+hipError_t launch_dkdv_d64_gs(const BwdArgs& a, bool causal, hipStream_t st) {
+  const dim3 grid(a.B * a.Hk * a.T), block(256);
+  if (causal) hipLaunchKernelGGL((dkdv_kernel<64, true, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((dkdv_kernel<64, false, true>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace backlite

@@ -52,6 +52,7 @@ __device__ __forceinline__ void stage_kbar(float* Bd, const KvSrc& s, int wave, 
 // stage while the current one is consumed.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
+  if (a.gsinfo != nullptr && a.gsinfo[0] != 0) return;  // the stored-G_S pass computes G_Q
   constexpr int NT = 256;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;

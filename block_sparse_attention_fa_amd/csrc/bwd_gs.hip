@@ -1,0 +1,321 @@
+// Stored-G_S backward path: the G_K/G_V pass keeps each kept tile's G_S (bf16)
+// in a workspace slot, and the G_Q pass computes G_Q += scale * G_S K from the
+// stored tiles ("Introducing BackLite", backward equations: G_Q = G_S K / sqrt(d)
+// over the kept tiles) instead of rebuilding S, P, G_P and G_S.  One slot is
+// 32 KB of G_S plus 2 KB of fp32 row sums; at the 32k-token video shape with
+// ~79% of the tiles skipped that is ~19 GB of the GPU's 288 GB, and the G_Q
+// pass becomes a stream over those bytes.
+//
+// Slots: the kept tiles of query tile (b, h, qt), in q-list order, take the
+// slots qbase[b,h,qt] + i, where qbase is the exclusive prefix sum of qcnt
+// over (b, h, qt).  kslot gives the same slot to each k-list entry, which is
+// what the G_K/G_V pass (walking k-lists) needs.
+//
+// Whether the path is taken is decided on the device: the scan compares the
+// number of kept tiles with the slot capacity and writes gsinfo[0]; the
+// kernels of the path not taken return at once.
+#include "bl_device.h"
+#include "bwd_common.h"
+#include "bwd_dkdv.h"  // CPOL_NT
+#include "prof.h"
+
+namespace backlite {
+
+// qbase = exclusive prefix sum of qcnt over the B*H*T query tiles; gsinfo[0] =
+// (kept tiles <= capacity), gsinfo[1] = kept tiles (clamped to int32).  One
+// workgroup: each thread sums a contiguous run, the run totals are scanned in
+// LDS, then each thread writes its run's prefix values.
+__global__ __launch_bounds__(1024) void gs_scan_kernel(BwdArgs a) {
+  __shared__ long long part[1024];
+  const long N = (long)a.B * a.H * a.T;
+  const int tid = threadIdx.x;
+  const long per = (N + 1023) / 1024;
+  const long s0 = min(N, (long)tid * per), s1 = min(N, s0 + per);
+  long long sum = 0;
+  for (long i = s0; i < s1; ++i) sum += max(0, min(a.qcnt[i], a.T));
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const long long v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  long long run = part[tid] - sum;
+  for (long i = s0; i < s1; ++i) {
+    a.qbase[i] = (uint32_t)run;
+    run += max(0, min(a.qcnt[i], a.T));
+  }
+  if (tid == 1023) {
+    const long long total = part[1023];
+    a.gsinfo[1] = (int32_t)min(total, 0x7fffffffLL);
+    a.gsinfo[0] = total <= a.gs_cap ? 1 : 0;
+  }
+}
+
+// kslot[b,h,kt,p] = slot of the tile (qt, kt) listed at position p of key tile
+// kt's k-list.  One workgroup per (b, h, qt): each kept kt of the q-list finds
+// qt in kt's ascending k-list by binary search.
+__global__ __launch_bounds__(256) void gs_slot_kernel(BwdArgs a) {
+  if (a.gsinfo[0] == 0) return;
+  const int T = a.T;
+  const long bq = blockIdx.x;  // (b * H + h) * T + qt
+  const int qt = (int)(bq % T);
+  const long bh = bq / T;
+  const int cnt = max(0, min(a.qcnt[bq], T));
+  const uint32_t base = a.qbase[bq];
+  for (int i = threadIdx.x; i < cnt; i += 256) {
+    const int kt = a.qidx[bq * T + i];
+    if (kt >= T) continue;
+    const long row = bh * T + kt;
+    const int kc = max(0, min(a.kcnt[row], T));
+    const uint16_t* list = a.kidx + row * T;
+    int lo = 0, hi = kc;  // first position whose entry is >= qt
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)list[mid] < qt) lo = mid + 1;
+      else hi = mid;
+    }
+    if (lo < kc && (int)list[lo] == qt) a.kslot[row * T + lo] = base + (uint32_t)i;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// G_Q from stored G_S.  One workgroup of 4 waves per (b, h, query tile qt);
+// wave w owns query rows 32w .. +31 and accumulates G_Q^T (C layout
+// [dim][query]) over the q-list:  G_Q^T += K^T G_S^T, both operands read from
+// LDS with the transpose read.  K rows are shared by the waves (two LDS
+// stages, the next tile's rows copied while the current one is consumed).
+// Each wave's own G_S rows (8 KB per tile, the HBM stream of this pass) are
+// loaded into registers two tiles ahead and written to a private LDS buffer at
+// the start of their tile, so two tiles of G_S are in flight per wave.
+//
+// G_S operand, per 16-key step ks (keys 16ks + 4*h32 + {0..3, 8..11}, the same
+// order as the K operand): the slot's fragment-order block of wave kw =
+// ks / 2, 16-byte position 2*key32 + hq (hq: which 4-row group of the 8 rows
+// the G_K/G_V lane packed), 8-byte half v.  A transpose read by lane i of a
+// 16-lane group supplies the address of key row k0 + i/4, query columns
+// n0 + 4(i%4) .. +3, i.e. position 2*key32 + (i & 1) and half (i >> 1) & 1.
+// Blocks of the second 16-row half (s = 1) are kept with 16-byte positions
+// XOR 8 (a 128-byte shift), so the four groups of one read cover all banks.
+// ---------------------------------------------------------------------------
+template <int D, int NT, int I>
+__device__ __forceinline__ void stage_k_part(bf16* Kd, const __amdgpu_buffer_rsrc_t& rs,
+                                             const DmaOffsets<D, NT>& dmo, int wave) {
+  lds_byte* dst = lds_ptr(Kd + ((I * (NT / 64) + wave) * 64) * 8);
+  load_lds16<true>(rs, nullptr, dst, dmo.off[I]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
+  if (a.gsinfo[0] == 0) return;
+  constexpr int NT = 256;
+  constexpr int NDB = D / 32;
+  constexpr int NKS = TILE / 16;  // 16-key contraction steps per key tile
+  constexpr int GW = 8 * 1024;    // one wave's G_S bytes per tile
+  constexpr int NI = DmaOffsets<D, NT>::NI;
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[TILE * D];
+  __shared__ __attribute__((aligned(16))) char Gw[4 * GW];
+  __shared__ __attribute__((aligned(16))) float Lw0[4 * TILE];  // per wave: [key quarter][32 rows]
+  __shared__ __attribute__((aligned(16))) float Lw1[4 * TILE];
+  __shared__ __attribute__((aligned(16))) float Kb0[D];
+  __shared__ __attribute__((aligned(16))) float Kb1[D];
+  __shared__ uint16_t itab[MAX_TILES];
+
+  const int T = a.T, n = a.n;
+  const int L = work_index(blockIdx.x);
+  const int qt = L % T;
+  const int bh = L / T;
+  const int h = bh % a.H, b = bh / a.H;
+  const int g = h / (a.H / a.Hk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int lrow = wave * 32 + l32;
+  const long qstride = (long)a.H * D;
+  const long kvstride = (long)a.Hk * D;
+  const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
+  const float* kbar = a.kbar + (long)(b * a.Hk + g) * T * D;
+  const long bq = (long)bh * T + qt;
+  const int cnt = max(0, min(a.qcnt[bq], T));
+  const uint32_t sbase = a.qbase[bq];
+  {
+    const uint16_t* list = a.qidx + bq * T;
+    for (int i = tid; i < cnt; i += NT) itab[i] = list[i];
+  }
+  LdsOffsets<D> lo;
+  lo.init(lane);
+  DmaOffsets<D, NT> dmo;
+  dmo.init(kvstride, tid);
+  const int i16 = lane & 15, sh = (lane >> 4) & 1;
+  const uint32_t goff = (uint32_t)(sh * 1024 + 128 * (h32 ^ sh) + 32 * (i16 >> 2) + 16 * (i16 & 1) +
+                                   8 * ((i16 >> 1) & 1));
+  char* gw = Gw + wave * GW;
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
+  __syncthreads();
+
+  auto kt_at = [&](int i) -> int { return i < cnt ? (int)__builtin_amdgcn_readfirstlane(itab[i]) : 0; };
+  // K rows, row sums and key mean of list item i (key tile kt); past the list, zeros
+  struct Src {
+    __amdgpu_buffer_rsrc_t k, ls, kb;
+  };
+  auto src_of = [&](int i) -> Src {
+    const bool valid = i < cnt;
+    const int kt = kt_at(i), key0 = kt * TILE;
+    const uint32_t rows = valid ? (uint32_t)min(TILE, n - key0) : 0u;
+    const size_t slot = (size_t)sbase + (size_t)i;
+    return Src{buffer_rsrc(kbase + (long)key0 * kvstride, rows * (uint32_t)kvstride * 2u),
+               buffer_rsrc(a.gsl + slot * (4 * TILE), valid ? 4u * TILE * 4u : 0u),
+               buffer_rsrc(kbar + (long)kt * D, valid ? (uint32_t)D * 4u : 0u)};
+  };
+  // this wave's row sums (2 words per lane) and, in wave 0, the key mean
+  auto stage_small = [&](const Src& s, float* Ld, float* Bd) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = lane + 64 * it;
+      load_lds4<true>(s.ls, nullptr, lds_ptr(Ld + wave * TILE + 64 * it),
+                      (uint32_t)((e >> 5) * TILE + 32 * wave + (e & 31)) * 4u);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i)
+      if (wave == 0) load_lds4<true>(s.kb, nullptr, lds_ptr(Bd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
+  };
+  // this wave's 8 blocks of item i's G_S into registers: block ib = (kw, s),
+  // lane l takes the 16 bytes at position l ^ 8s
+  u32x4 gr[2][8];
+  auto load_gs = [&](u32x4 (&r)[8], int i) {
+    const size_t slot = (size_t)sbase + (size_t)i;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.gs + slot * (TILE * TILE), i < cnt ? TILE * TILE * 2u : 0u);
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib) {
+      const int kw = ib >> 1, s2 = ib & 1;
+      r[ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, (uint32_t)((lane ^ (8 * s2)) * 16), ((kw * 4 + wave) * 2 + s2) * 1024,
+                                            CPOL_NT));
+    }
+  };
+
+  // prologue: G_S of item 0, K / sums of item 0, then G_S of item 1 (the last
+  // 8 vector-memory operations before the first tile)
+  load_gs(gr[0], 0);
+  {
+    const Src s0 = src_of(0);
+    stage_small(s0, Lw0, Kb0);
+    static_for<0, NI>([&](auto ic) { stage_k_part<D, NT, decltype(ic)::value>(Ks0, s0.k, dmo, wave); });
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_gs(gr[1], 1);
+
+  const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
+  // item j in K stage S and G_S register set S (j % 2 == S)
+  auto visit = [&](int j, auto stage) {
+    constexpr int S = decltype(stage)::value;
+    const bf16* Kc = S ? Ks1 : Ks0;
+    const float* Lc = S ? Lw1 : Lw0;
+    const float* Bc = S ? Kb1 : Kb0;
+    bf16* Kn = S ? Ks0 : Ks1;
+    float* Ln = S ? Lw0 : Lw1;
+    float* Bn = S ? Kb0 : Kb1;
+    // everything of item j has landed; item j + 1's G_S (the last 8 loads) may not have
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib) *reinterpret_cast<u32x4*>(gw + ib * 1024 + lane * 16) = gr[S][ib];
+    __syncthreads();  // K of item j visible; the other K stage is free
+    {
+      const Src ns = src_of(j + 1);
+      stage_small(ns, Ln, Bn);
+      static_for<0, NI>([&](auto ic) { stage_k_part<D, NT, decltype(ic)::value>(Kn, ns.k, dmo, wave); });
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_gs(gr[S], j + 2);  // the register set just written to LDS takes item j + 2
+    float hsum = 0.f;  // this row's sum of the bf16 G_S operands over the lane's 64 keys
+    static_for<0, NKS>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      const char* gb = gw + (ks >> 1) * 2048 + (ks & 1) * 512 + goff;
+      const bf16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(gb));
+      const bf16x4 g1 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(gb + 256));
+      const bf16x8 bop = cat8(g0, g1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(rd_tr<D>(Kc, lo, ks >> 1, ks & 1, db), bop, dq[db]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x2 pr = {bop[2 * u], bop[2 * u + 1]};
+        hsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, hsum, false);
+      }
+    });
+    // Rounding compensation: the stored G_S is bf16.  Its rounding residual lo
+    // contributes sum_j lo_ij K_j, whose dominant part when the tile's keys
+    // share a large common vector is (sum_j lo_ij) * kbar (rows of G_S nearly
+    // sum to zero, so that vector would otherwise multiply the rounding
+    // error).  sum_j lo_ij = (fp32 row sum of G_S, from the G_K/G_V pass) -
+    // (sum of the bf16 operands).  A rank-1 MFMA per 32-dim block, operands
+    // nonzero only in contraction slot 0.
+    {
+      hsum += __shfl_xor(hsum, 32);
+      const float* lw = Lc + wave * TILE + l32;
+      const float ls = ((lw[0] + lw[32]) + (lw[64] + lw[96])) - hsum;
+      bf16x8 bl = {};
+      if (h32 == 0) bl[0] = (bf16)ls;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        bf16x8 al = {};
+        if (h32 == 0) al[0] = (bf16)Bc[db * 32 + l32];
+        dq[db] = mfma32(al, bl, dq[db]);
+      }
+    }
+  };
+  int j = 0;
+  for (; j + 1 < cnt; j += 2) {
+    visit(j, std::integral_constant<int, 0>{});
+    visit(j + 1, std::integral_constant<int, 1>{});
+  }
+  if (j < cnt) visit(j, std::integral_constant<int, 0>{});
+
+  // epilogue: dq C layout is [dim = 32db + 8(r/4) + 4*h32 + r%4][query l32]
+  wait_vmem();
+  __syncthreads();
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int dim = db * 32 + 8 * jj + 4 * h32;
+      bf16x4 w4 = {(bf16)(dq[db][4 * jj] * a.scale), (bf16)(dq[db][4 * jj + 1] * a.scale),
+                   (bf16)(dq[db][4 * jj + 2] * a.scale), (bf16)(dq[db][4 * jj + 3] * a.scale)};
+      *reinterpret_cast<bf16x4*>(Ks0 + tile_off<D>(lrow, dim >> 3) + (dim & 7)) = w4;
+    }
+  __syncthreads();
+  {
+    constexpr int CH = D / 8;
+    uint16_t* op = a.dq + ((long)b * n + (long)qt * TILE) * qstride + (long)h * D;
+#pragma unroll
+    for (int it = 0; it < TILE * CH / NT; ++it) {
+      const int cc = tid + it * NT;
+      const int row = cc / CH, ch = cc % CH;
+      if (qt * TILE + row < n)
+        *reinterpret_cast<u32x4*>(op + (long)row * qstride + ch * 8) =
+            *reinterpret_cast<const u32x4*>(Ks0 + tile_off<D>(row, ch));
+    }
+  }
+}
+
+hipError_t launch_gs_slots(const BwdArgs& a, hipStream_t st) {
+  ProfScope ps(PK_GS_SLOTS, st);
+  hipLaunchKernelGGL(gs_scan_kernel, dim3(1), dim3(1024), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gs_slot_kernel, dim3(a.B * a.H * a.T), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_gs(const BwdArgs& a, int d, hipStream_t st) {
+  ProfScope ps(PK_DQ, st);
+  const dim3 grid(a.B * a.H * a.T), block(256);
+  if (d == 64) hipLaunchKernelGGL((dqs_kernel<64>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((dqs_kernel<128>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace backlite

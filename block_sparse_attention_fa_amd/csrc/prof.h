@@ -6,7 +6,17 @@
 
 namespace backlite {
 
-enum ProfKernel { PK_FWD = 0, PK_MASK_SELECT, PK_MASK_TRANSPOSE, PK_DELTA, PK_KMEAN, PK_DKDV, PK_DQ, PK_COUNT };
+enum ProfKernel {
+  PK_FWD = 0,
+  PK_MASK_SELECT,
+  PK_MASK_TRANSPOSE,
+  PK_DELTA,
+  PK_KMEAN,
+  PK_DKDV,
+  PK_DQ,
+  PK_GS_SLOTS,
+  PK_COUNT
+};
 
 struct ProfRec {
   int kernel;  // -1: profiling off, nothing recorded

@@ -69,6 +69,26 @@ size_t backlite_count_elems(int B, int H, int n);
  * 256 bytes.  0 for invalid sizes. */
 size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d);
 
+/* Bytes of a backward workspace that also holds slots for up to max_tiles
+ * kept tile pairs, enabling the stored-G_S path of backlite_bwd (the G_K/G_V
+ * pass keeps each kept tile's G_S = P * (G_P - D) in bf16, and G_Q = scale *
+ * G_S K is then formed from the stored tiles instead of a second
+ * recomputation of S, P and G_P; "Introducing BackLite", backward equations).
+ * Layout after the base workspace: 256 bytes of state words, slot starts per
+ * query tile uint32 [B, H, T], slots per k-list entry uint32 [B, H, T, T],
+ * then the slots (each 32 KB of bf16 G_S plus 2 KB of fp32 sums of its
+ * rounding residual).  Any workspace of at least the base size plus the state
+ * and index arrays plus one slot enables the path; the device takes it only
+ * when the mask's kept tile pairs fit the slots, and falls back to the
+ * recomputing G_Q pass otherwise.  max_tiles < 1 returns the base size. */
+size_t backlite_bwd_workspace_bytes_stored(int B, int H, int H_k, int n, int d, int64_t max_tiles);
+
+/* Byte offset, within a workspace enabling the stored path, of its state
+ * words (int32): [0] = 1 if the last backlite_bwd on it took the stored path,
+ * [1] = the kept tile pairs it counted.  Valid once that call has completed
+ * on its stream. */
+size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d);
+
 /* Forward: exact attention plus per-(row, key tile) statistics.
  *
  * ("Introducing BackLite", "Backpropagation for attention": S = scale*Q K^T,
@@ -136,7 +156,10 @@ int backlite_mask(const float* tile_lse, const float* lse_row,
  *   qcnt/qidx drive G_Q (per query tile); kcnt/kidx drive G_K, G_V (per key
  *   tile); both must describe the same tile set (as backlite_mask writes them).
  *   workspace: device buffer of at least backlite_bwd_workspace_bytes(); its
- *   contents on entry are ignored.
+ *   contents on entry are ignored.  A larger one (see
+ *   backlite_bwd_workspace_bytes_stored) enables the stored-G_S path, chosen
+ *   on the device when every kept tile has a slot; both paths compute the
+ *   same gradients (G_S rounded to bf16 for the G_Q product either way).
  * The result is deterministic (no atomics): repeated calls give identical bits. */
 int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
@@ -151,7 +174,9 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
  * backlite_profile_read waits for the outstanding events and returns, for the
  * named kernel, the accumulated elapsed time and the number of launches since
  * the last reset.  Kernel names: "fwd", "mask_select", "mask_transpose",
- * "delta", "kmean", "dkdv", "dq".  Process-wide state, thread-safe; enabling
+ * "delta", "kmean", "dkdv", "dq", "gs_slots" (slot assignment of the stored
+ * path; "dkdv" and "dq" then also count the launch of the pass variant that
+ * returns at once).  Process-wide state, thread-safe; enabling
  * adds two event records per launch.  read returns BACKLITE_ERR_INVALID_ARG
  * for an unknown name or NULL outputs, BACKLITE_ERR_HIP if an event failed. */
 int backlite_profile_enable(int on);

@@ -41,6 +41,16 @@ def test_sizes(L):
     # D and LSE*log2(e): 1*2*100 floats = 800 B -> 1024 each; kbar: 1*2*1*64 floats = 512 B
     assert L.backlite_bwd_workspace_bytes(1, 2, 2, 100, 64) == 2 * 1024 + 512
     assert L.backlite_tile_lse_elems(0, 1, 1, 0) == 0
+    # stored-G_S workspace: base, 256 B of state words, qbase (2 x 1 uint32 -> 256 B),
+    # kslot (2 x 1 x 1 uint32 -> 256 B), then 34816 B (32 KB G_S + 2 KB residual sums) per slot
+    base = 2 * 1024 + 512
+    assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 0) == base
+    assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 3) == base + 3 * 256 + 3 * 34816
+    assert L.backlite_bwd_state_offset(1, 2, 2, 100, 64) == base
+    # the 32k-token video shape: T = 256, 40 heads
+    big = L.backlite_bwd_workspace_bytes(1, 40, 40, 32760, 128)
+    assert L.backlite_bwd_workspace_bytes_stored(1, 40, 40, 32760, 128, 1000) == \
+        big + 256 + 40 * 256 * 4 + 40 * 256 * 256 * 4 + 1000 * 34816
 
 
 FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced

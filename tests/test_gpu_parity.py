@@ -120,40 +120,90 @@ def test_mask_end_to_end(w):
         check_lists(m, keep)
 
 
+PATHS = ("recompute", "stored")
+
+
+def _bwd_path(r, lists, path, o_lo=True):
+    """Backward through the C ABI on the given G_Q path: "recompute" (base
+    workspace) or "stored" (slots for every kept tile; the state words must
+    show the stored path taken)."""
+    bl, xg, w = r["bl"], r["xg"], r["w"]
+    ws = bl._lib.bwd_workspace(xg["q"], xg["k"], lists, stored_tiles=0 if path == "recompute" else "auto")
+    out = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], lists, causal=w.causal,
+                 o_lo=r["olo"] if o_lo else None, workspace=ws)
+    if path == "stored":
+        taken, kept = bl._lib.bwd_stored_taken(ws, w.B, w.H, w.Hk, w.n, w.d)
+        assert taken and kept == int(lists["qcnt"].sum().item())
+    return out
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("w", CASES, ids=IDS)
-def test_backward_on_oracle_mask(w):
+def test_backward_on_oracle_mask(w, path):
     r = _setup(w)
-    bl, dev, x, xg = r["bl"], r["dev"], r["x"], r["xg"]
+    dev, x = r["dev"], r["x"]
     keep = orc.mask_from_stats(r["ref"]["tile_lse"], r["ref"]["lse"], w.n, w.causal, NEGL)
     lists = lists_to_torch(keep, dev)
-    dq, dk, dv = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], lists, causal=w.causal,
-                        o_lo=r["olo"])
+    dq, dk, dv = _bwd_path(r, lists, path)
     g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal)
     for name, got, ref in (("dQ", dq, g["dQ"]), ("dK", dk, g["dK"]), ("dV", dv, g["dV"])):
         rl, cs = assert_close_grad(name, got.cpu(), ref)
-        flush_print(f"  {name}: rel-L2 {rl:.2e} cos {cs:.6f}")
+        flush_print(f"  {path} {name}: rel-L2 {rl:.2e} cos {cs:.6f}")
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("w", CASES, ids=IDS)
-def test_backward_dense(w):
+def test_backward_dense(w, path):
     """negl_prob = 0 without statistics: every candidate tile, dense gradients."""
     r = _setup(w)
-    bl, x, xg = r["bl"], r["x"], r["xg"]
+    bl, x = r["bl"], r["x"]
     m = bl.mask(None, r["lse"], w.n, w.causal, 0.0)
     check_lists(m, np.broadcast_to(orc.candidates(w.n, w.causal), (w.B, w.H) + (m["keep"].shape[-1],) * 2))
-    dq, dk, dv = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=w.causal,
-                        o_lo=r["olo"])
+    dq, dk, dv = _bwd_path(r, m, path)
     g = orc.backward(x["q"], x["k"], x["v"], x["do"], causal=w.causal)
     for name, got, ref in (("dQ", dq, g["dQ"]), ("dK", dk, g["dK"]), ("dV", dv, g["dV"])):
         assert_close_grad(name, got.cpu(), ref)
 
 
-def test_backward_deterministic():
+@pytest.mark.parametrize("w", [CASES[0], CASES[1], CASES[2]], ids=IDS[:3])
+def test_stored_path_matches_recompute(w):
+    """Both G_Q paths: G_K, G_V bit-identical (same pass, with or without the
+    G_S stores); G_Q equal to the recompute path up to fp32 summation order."""
+    r = _setup(w)
+    m = r["bl"].mask(r["tl"], r["lse"], w.n, w.causal, NEGL)
+    a = _bwd_path(r, m, "recompute")
+    b = _bwd_path(r, m, "stored")
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+    assert torch.equal(a[2].view(torch.int16), b[2].view(torch.int16))
+    rl = orc.rel_l2(b[0].cpu(), orc.to_f64(a[0].cpu()))
+    flush_print(f"  dQ stored vs recompute rel-L2 {rl:.2e}")
+    assert rl <= 2e-3
+
+
+def test_stored_path_falls_back_when_slots_run_out():
+    """A workspace with fewer slots than kept tiles: the device takes the
+    recompute path (state word 0) and the result equals the base workspace's."""
     r = _setup(CASES[1])
     bl, xg, w = r["bl"], r["xg"], r["w"]
     m = bl.mask(r["tl"], r["lse"], w.n, w.causal, NEGL)
-    a = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=True, o_lo=r["olo"])
-    b = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=True, o_lo=r["olo"])
+    kept = int(m["qcnt"].sum().item())
+    ws = bl._lib.bwd_workspace(xg["q"], xg["k"], m, stored_tiles=kept - 1)
+    a = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=True, o_lo=r["olo"],
+               workspace=ws)
+    taken, counted = bl._lib.bwd_stored_taken(ws, w.B, w.H, w.Hk, w.n, w.d)
+    assert not taken and counted == kept
+    b = _bwd_path(r, m, "recompute")
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_deterministic(path):
+    r = _setup(CASES[1])
+    bl, w = r["bl"], r["w"]
+    m = bl.mask(r["tl"], r["lse"], w.n, w.causal, NEGL)
+    a = _bwd_path(r, m, path)
+    b = _bwd_path(r, m, path)
     for u, v in zip(a, b):
         assert torch.equal(u.view(torch.int16), v.view(torch.int16))
 
