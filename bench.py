@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--workload", default="dit-480p-32k")
     ap.add_argument("--negl", type=float, default=None, help="negl_prob (default: the workload's first)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
-    ap.add_argument("--cpu-rows", type=int, default=12288,
+    ap.add_argument("--cpu-rows", type=int, default=20480,
                     help="query rows of head 0 in the oracle's timed sample")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-backward comparison")
     ap.add_argument("--gq-path", choices=["stored", "recompute"], default="stored",

@@ -271,6 +271,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // on one XCD by 20% in the backward, so no remapping is applied.
 __device__ __forceinline__ int work_index(int bid) { return bid; }
 
+
 __device__ __forceinline__ long pair_index(int qt, int kt, int T, bool causal) {
   return causal ? (long)qt * (qt + 1) / 2 + kt : (long)qt * T + kt;
 }

@@ -84,11 +84,10 @@ __global__ __launch_bounds__(256) void gs_slot_kernel(BwdArgs a) {
 // G_Q from stored G_S.  One workgroup of 4 waves per (b, h, query tile qt);
 // wave w owns query rows 32w .. +31 and accumulates G_Q^T (C layout
 // [dim][query]) over the q-list:  G_Q^T += K^T G_S^T, both operands read from
-// LDS with the transpose read.  K rows are shared by the waves (two LDS
-// stages, the next tile's rows copied while the current one is consumed).
-// Each wave's own G_S rows (8 KB per tile, the HBM stream of this pass) are
-// loaded into registers two tiles ahead and written to a private LDS buffer at
-// the start of their tile, so two tiles of G_S are in flight per wave.
+// LDS with the transpose read.  K rows are shared by the waves (three LDS
+// stages, copied two tiles ahead).  Each wave's own G_S rows (8 KB per tile,
+// the HBM stream of this pass) are loaded into registers three tiles ahead and
+// written to a private LDS buffer at the start of their tile.
 //
 // G_S operand, per 16-key step ks (keys 16ks + 4*h32 + {0..3, 8..11}, the same
 // order as the K operand): the slot's fragment-order block of wave kw =
@@ -114,13 +113,22 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   constexpr int NKS = TILE / 16;  // 16-key contraction steps per key tile
   constexpr int GW = 8 * 1024;    // one wave's G_S bytes per tile
   constexpr int NI = DmaOffsets<D, NT>::NI;
+  constexpr int NST = 3;          // K stages (two tiles ahead) and G_S register sets (three ahead)
+  // vector-memory operations one visit issues per wave: NI K copies, 2 row-sum
+  // words, 1 key-mean word, 8 G_S loads
+  constexpr int NSMALL = 3, NGS = 8, PER_VISIT = NI + NSMALL + NGS;
+  // one variable per stage: the compiler then knows a copy into one stage
+  // does not alias reads of another and waits for it only where it is read
   __shared__ __attribute__((aligned(16))) bf16 Ks0[TILE * D];
   __shared__ __attribute__((aligned(16))) bf16 Ks1[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 Ks2[TILE * D];
   __shared__ __attribute__((aligned(16))) char Gw[4 * GW];
   __shared__ __attribute__((aligned(16))) float Lw0[4 * TILE];  // per wave: [key quarter][32 rows]
   __shared__ __attribute__((aligned(16))) float Lw1[4 * TILE];
+  __shared__ __attribute__((aligned(16))) float Lw2[4 * TILE];
   __shared__ __attribute__((aligned(16))) float Kb0[D];
   __shared__ __attribute__((aligned(16))) float Kb1[D];
+  __shared__ __attribute__((aligned(16))) float Kb2[D];
   __shared__ uint16_t itab[MAX_TILES];
 
   const int T = a.T, n = a.n;
@@ -156,35 +164,44 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
   __syncthreads();
 
-  auto kt_at = [&](int i) -> int { return i < cnt ? (int)__builtin_amdgcn_readfirstlane(itab[i]) : 0; };
-  // K rows, row sums and key mean of list item i (key tile kt); past the list, zeros
-  struct Src {
-    __amdgpu_buffer_rsrc_t k, ls, kb;
+  // K rows, row sums and key-mean words of list item i into K stage st; past
+  // the list, zero-range sources (nothing is read, zeros land)
+  auto k_of = [&](auto st) -> bf16* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? Ks0 : S == 1 ? Ks1 : Ks2;
   };
-  auto src_of = [&](int i) -> Src {
+  auto l_of = [&](auto st) -> float* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? Lw0 : S == 1 ? Lw1 : Lw2;
+  };
+  auto b_of = [&](auto st) -> float* {
+    constexpr int S = decltype(st)::value;
+    return S == 0 ? Kb0 : S == 1 ? Kb1 : Kb2;
+  };
+  auto stage_k = [&](int i, auto st) {
     const bool valid = i < cnt;
-    const int kt = kt_at(i), key0 = kt * TILE;
+    const int kt = valid ? (int)__builtin_amdgcn_readfirstlane(itab[i]) : 0, key0 = kt * TILE;
     const uint32_t rows = valid ? (uint32_t)min(TILE, n - key0) : 0u;
     const size_t slot = (size_t)sbase + (size_t)i;
-    return Src{buffer_rsrc(kbase + (long)key0 * kvstride, rows * (uint32_t)kvstride * 2u),
-               buffer_rsrc(a.gsl + slot * (4 * TILE), valid ? 4u * TILE * 4u : 0u),
-               buffer_rsrc(kbar + (long)kt * D, valid ? (uint32_t)D * 4u : 0u)};
-  };
-  // this wave's row sums (2 words per lane) and, in wave 0, the key mean
-  auto stage_small = [&](const Src& s, float* Ld, float* Bd) {
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + (long)key0 * kvstride, rows * (uint32_t)kvstride * 2u);
+    const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a.gsl + slot * (4 * TILE), valid ? 4u * TILE * 4u : 0u);
+    // key mean: D/64 copy instructions; wave w issues number w % (D/64), so
+    // waves beyond the first D/64 repeat a copy (same words to the same place)
+    // and every wave issues one
+    const int kb_part = wave % (D / 64);
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(kbar + (long)kt * D, valid ? (uint32_t)D * 4u : 0u);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int e = lane + 64 * it;
-      load_lds4<true>(s.ls, nullptr, lds_ptr(Ld + wave * TILE + 64 * it),
+      load_lds4<true>(rl, nullptr, lds_ptr(l_of(st) + wave * TILE + 64 * it),
                       (uint32_t)((e >> 5) * TILE + 32 * wave + (e & 31)) * 4u);
     }
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i)
-      if (wave == 0) load_lds4<true>(s.kb, nullptr, lds_ptr(Bd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
+    load_lds4<true>(rb, nullptr, lds_ptr(b_of(st) + 64 * kb_part), (uint32_t)(64 * kb_part + lane) * 4u);
+    static_for<0, NI>([&](auto ic) { stage_k_part<D, NT, decltype(ic)::value>(k_of(st), rk, dmo, wave); });
   };
   // this wave's 8 blocks of item i's G_S into registers: block ib = (kw, s),
   // lane l takes the 16 bytes at position l ^ 8s
-  u32x4 gr[2][8];
+  u32x4 gr[NST][8];
   auto load_gs = [&](u32x4 (&r)[8], int i) {
     const size_t slot = (size_t)sbase + (size_t)i;
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.gs + slot * (TILE * TILE), i < cnt ? TILE * TILE * 2u : 0u);
@@ -197,39 +214,42 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     }
   };
 
-  // prologue: G_S of item 0, K / sums of item 0, then G_S of item 1 (the last
-  // 8 vector-memory operations before the first tile)
+  // prologue, in the order the steady state keeps: G_S 0, K 0, G_S 1, K 1, G_S 2
   load_gs(gr[0], 0);
-  {
-    const Src s0 = src_of(0);
-    stage_small(s0, Lw0, Kb0);
-    static_for<0, NI>([&](auto ic) { stage_k_part<D, NT, decltype(ic)::value>(Ks0, s0.k, dmo, wave); });
-  }
+  stage_k(0, std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
   load_gs(gr[1], 1);
+  stage_k(1, std::integral_constant<int, 1>{});
+  __builtin_amdgcn_sched_barrier(0);
+  load_gs(gr[2], 2);
 
   const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
-  // item j in K stage S and G_S register set S (j % 2 == S)
+  // item j in K stage and G_S register set S = j % 3
   auto visit = [&](int j, auto stage) {
     constexpr int S = decltype(stage)::value;
-    const bf16* Kc = S ? Ks1 : Ks0;
-    const float* Lc = S ? Lw1 : Lw0;
-    const float* Bc = S ? Kb1 : Kb0;
-    bf16* Kn = S ? Ks0 : Ks1;
-    float* Ln = S ? Lw0 : Lw1;
-    float* Bn = S ? Kb0 : Kb1;
-    // everything of item j has landed; item j + 1's G_S (the last 8 loads) may not have
-    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    const std::integral_constant<int, S> cur;
+    const bf16* Kc = k_of(cur);
+    const float* Lc = l_of(cur);
+    const float* Bc = b_of(cur);
+    // item j's K, sums and G_S have landed once at most the operations of the
+    // two later visits' worth (G_S j+1, K j+1, G_S j+2) are outstanding
+    constexpr int VM = NGS + PER_VISIT;
+    static_assert(VM < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib) *reinterpret_cast<u32x4*>(gw + ib * 1024 + lane * 16) = gr[S][ib];
-    __syncthreads();  // K of item j visible; the other K stage is free
-    {
-      const Src ns = src_of(j + 1);
-      stage_small(ns, Ln, Bn);
-      static_for<0, NI>([&](auto ic) { stage_k_part<D, NT, decltype(ic)::value>(Kn, ns.k, dmo, wave); });
-    }
+    // Barrier without the workgroup fence of __syncthreads: the fence would
+    // make every wave finish all its pending LDS copies here (item j + 1's K
+    // too), which would leave K only one tile of lead.  What the barrier must
+    // order is covered explicitly: item j's copies are complete in every wave
+    // (the vmcnt wait above), and every wave's LDS reads of item j - 1, whose
+    // stage the copies issued next overwrite, have returned (lgkmcnt(0)).
+    // The memory clobber keeps the compiler from moving LDS accesses across.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    stage_k(j + 2, std::integral_constant<int, (S + 2) % NST>{});
     __builtin_amdgcn_sched_barrier(0);
-    load_gs(gr[S], j + 2);  // the register set just written to LDS takes item j + 2
+    load_gs(gr[S], j + 3);  // the register set just written to LDS takes item j + 3
     float hsum = 0.f;  // this row's sum of the bf16 G_S operands over the lane's 64 keys
     static_for<0, NKS>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
@@ -268,11 +288,13 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     }
   };
   int j = 0;
-  for (; j + 1 < cnt; j += 2) {
+  for (; j + 2 < cnt; j += 3) {
     visit(j, std::integral_constant<int, 0>{});
     visit(j + 1, std::integral_constant<int, 1>{});
+    visit(j + 2, std::integral_constant<int, 2>{});
   }
   if (j < cnt) visit(j, std::integral_constant<int, 0>{});
+  if (j + 1 < cnt) visit(j + 1, std::integral_constant<int, 1>{});
 
   // epilogue: dq C layout is [dim = 32db + 8(r/4) + 4*h32 + r%4][query l32]
   wait_vmem();
