@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=20480,
                     help="query rows of head 0 in the oracle's timed sample")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-backward comparison")
+    ap.add_argument("--grad-check", action="store_true",
+                    help="report cosine and rel-L2 of the sparse gradients against the dense (negl_prob = 0) ones")
     ap.add_argument("--gq-path", choices=["stored", "recompute"], default="stored",
                     help="G_Q from stored bf16 G_S tiles (workspace slots for every kept tile) or by recomputation")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -220,6 +222,7 @@ def main():
     # the same library's dense backward (negl_prob = 0: every candidate tile)
     dense_ms = None
     dense_stored = None
+    sparse_grads = (dq.clone(), dk.clone(), dv.clone()) if (args.grad_check and not args.no_dense) else None
     if not args.no_dense:
         o, lse, olo = step()
         md = bl.mask(None, lse, n, causal, 0.0)
@@ -237,6 +240,16 @@ def main():
         dense_ms = e0.elapsed_time(e1) / args.steps
         dense_stored = _lib.bwd_stored_taken(ws, B, H, Hk, n, d)[0] if ws.numel() > _lib.bwd_workspace_bytes(
             B, H, Hk, n, d) else False
+
+    # dense-vs-sparse gradients (after the dense timing dq, dk, dv hold the dense ones)
+    grad_cmp = None
+    if sparse_grads is not None:
+        grad_cmp = {}
+        for nm, sp, de in (("dQ", sparse_grads[0], dq), ("dK", sparse_grads[1], dk), ("dV", sparse_grads[2], dv)):
+            a_, r_ = sp.float().flatten(), de.float().flatten()
+            grad_cmp[nm] = {"cos": float(torch.dot(a_, r_) / (a_.norm() * r_.norm())),
+                            "rel_l2": float((a_ - r_).norm() / r_.norm())}
+        del sparse_grads
 
     pairs_dense = (n * (n + 1) / 2) if causal else float(n) * n
     f_dense_bwd = 10.0 * d * B * H * pairs_dense
@@ -292,6 +305,7 @@ def main():
         "mask_ms": mask_ms,
         "dense_bwd_ms": dense_ms,
         "bwd_speedup_vs_dense": (dense_ms / bwd_ms) if dense_ms else None,
+        "dense_vs_sparse_grads": grad_cmp,
         "gq_path": "stored" if gq_stored else "recompute",
         "dense_gq_path": None if dense_stored is None else ("stored" if dense_stored else "recompute"),
         "bwd_workspace_gb": ws_bytes / 1e9,

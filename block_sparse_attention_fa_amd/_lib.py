@@ -234,7 +234,8 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
     return dq, dk, dv
 
 
-PROFILE_KERNELS = ("fwd", "mask_select", "mask_transpose", "delta", "kmean", "dkdv", "dq", "gs_slots")
+PROFILE_KERNELS = ("fwd", "mask_select", "mask_transpose", "delta", "kmean", "dk_plan", "dkdv", "dk_reduce", "dq",
+                   "gs_slots")
 
 
 def profile_enable(on: bool = True):

@@ -23,7 +23,8 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
                       int H, int Hk, int d, float scale, int causal, uint16_t* dq, uint16_t* dk,
                       uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
-                      uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, hipStream_t st);
+                      uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
+                      float* dkpart, int dk_chmin, hipStream_t st);
 }  // namespace backlite
 
 namespace {
@@ -117,9 +118,23 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t delta_bytes(int B, int H, int n) { return round256((size_t)B * H * n * sizeof(float)); }
 }  // namespace
 
+namespace {
+// chunked G_K/G_V work: plan (header, chunk table, per-key-tile counts) and
+// the fp32 partial slots of split key tiles
+size_t dkplan_bytes(int B, int H_k, int n) {
+  const size_t NK = (size_t)B * H_k * ntiles(n);
+  return round256((4 + 11 * NK) * sizeof(int32_t));
+}
+size_t dkpart_bytes(int B, int H_k, int n, int d) {
+  const size_t NK = (size_t)B * H_k * ntiles(n);
+  return round256(NK * 2 * 128 * (size_t)d * sizeof(float));
+}
+}  // namespace
+
 size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d) {
   if (B < 1 || H < 1 || H_k < 1 || n < 1 || d < 1) return 0;
-  return 2 * delta_bytes(B, H, n) + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
+  return 2 * delta_bytes(B, H, n) + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float)) +
+         dkplan_bytes(B, H_k, n) + dkpart_bytes(B, H_k, n, d);
 }
 
 namespace {
@@ -244,11 +259,19 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
     gs = (uint16_t*)(ws + need + idx);
     gsl = (float*)(ws + need + idx + (size_t)cap * 128 * 128 * 2);
   }
+  const size_t kbar_off = 2 * delta_bytes(B, H, n);
+  const size_t plan_off = kbar_off + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
+  const size_t part_off = plan_off + dkplan_bytes(B, H_k, n);
+  int chmin = 16;  // smallest chunk of a split G_K/G_V list (BACKLITE_DKDV_MIN_CHUNK overrides)
+  if (const char* env = std::getenv("BACKLITE_DKDV_MIN_CHUNK")) {
+    const int v = std::atoi(env);
+    if (v >= 1) chmin = v;
+  }
   return hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d,
                                          scale, causal ? 1 : 0, dQ, dK, dV, (float*)ws,
-                                         (float*)(ws + delta_bytes(B, H, n)),
-                                         (float*)(ws + 2 * delta_bytes(B, H, n)), gsinfo, qbase, kslot, gs, gsl,
-                                         cap, (hipStream_t)stream),
+                                         (float*)(ws + delta_bytes(B, H, n)), (float*)(ws + kbar_off), gsinfo,
+                                         qbase, kslot, gs, gsl, cap, (int32_t*)(ws + plan_off),
+                                         (float*)(ws + part_off), chmin, (hipStream_t)stream),
                     "backlite_bwd launch");
 }
 

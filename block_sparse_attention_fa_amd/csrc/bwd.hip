@@ -114,6 +114,146 @@ __global__ __launch_bounds__(256) void kmean_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunked G_K/G_V work.  A key tile's list (every kept query tile of every head
+// of its group) is walked by one workgroup, so one long list serialises the
+// whole pass: with attention sinks every query tile keeps key tile 0, a list
+// of T (x group size) tiles.  Lists longer than the chunk length CH are split
+// into chunks of CH items, each its own workgroup; split chunks leave fp32
+// partial sums that dk_reduce_kernel adds up in chunk order (deterministic).
+// CH = max(minimum, ceil(2 * items / NK)): a split list of m > CH items makes
+// ceil(m / CH) < 2m / CH chunks, so all split chunks together are fewer than
+// 2 * items / CH <= NK.  That bounds the partial slots by NK and the chunks
+// by 2 NK without reading anything back.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void dk_plan_kernel(BwdArgs a) {
+  __shared__ long long part[1024];
+  __shared__ long long part2[1024];
+  __shared__ int chs;
+  const int T = a.T, G = a.H / a.Hk;
+  const int NK = a.B * a.Hk * T;
+  int32_t* items = a.dkplan + 4 + 8 * NK;
+  int32_t* cbase = items + NK;
+  int32_t* pbase = cbase + NK;
+  const int tid = threadIdx.x;
+  const int per = (NK + 1023) / 1024;
+  const int s0 = min(NK, tid * per), s1 = min(NK, s0 + per);
+  long long sum = 0;
+  for (int k = s0; k < s1; ++k) {
+    const int kt = k % T, bg = k / T;
+    const int g = bg % a.Hk, b = bg / a.Hk;
+    int m = 0;
+    for (int hh = 0; hh < G; ++hh) m += max(0, min(a.kcnt[((long)b * a.H + g * G + hh) * T + kt], T));
+    items[k] = m;
+    sum += m;
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 512; off >= 1; off >>= 1) {
+    if (tid < off) part[tid] += part[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const long long total = part[0];
+    chs = (int)max((long long)a.dk_chmin, (2 * total + NK - 1) / NK);
+  }
+  __syncthreads();
+  const int CH = chs;
+  long long csum = 0, psum = 0;
+  for (int k = s0; k < s1; ++k) {
+    const int m = items[k];
+    const int c = m <= CH ? 1 : (m + CH - 1) / CH;
+    csum += c;
+    psum += m <= CH ? 0 : c;
+  }
+  __syncthreads();
+  part[tid] = csum;
+  part2[tid] = psum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const long long v = tid >= off ? part[tid - off] : 0, v2 = tid >= off ? part2[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    part2[tid] += v2;
+    __syncthreads();
+  }
+  long long cr = part[tid] - csum, pr = part2[tid] - psum;
+  for (int k = s0; k < s1; ++k) {
+    const int m = items[k];
+    const int c = m <= CH ? 1 : (m + CH - 1) / CH;
+    cbase[k] = (int)cr;
+    pbase[k] = (int)pr;
+    cr += c;
+    pr += m <= CH ? 0 : c;
+  }
+  if (tid == 1023) {
+    a.dkplan[0] = (int)part[1023];
+    a.dkplan[1] = (int)part2[1023];
+    a.dkplan[2] = CH;
+    a.dkplan[3] = 0;
+  }
+}
+
+// the chunk table: one thread per key tile writes its chunks
+__global__ __launch_bounds__(256) void dk_fill_kernel(BwdArgs a) {
+  const int NK = a.B * a.Hk * a.T;
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= NK) return;
+  const int32_t* items = a.dkplan + 4 + 8 * NK;
+  const int m = items[k], cb = items[NK + k], pb = items[2 * NK + k], CH = a.dkplan[2];
+  int4* tab = reinterpret_cast<int4*>(a.dkplan + 4);
+  if (m <= CH) {
+    tab[cb] = int4{k, 0, m, -1};
+  } else {
+    const int c = (m + CH - 1) / CH;
+    for (int i = 0; i < c; ++i) tab[cb + i] = int4{k, i * CH, min(m, (i + 1) * CH), pb + i};
+  }
+}
+
+// G_K, G_V of split key tiles: sum of the chunks' fp32 partials, in chunk
+// order.  Workgroup (key tile k, slice s) handles 1/RS of the tile's 2*128*d
+// values, 8 per thread, so the partials of one tile are read by RS workgroups
+// at once; unsplit tiles return at once.
+constexpr int DK_RS = 16;
+template <int D>
+__global__ __launch_bounds__(256) void dk_reduce_kernel(BwdArgs a) {
+  const int T = a.T, n = a.n;
+  const int NK = a.B * a.Hk * T;
+  const int k = blockIdx.x / DK_RS, sl = blockIdx.x % DK_RS;
+  const int32_t* items = a.dkplan + 4 + 8 * NK;
+  const int m = items[k], CH = a.dkplan[2];
+  if (m <= CH) return;
+  const int c = (m + CH - 1) / CH, pb = items[2 * NK + k];
+  const int kt = k % T, bg = k / T;
+  const int g = bg % a.Hk, b = bg / a.Hk;
+  const long kvstride = (long)a.Hk * D;
+  const long base = ((long)b * n + (long)kt * TILE) * kvstride + (long)g * D;
+  constexpr int PER = 2 * TILE * D / DK_RS;  // values per workgroup (multiple of 2048)
+#pragma unroll
+  for (int h2 = 0; h2 < PER / 1024; ++h2) {
+    const int e = sl * PER + h2 * 1024 + threadIdx.x * 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float* src = a.dkpart + (size_t)pb * 2 * TILE * D + e;
+    int i = 0;
+    for (; i + 4 <= c; i += 4) {  // four independent loads in flight, added in chunk order
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(src + (size_t)(i + 0) * 2 * TILE * D);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(src + (size_t)(i + 1) * 2 * TILE * D);
+      const f32x4 p2 = *reinterpret_cast<const f32x4*>(src + (size_t)(i + 2) * 2 * TILE * D);
+      const f32x4 p3 = *reinterpret_cast<const f32x4*>(src + (size_t)(i + 3) * 2 * TILE * D);
+      acc += p0;
+      acc += p1;
+      acc += p2;
+      acc += p3;
+    }
+    for (; i < c; ++i) acc += *reinterpret_cast<const f32x4*>(src + (size_t)i * 2 * TILE * D);
+    const int t = e / (TILE * D), row = (e % (TILE * D)) / D, dim = e % D;
+    if (kt * TILE + row >= n) continue;
+    const float sc = t == 0 ? a.scale : 1.f;
+    const bf16x4 o = {(bf16)(acc[0] * sc), (bf16)(acc[1] * sc), (bf16)(acc[2] * sc), (bf16)(acc[3] * sc)};
+    *reinterpret_cast<bf16x4*>((t == 0 ? a.dk : a.dv) + base + (long)row * kvstride + dim) = o;
+  }
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   {
@@ -130,6 +270,16 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int NK = a.B * a.Hk * a.T;
+  {
+    ProfScope ps(PK_DK_PLAN, st);
+    hipLaunchKernelGGL(dk_plan_kernel, dim3(1), dim3(1024), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dk_fill_kernel, dim3((NK + 255) / 256), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // With slots in the workspace, the slot pass decides on the device whether
   // every kept tile fits; the variant of each pass that does not apply returns
   // at once.
@@ -145,6 +295,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     e = D == 64 ? launch_dkdv_d64(a, CAUSAL, st) : launch_dkdv_d128(a, CAUSAL, st);
   }
   if (e != hipSuccess) return e;
+  {
+    ProfScope ps(PK_DK_REDUCE, st);
+    hipLaunchKernelGGL((dk_reduce_kernel<D>), dim3(NK * DK_RS), dim3(256), 0, st, a);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
   e = launch_dq(a, D, CAUSAL, st);
   if (e != hipSuccess || !a.gsinfo) return e;
   return launch_dq_gs(a, D, st);
@@ -155,10 +311,11 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
                       int H, int Hk, int d, float scale, int causal, uint16_t* dq, uint16_t* dk,
                       uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
-                      uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, hipStream_t st) {
-  BwdArgs a{q,    k,      v,     o,     olo, dout, lse,    qcnt, qidx, kcnt, kidx, dq,
-            dk,   dv,     dbuf,  lse2,  kbar, gsinfo, qbase, kslot, gs, gsl, gs_cap, B,
-            n,    H,      Hk,    (n + TILE - 1) / TILE, scale, scale * LOG2E};
+                      uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
+                      float* dkpart, int dk_chmin, hipStream_t st) {
+  BwdArgs a{q,    k,      v,     o,     olo,    dout,   lse,      qcnt, qidx, kcnt, kidx, dq,
+            dk,   dv,     dbuf,  lse2,  kbar,   gsinfo, qbase,    kslot, gs, gsl, gs_cap, dkplan,
+            dkpart, dk_chmin, B, n, H, Hk, (n + TILE - 1) / TILE, scale, scale * LOG2E};
   if (d == 64) return causal ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
   return causal ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
 }

@@ -30,6 +30,14 @@ struct BwdArgs {
   uint16_t* gs;        // slots of 128 x 128 bf16 G_S
   float* gsl;          // per slot, [4 key quarters][128 rows] sums of the G_S rounding residual
   long long gs_cap;    // slots available
+  // Chunked G_K/G_V work (always present): header [4] = {chunks, partial slots,
+  // chunk length, -}, then the chunk table int4 [2 * NK] = {key tile (b, g, kt)
+  // index, first item, end item, partial slot or -1}, then per key tile the
+  // item count, first chunk and first partial slot (int32 [NK] each), where
+  // NK = B * Hk * T.
+  int32_t* dkplan;
+  float* dkpart;       // partial G_K, G_V of split key tiles: [slot][2][128][d] fp32, NK slots
+  int dk_chmin;        // smallest chunk length
   int B, n, H, Hk, T;
   float scale;
   float scale_log2;

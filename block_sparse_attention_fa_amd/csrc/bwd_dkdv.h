@@ -102,11 +102,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ uint32_t stab[GS ? ITAB : 1];  // G_S slot of each windowed item
 
   const int T = a.T, n = a.n;
-  const int L = work_index(blockIdx.x);
-  const int kt = L % T;
-  const int bg = L / T;
+  // this workgroup's chunk of the work: items [i0, i1) of key tile bgk's list
+  // (long lists are split over several workgroups; see dk_plan_kernel)
+  const int NK = a.B * a.Hk * T;
+  const int nchunks = a.dkplan[0];
+  if ((int)blockIdx.x >= nchunks) return;
+  const int4 chunk = reinterpret_cast<const int4*>(a.dkplan + 4)[work_index(blockIdx.x)];
+  const int kt = chunk.x % T;
+  const int bg = chunk.x / T;
   const int g = bg % a.Hk, b = bg / a.Hk;
   const int G = a.H / a.Hk;
+  const int i0 = chunk.y, i1 = chunk.z, pslot = chunk.w;
+  (void)NK;
 
   // wave index as a scalar: branches and LDS copy destinations built from it stay scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -147,17 +154,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   // item is an LDS read, not a global load whose latency would stall the wave
   // between a tile's barrier and the copy of the next tile.
   const long bh0 = (long)b * a.H + (long)g * G;
-  int nitems = 0;
-  for (int hh = 0; hh < G; ++hh) nitems += a.kcnt[(bh0 + hh) * T + kt];
-  auto fill_items = [&](int base) {  // items [base, base + ITAB) of the list, all threads
+  const int nitems = i1 - i0;
+  auto fill_items = [&](int base) {  // items [base, base + ITAB) of the chunk, all threads
+    const int f0 = i0 + base, f1 = min(i0 + base + ITAB, i1);  // in the flattened list
     int p0 = 0;
-    for (int hh = 0; hh < G && p0 < base + ITAB; ++hh) {
+    for (int hh = 0; hh < G && p0 < f1; ++hh) {
       const long row = ((bh0 + hh) * T + kt);
       const int c = a.kcnt[row];
-      const int lo_p = max(base, p0), hi_p = min(base + ITAB, p0 + c);
+      const int lo_p = max(f0, p0), hi_p = min(f1, p0 + c);
       for (int p = lo_p + tid; p < hi_p; p += NT) {
-        itab[p - base] = ((uint32_t)hh << 16) | a.kidx[row * T + (p - p0)];
-        if constexpr (GS) stab[p - base] = a.kslot[row * T + (p - p0)];
+        itab[p - f0] = ((uint32_t)hh << 16) | a.kidx[row * T + (p - p0)];
+        if constexpr (GS) stab[p - f0] = a.kslot[row * T + (p - p0)];
       }
       p0 += c;
     }
@@ -420,9 +427,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     if (def_pending) store_late(def_slot);
   }
 
-  // epilogue: stage as [key][dim] bf16 and store coalesced rows.
-  // C layout: [key = 8(r/4) + 4*h32 + r%4 of block kw][dim = 32db + l32].
+  // epilogue.  C layout: [key = 8(r/4) + 4*h32 + r%4 of block kw][dim = 32db + l32].
   wait_vmem();
+  if (pslot >= 0) {
+    // a chunk of a split list: fp32 partial sums, reduced by dk_reduce_kernel
+    float* pk_ = a.dkpart + (size_t)pslot * 2 * TILE * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = kw * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        pk_[kr * D + db * 32 + l32] = dk[db][r];
+        pk_[(TILE + kr) * D + db * 32 + l32] = dv[db][r];
+      }
+    return;
+  }
+  // a whole list: stage as [key][dim] bf16 and store coalesced rows
   __syncthreads();
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

@@ -5,7 +5,7 @@
 namespace backlite {
 
 hipError_t launch_dkdv_d128_gs(const BwdArgs& a, bool causal, hipStream_t st) {
-  const dim3 grid(a.B * a.Hk * a.T), block(256);
+  const dim3 grid(2 * a.B * a.Hk * a.T), block(256);  // at most 2 chunks per key tile on average
   if (causal) hipLaunchKernelGGL((dkdv_kernel<128, true, true>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((dkdv_kernel<128, false, true>), grid, block, 0, st, a);
   return hipGetLastError();

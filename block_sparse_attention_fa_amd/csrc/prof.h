@@ -15,6 +15,8 @@ enum ProfKernel {
   PK_DKDV,
   PK_DQ,
   PK_GS_SLOTS,
+  PK_DK_PLAN,
+  PK_DK_REDUCE,
   PK_COUNT
 };
 

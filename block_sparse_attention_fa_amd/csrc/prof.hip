@@ -12,7 +12,7 @@
 namespace backlite {
 namespace {
 
-const char* kNames[PK_COUNT] = {"fwd", "mask_select", "mask_transpose", "delta", "kmean", "dkdv", "dq", "gs_slots"};
+const char* kNames[PK_COUNT] = {"fwd", "mask_select", "mask_transpose", "delta", "kmean", "dkdv", "dq", "gs_slots", "dk_plan", "dk_reduce"};
 
 std::atomic<int> g_on{0};
 std::mutex g_mu;

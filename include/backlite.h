@@ -64,9 +64,11 @@ size_t backlite_mask_elems(int B, int H, int n);
 size_t backlite_count_elems(int B, int H, int n);
 
 /* Bytes of device workspace backlite_bwd needs: the per-row D = rowsum(G_O*O)
- * values in fp32 [B, H, n], the row LSE times log2(e) in fp32 [B, H, n], then
- * the per-key-tile mean of K in fp32 [B, H_k, T, d], each part rounded up to
- * 256 bytes.  0 for invalid sizes. */
+ * values in fp32 [B, H, n], the row LSE times log2(e) in fp32 [B, H, n], the
+ * per-key-tile mean of K in fp32 [B, H_k, T, d], the plan of the G_K/G_V
+ * chunks (int32, 4 + 11 NK with NK = B*H_k*T), and fp32 partial sums for key
+ * tiles whose lists are split over several workgroups (NK x 2 x 128 x d),
+ * each part rounded up to 256 bytes.  0 for invalid sizes. */
 size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d);
 
 /* Bytes of a backward workspace that also holds slots for up to max_tiles
@@ -160,6 +162,11 @@ int backlite_mask(const float* tile_lse, const float* lse_row,
  *   backlite_bwd_workspace_bytes_stored) enables the stored-G_S path, chosen
  *   on the device when every kept tile has a slot; both paths compute the
  *   same gradients (G_S rounded to bf16 for the G_Q product either way).
+ * The G_K/G_V work of a key tile whose list is much longer than the average
+ * (e.g. an attention-sink key tile kept by every query tile) is split over
+ * several workgroups whose fp32 partial sums are added in a fixed order; the
+ * environment variable BACKLITE_DKDV_MIN_CHUNK (default 16) sets the smallest
+ * chunk length in tiles.
  * The result is deterministic (no atomics): repeated calls give identical bits. */
 int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
@@ -174,7 +181,8 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
  * backlite_profile_read waits for the outstanding events and returns, for the
  * named kernel, the accumulated elapsed time and the number of launches since
  * the last reset.  Kernel names: "fwd", "mask_select", "mask_transpose",
- * "delta", "kmean", "dkdv", "dq", "gs_slots" (slot assignment of the stored
+ * "delta", "kmean", "dkdv", "dq", "dk_plan" (the G_K/G_V chunk plan),
+ * "dk_reduce" (sums of split chunks), "gs_slots" (slot assignment of the stored
  * path; "dkdv" and "dq" then also count the launch of the pass variant that
  * returns at once).  Process-wide state, thread-safe; enabling
  * adds two event records per launch.  read returns BACKLITE_ERR_INVALID_ARG

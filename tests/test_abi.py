@@ -38,12 +38,14 @@ def test_sizes(L):
     assert L.backlite_tile_lse_elems(1, 40, 75600, 0) == 40 * 591 * 591 * 128
     assert L.backlite_mask_elems(2, 3, 129) == 2 * 3 * 4
     assert L.backlite_count_elems(2, 3, 129) == 2 * 3 * 2
-    # D and LSE*log2(e): 1*2*100 floats = 800 B -> 1024 each; kbar: 1*2*1*64 floats = 512 B
-    assert L.backlite_bwd_workspace_bytes(1, 2, 2, 100, 64) == 2 * 1024 + 512
+    # D and LSE*log2(e): 1*2*100 floats = 800 B -> 1024 each; kbar: 1*2*1*64 floats = 512 B;
+    # G_K/G_V chunk plan: NK = 2 key tiles, 4 + 11*2 int32 = 104 B -> 256; partial sums:
+    # 2 x 2 x 128 x 64 floats = 131072 B
+    base = 2 * 1024 + 512 + 256 + 131072
+    assert L.backlite_bwd_workspace_bytes(1, 2, 2, 100, 64) == base
     assert L.backlite_tile_lse_elems(0, 1, 1, 0) == 0
     # stored-G_S workspace: base, 256 B of state words, qbase (2 x 1 uint32 -> 256 B),
-    # kslot (2 x 1 x 1 uint32 -> 256 B), then 34816 B (32 KB G_S + 2 KB residual sums) per slot
-    base = 2 * 1024 + 512
+    # kslot (2 x 1 x 1 uint32 -> 256 B), then 34816 B (32 KB G_S + 2 KB row sums) per slot
     assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 0) == base
     assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 3) == base + 3 * 256 + 3 * 34816
     assert L.backlite_bwd_state_offset(1, 2, 2, 100, 64) == base

@@ -197,6 +197,43 @@ def test_stored_path_falls_back_when_slots_run_out():
         assert torch.equal(u.view(torch.int16), v.view(torch.int16))
 
 
+# attention sinks: every query tile keeps key tile 0, whose list (48 items over
+# the 4 heads of the group) is several times the average list
+SINK = small(1536, H=4, Hk=1, d=64, causal=True, kind="positional", seed=9, period=512.0)
+
+
+def _expected_split(lists, B, Hk, G, T, chmin):
+    """Host-side copy of the chunk-length rule, to check that a case splits."""
+    kc = lists["kcnt"].cpu().numpy().reshape(B, Hk, G, T).sum(axis=2)
+    ch = max(chmin, -(-2 * int(kc.sum()) // (B * Hk * T)))
+    return int(kc.max()), ch
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("chmin", [1, 16])
+def test_backward_split_lists(chmin, path, monkeypatch):
+    """G_K/G_V lists split over several workgroups (the sink key tile's list is
+    split into chunks whose fp32 partials are summed in order): gradients match
+    the oracle, G_Q is unchanged by the split, and results repeat bit for bit."""
+    w = SINK
+    r = _setup(w)
+    x = r["x"]
+    keep = orc.mask_from_stats(r["ref"]["tile_lse"], r["ref"]["lse"], w.n, w.causal, NEGL)
+    lists = lists_to_torch(keep, r["dev"])
+    longest, ch = _expected_split(lists, w.B, w.Hk, w.H // w.Hk, orc.ntiles(w.n), chmin)
+    flush_print(f"  longest list {longest} items, chunk length {ch}")
+    assert longest > ch, "the case must split a list"
+    monkeypatch.setenv("BACKLITE_DKDV_MIN_CHUNK", str(chmin))
+    dq, dk, dv = _bwd_path(r, lists, path)
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal)
+    for name, got, ref in (("dQ", dq, g["dQ"]), ("dK", dk, g["dK"]), ("dV", dv, g["dV"])):
+        rl, cs = assert_close_grad(name, got.cpu(), ref)
+        flush_print(f"  split {path} {name}: rel-L2 {rl:.2e} cos {cs:.6f}")
+    again = _bwd_path(r, lists, path)
+    for u, v in zip((dq, dk, dv), again):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_backward_deterministic(path):
     r = _setup(CASES[1])
