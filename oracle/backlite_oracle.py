@@ -383,3 +383,76 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
     out["dK"] = dK
     out["dV"] = dV
     return out
+
+
+# ----------------------------------------------------------------------------
+# negl_prob calibration
+# ----------------------------------------------------------------------------
+GRADS = ("dQ", "dK", "dV")
+
+
+def gradient_agreement(g, ref):
+    """(cosine, rel-L2) of each of G_Q, G_K, G_V against the reference
+    gradients: the two similarity metrics the blog compares BackLite's
+    gradients with exact FlashAttention's by ("Introducing BackLite",
+    "Experiments")."""
+    return {nm: (cosine(g[nm], ref[nm]), rel_l2(g[nm], ref[nm])) for nm in GRADS}
+
+
+def within_targets(agree, cos_min, rel_max):
+    """Every gradient has cosine > cos_min and rel-L2 < rel_max (the blog's
+    calibration targets are strict: cosine similarity > 0.99, relative L2
+    difference < 0.1; "Preliminary results with Wan 2.1 1.3b", Fig. 4)."""
+    return all(c > cos_min and r < rel_max for c, r in agree.values())
+
+
+def calibrate(q, k, v, do, causal=False, scale=None, cos_min=0.99, rel_max=0.1, pi_max=0.5, iters=8,
+              tile=TILE):
+    """The largest negl_prob in [0, pi_max] (to the bisection's resolution) whose
+    masked gradients stay within the targets of the dense (negl_prob = 0) ones.
+
+    The pages describe a tool that picks the neglected weight to meet a minimum
+    cosine similarity and a maximum relative L2 difference ("Introducing
+    BackLite", "Preliminary results with Wan 2.1 1.3b"; README "Overview",
+    Tunable).  They do not give its search; this reading bisects, which relies
+    on the keep sets shrinking as negl_prob grows: pi_max is tried first, then
+    `iters` halvings of [lo, hi] with lo always within the targets (lo = 0 is
+    the dense backward itself).
+
+    Returns negl_prob (the last value within the targets), upper (the smallest
+    value tried that was not, or pi_max), its keep mask, the gradient agreement
+    and the sparsity (1 - kept / candidate tile pairs), plus every probe
+    (negl_prob, within) in order.
+    """
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, n, H, _ = q.shape
+    f = forward(q, k, v, scale=scale, causal=causal, tile=tile)
+    dense = backward(q, k, v, do, keep=None, scale=scale, causal=causal, tile=tile)
+    cand = candidates(n, causal, tile)
+    ncand = B * H * int(cand.sum())
+
+    def probe(pi):
+        keep = mask_from_stats(f["tile_lse"], f["lse"], n, causal, pi, tile)
+        g = backward(q, k, v, do, keep=keep, scale=scale, causal=causal, tile=tile)
+        agree = gradient_agreement(g, dense)
+        return within_targets(agree, cos_min, rel_max), keep, agree
+
+    probes = []
+    ok, keep, agree = probe(pi_max)
+    probes.append((pi_max, ok))
+    if ok:
+        return dict(negl_prob=pi_max, upper=pi_max, keep=keep, agreement=agree,
+                    sparsity=1.0 - keep.sum() / ncand, probes=probes)
+    lo, hi = 0.0, pi_max
+    best_keep = np.broadcast_to(cand, (B, H) + cand.shape).copy()
+    best_agree = gradient_agreement(dense, dense)
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        ok, keep, agree = probe(mid)
+        probes.append((mid, ok))
+        if ok:
+            lo, best_keep, best_agree = mid, keep, agree
+        else:
+            hi = mid
+    return dict(negl_prob=lo, upper=hi, keep=best_keep, agreement=best_agree,
+                sparsity=1.0 - best_keep.sum() / ncand, probes=probes)

@@ -414,3 +414,68 @@ def test_sampled_rows_only_mode_and_stats_reuse():
     again = orc.sampled_head_group(q, k, v, do, [0], 0.1, True, q_tiles=[1, 4], k_tiles=[0], tile=64,
                                    stats=full["stats"])
     np.testing.assert_allclose(again["dK"][0], full["dK"][0], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# negl_prob calibration
+# ----------------------------------------------------------------------------
+def test_calibrate_block_diagonal_limit_takes_pi_max():
+    """Block-structured inputs: off-diagonal tile weights are ~1e-19, so every
+    negl_prob in [1e-15, 1) keeps exactly the diagonal tiles, whose masked
+    gradients differ from the dense ones by ~1e-10 relative (the skipped
+    tiles' own weight): the first probe, pi_max, is within any target."""
+    x = make_inputs(TINY)
+    r = orc.calibrate(x["q"], x["k"], x["v"], x["do"], causal=False, pi_max=0.9, iters=4)
+    assert r["negl_prob"] == 0.9 and r["probes"] == [(0.9, True)]
+    assert r["sparsity"] == 1.0 - 1.0 / 8
+    for c, rl in r["agreement"].values():
+        assert c > 1 - 1e-12 and rl < 1e-8
+
+
+def test_calibrate_trivial_targets():
+    """Targets every gradient meets -> pi_max; a cosine above 1 that nothing
+    meets (strict) -> 0, bracketed by the first bisection step."""
+    w = small(384, H=1, d=64, causal=True, kind="gaussian", seed=31)
+    x = make_inputs(w)
+    r = orc.calibrate(x["q"], x["k"], x["v"], x["do"], causal=True, cos_min=-2.0, rel_max=np.inf, pi_max=0.5)
+    assert r["negl_prob"] == 0.5 and len(r["probes"]) == 1
+    r = orc.calibrate(x["q"], x["k"], x["v"], x["do"], causal=True, cos_min=1.0, rel_max=np.inf, pi_max=0.5,
+                      iters=3)
+    assert r["negl_prob"] == 0.0 and r["upper"] == 0.0625 and r["sparsity"] == 0.0
+    assert [p for p, _ in r["probes"]] == [0.5, 0.25, 0.125, 0.0625]
+
+
+def test_calibrate_brackets_the_largest_value_within_targets():
+    """On unstructured inputs the bisection ends with negl_prob within the
+    targets and `upper` (pi_max / 2^iters above it) outside them, each checked
+    here by recomputing mask, gradients and metrics; the keep sets of the
+    probed values are nested (larger negl_prob keeps a subset)."""
+    w = small(640, H=2, Hk=1, d=64, causal=True, kind="gaussian", seed=22)
+    x = make_inputs(w)
+    iters = 6
+    r = orc.calibrate(x["q"], x["k"], x["v"], x["do"], causal=True, cos_min=0.99, rel_max=0.1, pi_max=0.5,
+                      iters=iters)
+    assert 0.0 < r["negl_prob"] < r["upper"] < 0.5
+    assert r["upper"] - r["negl_prob"] == 0.5 / 2 ** iters
+    f = orc.forward(x["q"], x["k"], x["v"], causal=True)
+    dense = orc.backward(x["q"], x["k"], x["v"], x["do"], causal=True)
+
+    def agree(pi):
+        keep = orc.mask_from_stats(f["tile_lse"], f["lse"], w.n, True, pi)
+        g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=True)
+        out = {}
+        for nm in ("dQ", "dK", "dV"):
+            a, b = g[nm].ravel(), dense[nm].ravel()
+            out[nm] = (float(a @ b / np.linalg.norm(a) / np.linalg.norm(b)),
+                       float(np.linalg.norm(a - b) / np.linalg.norm(b)))
+        return keep, out
+
+    keep_lo, a_lo = agree(r["negl_prob"])
+    assert all(c > 0.99 and rl < 0.1 for c, rl in a_lo.values())
+    assert (keep_lo == r["keep"]).all()
+    _, a_hi = agree(r["upper"])
+    assert not all(c > 0.99 and rl < 0.1 for c, rl in a_hi.values())
+    pis = sorted(p for p, _ in r["probes"])
+    keeps = [orc.mask_from_stats(f["tile_lse"], f["lse"], w.n, True, p) for p in pis]
+    for k0, k1 in zip(keeps, keeps[1:]):
+        assert not (k1 & ~k0).any()
