@@ -191,34 +191,30 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   // it reads to get the rounding residual's row sums.  After the butterfly in
   // the tile's B phases, lane (bits b0..b5) holds the sum for query row
   // 16 b3 + 8 b2 + 4 b5 + 2 b1 + b4 of the chunk; odd lanes hold a copy and
-  // store out of range (dropped).  The stores of chunks 2 and 3 are issued
-  // after the next tile's barrier (or after the last tile): issued at the end
-  // of a tile they would still be in flight at the next tile's wait for its
-  // staged operands, which counts stores too.
+  // store out of range (dropped).  The stores of chunk 3 are issued after the
+  // next tile's barrier (or after the last tile): issued at the end of a tile
+  // they would still be in flight at the next tile's wait for its staged
+  // operands, which counts stores too.
   const bool kragged = (kt + 1) * TILE > n;
   const uint32_t gs_voff = (uint32_t)(2 * l32 + h32) * 16u;
   const uint32_t ls_q = 16 * ((lane >> 3) & 1) + 8 * ((lane >> 2) & 1) + 4 * (lane >> 5) + 2 * ((lane >> 1) & 1) +
                         ((lane >> 4) & 1);
   const bool sel3 = (lane >> 3) & 1, sel2 = (lane >> 2) & 1, sel1 = (lane >> 1) & 1;
   bf16x8 pk[2][2], sk[2][2];  // packed bf16 P and G_S operands [chunk parity][sub-step]
-  float bw_def[2] = {0.f, 0.f};   // row sums of chunks 2, 3 awaiting their store
-  bool def_pending = false;       // chunks 2, 3 of the previous tile not stored yet
+  float bw_def = 0.f;             // row sums of chunk 3 awaiting their store
+  bool def_pending = false;       // chunk 3 of the previous tile not stored yet
   uint32_t def_slot = 0;
-  // stores of chunks 2 and 3 of the tile in slot `slot` (their operands are
-  // still in sk[0], sk[1])
+  // stores of chunk 3 of the tile in slot `slot` (its operands are still in sk[1])
   auto store_late = [&](uint32_t slot) {
     const bool ok = (long long)slot < a.gs_cap;
     const __amdgpu_buffer_rsrc_t r1 = buffer_rsrc(a.gs + (size_t)slot * (TILE * TILE), ok ? TILE * TILE * 2u : 0u);
     const __amdgpu_buffer_rsrc_t r2 = buffer_rsrc(a.gsl + (size_t)slot * (4 * TILE), ok ? 4u * TILE * 4u : 0u);
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sk[c2][s2]), r1, gs_voff,
-                                               (kw * 8 + (2 + c2) * 2 + s2) * 1024, CPOL_NT);
-      const uint32_t off = (lane & 1) ? 0x40000000u : (uint32_t)(kw * TILE + 32 * (2 + c2) + ls_q) * 4u;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, bw_def[c2]), r2, off, 0, CPOL_NT);
-    }
+    for (int s2 = 0; s2 < 2; ++s2)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sk[1][s2]), r1, gs_voff,
+                                             (kw * 8 + 3 * 2 + s2) * 1024, CPOL_NT);
+    const uint32_t off = (lane & 1) ? 0x40000000u : (uint32_t)(kw * TILE + 32 * 3 + ls_q) * 4u;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, bw_def), r2, off, 0, CPOL_NT);
   };
   // stage S (a compile-time 0 or 1) holds item j; the other stage receives j + 1
   auto visit = [&](int j, auto stage) {
@@ -298,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         sacc[c4 & 1] = f32x16{};
         gacc[c4 & 1] = f32x16{};
       }
-      if constexpr (GS && SC::is_b(ph) && st == 0 && c4 < 2) {
+      if constexpr (GS && SC::is_b(ph) && st == 0 && c4 < 3) {
         // chunk c4's bf16 G_S operands to the tile's slot
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
@@ -331,8 +327,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         // lane, summed over lanes l, l ^ 16 by the 16-lane row swap (row parity
         // picks the row).  Groups 8-14: halving exchanges within 16-lane rows
         // (mirror, half mirror, xor 2), each lane keeping the half its lane bit
-        // selects.  Group 15: the xor-1 sum and the store (chunks 0, 1) or its
-        // deferral (chunks 2, 3).
+        // selects.  Group 15: the xor-1 sum and the store (chunks 0-2) or its
+        // deferral (chunk 3).
         f32x16& gv = gacc[c4 & 1];
         static_for<0, 16>([&](auto gc) {
           constexpr int gi = decltype(gc)::value;
@@ -357,11 +353,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
               bw = kp + dpp<DPP_XOR2>(snd);
             } else {
               bw += dpp<DPP_XOR1>(bw);
-              if constexpr (c4 < 2) {
+              if constexpr (c4 < 3) {
                 const uint32_t off = (lane & 1) ? 0x40000000u : (uint32_t)(kw * TILE + 32 * c4 + ls_q) * 4u;
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, bw), lsr, off, 0, CPOL_NT);
               } else {
-                bw_def[c4 - 2] = bw;
+                bw_def = bw;
               }
             }
           }
