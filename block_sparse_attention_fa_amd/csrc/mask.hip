@@ -13,9 +13,9 @@
 //      groups each take one key tile at a time, a lane reads 4 rows (one
 //      16-byte load per lane, 512 contiguous bytes per tile).
 //   2. bitonic sort of (a, kt) in LDS, ascending, ties by kt.
-//   3. one lane walks the sorted list adding exp(a) in fp64 left to right and
-//      stops at the first running sum >= negl_prob; everything before is
-//      skipped (the walk visits only the skipped prefix plus one).
+//   3. all threads form the weights exp(a) in fp64; one lane then walks the
+//      sorted list adding them left to right and stops at the first running
+//      sum >= negl_prob; everything before is skipped.
 //   4. keep row and the ascending q-list (block-wide prefix count).
 // transpose_kernel: one workgroup per (b, h, kt) turns column kt of the keep
 // bitmap into the ascending k-list.
@@ -90,17 +90,30 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
     for (int u = 0; u < 4; ++u) ls[u] = (r0 + u < a.n) ? (double)a.lse[(long)bh * a.n + r0 + u] : 0.0;
     const long pairs = a.causal ? (long)T * (T + 1) / 2 : (long)T * T;
     const float* tl = a.tlse + (long)bh * pairs * TILE;
-    for (int kt = grp; kt < nc; kt += MASK_NT / 32) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(tl + pair_index(qt, kt, T, a.causal) * TILE + gl * 4);
-      double m = -INFINITY;
+    // four key tiles per group and pass: their loads are issued together, so
+    // each lane has four 16-byte loads in flight instead of one
+    constexpr int NG = MASK_NT / 32, UN = 4;
+    for (int kb = grp; kb < nc; kb += NG * UN) {
+      f32x4 v[UN];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (r0 + u < a.n) m = fmax(m, (double)v[u] - ls[u]);
+      for (int x = 0; x < UN; ++x) {
+        const int kt = kb + x * NG;
+        v[x] = kt < nc ? *reinterpret_cast<const f32x4*>(tl + pair_index(qt, kt, T, a.causal) * TILE + gl * 4)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 32));
-      if (gl == 0) {
-        sa[kt] = m;
-        sk[kt] = kt;
+      for (int x = 0; x < UN; ++x) {
+        const int kt = kb + x * NG;
+        double m = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (r0 + u < a.n) m = fmax(m, (double)v[x][u] - ls[u]);
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 32));
+        if (gl == 0 && kt < nc) {
+          sa[kt] = m;
+          sk[kt] = kt;
+        }
       }
     }
     for (int i = nc + tid; i < P2; i += MASK_NT) {
@@ -128,12 +141,17 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
         __syncthreads();
       }
     }
-    // ---- 3. sequential fp64 prefix, stop at the first sum >= negl_prob
+    // ---- 3. sequential fp64 prefix, stop at the first sum >= negl_prob.  The
+    // weights exp(a) are formed by all threads first (in place; the sorted
+    // log-weights are not needed afterwards), so the one walking lane only
+    // adds, in the same left-to-right order.
+    for (int i = tid; i < nc; i += MASK_NT) sa[i] = exp(sa[i]);
+    __syncthreads();
     if (tid == 0) {
       double acc = 0.0;
       int r = 0;
       for (; r < nc; ++r) {
-        acc += exp(sa[r]);
+        acc += sa[r];
         if (!(acc < a.negl)) break;
       }
       s_skip = r;
