@@ -152,24 +152,33 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt * c);
-    const float alpha = fast_exp2(m_run - m_new);
+    // Lazy rescaling: the running maximum (and with it O and l) moves only when
+    // some row's maximum grows by more than 2^8; otherwise the tile's
+    // probabilities are taken against the old maximum (at most 2^8, exact in
+    // fp32 and in the bf16 operand's relative precision).  Every quantity is
+    // m + log2(sum 2^(s - m)) for whichever m is used, so the result is the same
+    // softmax; the wave skips the rescale of its O accumulators in most tiles.
+    const float m_cand = fmaxf(m_run, mt * c);
+    if (__any(m_cand - m_run > 8.f)) {
+      const float alpha = fast_exp2(m_run - m_cand);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_run = m_cand;
+    }
     float ts = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(fmaf(s[kb][r], c, -m_new));
+        const float pv = fast_exp2(fmaf(s[kb][r], c, -m_run));
         s[kb][r] = pv;
         ts += pv;
       }
     ts += __shfl_xor(ts, 32);
-    l_run = l_run * alpha + ts;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    l_run += ts;
     if (tl_row && h32 == 0) {
-      const float t = (qrow < n) ? (m_new + __log2f(ts)) * LN2 : -INFINITY;
+      const float t = (qrow < n) ? (m_run + __log2f(ts)) * LN2 : -INFINITY;
       tl_row[pair_index(qt, kt, T, CAUSAL) * TILE + lrow] = t;
     }
     // O^T += V^T P^T.  Step st of key block kb covers keys 32kb + 16st + 4*h32 + 0..3
