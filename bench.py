@@ -127,8 +127,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the hot path shards by (batch, kv-head group) with no exchange, so multi-GPU runs are not "
-              "part of this build", file=sys.stderr)
+              "the hot path would shard by (batch, kv-head group) with no exchange; multi-GPU runs are "
+              "not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
