@@ -65,23 +65,38 @@ def kv_head(h: int, H: int, Hk: int) -> int:
     return h // (H // Hk)
 
 
-def candidates(n: int, causal: bool, tile: int = TILE) -> np.ndarray:
+def candidates(n: int, causal: bool, tile: int = TILE, window: int = 0) -> np.ndarray:
     """cand[qt, kt]: the key tile holds at least one (i, j) with i, j < n that the
-    causal rule (j <= i) allows.  Causally empty tiles are never candidates."""
+    causal rule (j <= i) allows.  Causally empty tiles are never candidates.
+
+    window > 0 (causal only): a sliding window of `window` keys, key j visible to
+    query i iff i - window < j <= i (our reading of the blog's Nanochat windows of
+    1024 / 2048 tokens, "Training Nanochat").  A tile pair is then a candidate iff
+    its first key is <= its last row and its last key is > its first row - window.
+    """
     T = ntiles(n, tile)
     qt = np.arange(T)[:, None]
     kt = np.arange(T)[None, :]
+    if window:
+        assert causal, "a sliding window is causal"
+        i_lo, i_hi = qt * tile, np.minimum(n, (qt + 1) * tile) - 1
+        k_lo, k_hi = kt * tile, np.minimum(n, (kt + 1) * tile) - 1
+        return (k_lo <= i_hi) & (k_hi > i_lo - window)
     if causal:
         return kt <= qt   # tile kt's first key 128*kt is <= the last row of tile qt
     return np.ones((T, T), bool)
 
 
-def _score_block(qh, kh, rows, scale, causal):
-    """S for query rows `rows` against all keys, -inf where causally masked."""
+def _score_block(qh, kh, rows, scale, causal, window=0):
+    """S for query rows `rows` against all keys, -inf where causally masked
+    (and, with a sliding window, where j <= i - window)."""
     S = scale * (qh[rows] @ kh.T)
     if causal:
         j = np.arange(kh.shape[0])[None, :]
-        S = np.where(j <= rows[:, None], S, -np.inf)
+        ok = j <= rows[:, None]
+        if window:
+            ok &= j > rows[:, None] - window
+        S = np.where(ok, S, -np.inf)
     return S
 
 
@@ -108,7 +123,7 @@ def _tile_lse(S, n, tile):
 # ----------------------------------------------------------------------------
 # forward with per-(row, key tile) statistics
 # ----------------------------------------------------------------------------
-def forward(q, k, v, scale=None, causal=False, tile=TILE, heads=None, rows=None, block=128):
+def forward(q, k, v, scale=None, causal=False, tile=TILE, heads=None, rows=None, block=128, window=0):
     """Exact attention forward plus tile statistics.
 
     Returns dict with O [B, nr, H', d], lse [B, H', nr], tile_lse [B, H', nr, T]
@@ -130,7 +145,7 @@ def forward(q, k, v, scale=None, causal=False, tile=TILE, heads=None, rows=None,
             qh, kh, vh = q[b, :, h], k[b, :, g], v[b, :, g]
             for s in range(0, len(rows), block):
                 r = rows[s:s + block]
-                S = _score_block(qh, kh, r, scale, causal)
+                S = _score_block(qh, kh, r, scale, causal, window)
                 L = _row_lse(S)
                 P = np.exp(S - L[:, None])
                 O[b, s:s + block, hi] = P @ vh
@@ -142,7 +157,7 @@ def forward(q, k, v, scale=None, causal=False, tile=TILE, heads=None, rows=None,
 # ----------------------------------------------------------------------------
 # mask from statistics
 # ----------------------------------------------------------------------------
-def tile_log_weights(tile_lse, lse, n, causal, tile=TILE):
+def tile_log_weights(tile_lse, lse, n, causal, tile=TILE, window=0):
     """a[b, h, qt, kt] = max over valid rows i of the query tile of
     (LSE_tile[i, kt] - LSE_row[i]), in fp64; the tile weight is w = exp(a)
     (README phase 2: p_tile = exp(LSE_tile - LSE_row)).  -inf off-candidate.
@@ -157,7 +172,7 @@ def tile_log_weights(tile_lse, lse, n, causal, tile=TILE):
     pad = np.full((B, H, T * tile, T), -np.inf)
     pad[:, :, :n] = diff
     a = pad.reshape(B, H, T, tile, T).max(axis=3)
-    cand = candidates(n, causal, tile)
+    cand = candidates(n, causal, tile, window)
     return np.where(cand[None, None], a, -np.inf)
 
 
@@ -188,9 +203,9 @@ def select_keep(a, cand, negl_prob):
     return keep
 
 
-def mask_from_stats(tile_lse, lse, n, causal, negl_prob, tile=TILE):
-    a = tile_log_weights(tile_lse, lse, n, causal, tile)
-    cand = candidates(n, causal, tile)
+def mask_from_stats(tile_lse, lse, n, causal, negl_prob, tile=TILE, window=0):
+    a = tile_log_weights(tile_lse, lse, n, causal, tile, window)
+    cand = candidates(n, causal, tile, window)
     return select_keep(a, cand, negl_prob)
 
 
@@ -224,7 +239,7 @@ def delta(do, o):
 
 
 def backward(q, k, v, do, keep=None, scale=None, causal=False, tile=TILE,
-             heads=None, q_rows=None):
+             heads=None, q_rows=None, window=0):
     """Masked attention backward in fp64.
 
     keep: [B, H, T, T] bool tile mask over *all* heads (None = every candidate).
@@ -240,7 +255,7 @@ def backward(q, k, v, do, keep=None, scale=None, causal=False, tile=TILE,
     heads = list(range(H)) if heads is None else list(heads)
     rows = np.arange(n) if q_rows is None else np.asarray(q_rows)
     T = ntiles(n, tile)
-    cand = candidates(n, causal, tile)
+    cand = candidates(n, causal, tile, window)
     dQ = np.zeros((B, len(rows), len(heads), d))
     dK = np.zeros((B, n, Hk, d))
     dV = np.zeros((B, n, Hk, d))
@@ -255,7 +270,7 @@ def backward(q, k, v, do, keep=None, scale=None, causal=False, tile=TILE,
             km = cand if keep is None else np.asarray(keep[b, h], bool)
             for s in range(0, len(rows), tile):
                 r = rows[s:s + tile]
-                S = _score_block(qh, kh, r, scale, causal)
+                S = _score_block(qh, kh, r, scale, causal, window)
                 L = _row_lse(S)
                 P = np.exp(S - L[:, None])
                 O = P @ vh

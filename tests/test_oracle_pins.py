@@ -479,3 +479,89 @@ def test_calibrate_brackets_the_largest_value_within_targets():
     keeps = [orc.mask_from_stats(f["tile_lse"], f["lse"], w.n, True, p) for p in pis]
     for k0, k1 in zip(keeps, keeps[1:]):
         assert not (k1 & ~k0).any()
+
+
+# ----------------------------------------------------------------------------
+# sliding window (causal, `window` keys: i - window < j <= i)
+# ----------------------------------------------------------------------------
+def _torch_window_attention(q, k, v, scale, window):
+    """torch fp64 attention with an explicit boolean band mask (library ops)."""
+    B, n, H, d = q.shape
+    G = H // k.shape[2]
+    qt = q.permute(0, 2, 1, 3)
+    kt = k.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    vt = v.repeat_interleave(G, dim=2).permute(0, 2, 1, 3)
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    band = (j <= i) & (j > i - window)
+    S = (scale * torch.matmul(qt, kt.transpose(-1, -2).contiguous())).masked_fill(~band, float("-inf"))
+    P = torch.softmax(S, dim=-1)
+    return torch.matmul(P, vt).permute(0, 2, 1, 3), torch.logsumexp(S, dim=-1)
+
+
+@pytest.mark.parametrize("n,tile,window", [(50, 8, 1), (50, 8, 7), (50, 8, 8), (50, 8, 13), (37, 4, 5)])
+def test_window_candidates_brute_force(n, tile, window):
+    """A tile pair is a candidate iff it holds a visible (i, j): every pair enumerated."""
+    T = orc.ntiles(n, tile)
+    ref = np.zeros((T, T), bool)
+    for i in range(n):
+        for j in range(max(0, i - window + 1), i + 1):
+            ref[i // tile, j // tile] = True
+    assert (orc.candidates(n, True, tile, window) == ref).all()
+
+
+def test_window_at_least_n_is_plain_causal():
+    n = 300
+    q, k, v, do = (_rand((1, n, h, 16), s) for s, h in ((1, 4), (2, 2), (3, 2), (4, 4)))
+    for w in (n, n + 50):
+        a = orc.forward(q, k, v, causal=True, tile=64, window=w)
+        b = orc.forward(q, k, v, causal=True, tile=64)
+        for key in ("O", "lse", "tile_lse"):
+            assert np.array_equal(a[key], b[key])
+        ga = orc.backward(q, k, v, do, causal=True, tile=64, window=w)
+        gb = orc.backward(q, k, v, do, causal=True, tile=64)
+        for key in ("dQ", "dK", "dV"):
+            assert np.array_equal(ga[key], gb[key])
+        assert (orc.candidates(n, True, 64, w) == orc.candidates(n, True, 64)).all()
+
+
+def test_window_one_is_self_attention():
+    """window = 1: each row sees only itself, so O = V (of its kv head),
+    LSE_i = s_ii, G_S = 0 (P = I and G_P_ii = D_i), hence G_Q = G_K = 0, and
+    G_V = G_O summed over the query heads of each kv head."""
+    n, H, Hk, d = 200, 4, 2, 16
+    q, k, v, do = _rand((1, n, H, d), 5), _rand((1, n, Hk, d), 6), _rand((1, n, Hk, d), 7), _rand((1, n, H, d), 8)
+    sc = 0.25
+    f = orc.forward(q, k, v, scale=sc, causal=True, tile=64, window=1)
+    g = orc.backward(q, k, v, do, scale=sc, causal=True, tile=64, window=1)
+    G = H // Hk
+    for h in range(H):
+        kv = h // G
+        np.testing.assert_array_equal(f["O"][0, :, h], v[0, :, kv])
+        np.testing.assert_allclose(f["lse"][0, h], sc * (q[0, :, h] * k[0, :, kv]).sum(-1), rtol=0, atol=1e-12)
+    assert np.abs(g["dQ"]).max() < 1e-12 and np.abs(g["dK"]).max() < 1e-12
+    np.testing.assert_allclose(g["dV"][0], do[0].reshape(n, Hk, G, d).sum(2), rtol=0, atol=1e-12)
+    # only the diagonal tiles are candidates
+    assert (orc.candidates(n, True, 64, 1) == np.eye(orc.ntiles(n, 64), dtype=bool)).all()
+
+
+@pytest.mark.parametrize("n,window", [(300, 100), (257, 64), (200, 129)])
+def test_window_matches_torch_library(n, window):
+    """Forward against torch fp64 with an explicit band mask; gradients against
+    torch autograd through the same masked attention."""
+    H, Hk, d = 4, 2, 16
+    q, k, v, do = _rand((1, n, H, d), 11), _rand((1, n, Hk, d), 12), _rand((1, n, Hk, d), 13), _rand((1, n, H, d), 14)
+    sc = 0.3
+    f = orc.forward(q, k, v, scale=sc, causal=True, tile=64, window=window)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    O, lse = _torch_window_attention(tq, tk, tv, sc, window)
+    np.testing.assert_allclose(f["O"], O.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(f["lse"][0], lse.detach().numpy()[0], rtol=0, atol=1e-12)
+    O.backward(torch.from_numpy(do))
+    g = orc.backward(q, k, v, do, scale=sc, causal=True, tile=64, window=window)
+    for name, t in (("dQ", tq), ("dK", tk), ("dV", tv)):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=0, atol=1e-10)
+    # logsumexp over the tile LSEs is the row LSE (identity I1 under the window)
+    tl = f["tile_lse"][0]
+    m = tl.max(-1, keepdims=True)
+    np.testing.assert_allclose(m[..., 0] + np.log(np.exp(tl - m).sum(-1)), f["lse"][0], rtol=0, atol=1e-12)
