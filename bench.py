@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dit-480p-32k")
     ap.add_argument("--negl", type=float, default=None, help="negl_prob (default: the workload's first)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window of a causal workload (key j visible to query i iff i - window < j <= i)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-rows", type=int, default=20480,
                     help="query rows of head 0 in the oracle's timed sample")
@@ -79,7 +81,15 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x_h0, negl, rows):
+def visible_pairs(rows, window):
+    """(i, j) pairs with j <= i < rows that a sliding window of `window` keys
+    allows (window 0: all of them)."""
+    if window <= 0 or window >= rows:
+        return rows * (rows + 1) / 2
+    return window * (window + 1) / 2 + (rows - window) * float(window)
+
+
+def cpu_baseline(w, x_h0, negl, rows, window=0):
     """fp64 oracle on head 0, query rows [0, rows): forward, mask and backward of
     those rows against all keys.  Rate = dense-equivalent backward FLOP of the
     sample / the oracle's backward seconds."""
@@ -92,7 +102,7 @@ def cpu_baseline(w, x_h0, negl, rows):
     rows = min(rows, n)
     rr = np.arange(rows)
     t0 = time.perf_counter()
-    f = orc.forward(q, k, v, causal=w.causal, rows=rr)
+    f = orc.forward(q, k, v, causal=w.causal, rows=rr, window=window)
     t1 = time.perf_counter()
     # tile weights / selection on the sampled query tiles only
     nt = (rows + TILE - 1) // TILE
@@ -100,15 +110,15 @@ def cpu_baseline(w, x_h0, negl, rows):
     ls = np.zeros((1, 1, n))
     tl[:, :, :rows] = f["tile_lse"]
     ls[:, :, :rows] = f["lse"]
-    a = orc.tile_log_weights(tl, ls, n, w.causal)
-    cand = orc.candidates(n, w.causal).copy()
+    a = orc.tile_log_weights(tl, ls, n, w.causal, window=window)
+    cand = orc.candidates(n, w.causal, window=window).copy()
     cand[nt:] = False                       # only the sampled query tiles
     keep = orc.select_keep(a, cand, negl)
     t2 = time.perf_counter()
-    orc.backward(q, k, v, do, keep=keep, causal=w.causal, q_rows=rr)
+    orc.backward(q, k, v, do, keep=keep, causal=w.causal, q_rows=rr, window=window)
     t3 = time.perf_counter()
-    # dense-equivalent: every (row, key) pair the causal rule allows
-    flops = 10.0 * d * (rows * (rows + 1) / 2 if w.causal else rows * n)
+    # dense-equivalent: every (row, key) pair the causal rule (and window) allows
+    flops = 10.0 * d * (visible_pairs(rows, window) if w.causal else rows * n)
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     return {
         "value": flops / (t3 - t2) / 1e12,
@@ -140,8 +150,12 @@ def main():
     w = ALL[args.workload]
     negl = w.negl_probs[0] if args.negl is None else args.negl
     B, H, Hk, n, d, causal = w.B, w.H, w.Hk, w.n, w.d, w.causal
+    win = args.window
+    if win < 0 or (win and not causal):
+        sys.exit(f"--window {win}: a sliding window needs a causal workload and window >= 0")
     dev = torch.device("cuda:0")
-    log(f"[bench] workload {w.name}: B={B} H={H} H_k={Hk} n={n} d={d} causal={causal} negl_prob={negl}")
+    log(f"[bench] workload {w.name}: B={B} H={H} H_k={Hk} n={n} d={d} causal={causal} window={win} "
+        f"negl_prob={negl}")
     t = time.time()
     x = make_inputs(w)
     log(f"[bench] inputs generated in {time.time() - t:.1f} s")
@@ -172,18 +186,18 @@ def main():
         # outside the timed region: the kept count is read back here)
         return _lib.bwd_workspace(q, k, lists, stored_tiles="auto" if stored else 0)
 
-    o0, lse0, _, _ = bl.fwd(q, k, v, causal=causal, tile_lse=tl, with_residual=True)
-    ws = workspace(bl.mask(tl, lse0, n, causal, negl))
+    o0, lse0, _, _ = bl.fwd(q, k, v, causal=causal, window=win, tile_lse=tl, with_residual=True)
+    ws = workspace(bl.mask(tl, lse0, n, causal, negl, window=win))
     del o0, lse0
 
     def step(rec=None):
-        o, lse, _, olo = bl.fwd(q, k, v, causal=causal, tile_lse=tl, with_residual=True)
+        o, lse, _, olo = bl.fwd(q, k, v, causal=causal, window=win, tile_lse=tl, with_residual=True)
         if rec is not None:
             rec[0].record()
-        m = bl.mask(tl, lse, n, causal, negl, stats=stats)
+        m = bl.mask(tl, lse, n, causal, negl, window=win, stats=stats)
         if rec is not None:
             rec[1].record()
-        bl.bwd(q, k, v, o, do, lse, m, causal=causal, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+        bl.bwd(q, k, v, o, do, lse, m, causal=causal, window=win, workspace=ws, out=(dq, dk, dv), o_lo=olo)
         return o, lse, olo
 
     for _ in range(args.warmup):
@@ -225,16 +239,16 @@ def main():
     sparse_grads = (dq.clone(), dk.clone(), dv.clone()) if (args.grad_check and not args.no_dense) else None
     if not args.no_dense:
         o, lse, olo = step()
-        md = bl.mask(None, lse, n, causal, 0.0)
+        md = bl.mask(None, lse, n, causal, 0.0, window=win)
         del ws
         ws = workspace(md)
         for _ in range(max(1, args.warmup)):
-            bl.bwd(q, k, v, o, do, lse, md, causal=causal, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+            bl.bwd(q, k, v, o, do, lse, md, causal=causal, window=win, workspace=ws, out=(dq, dk, dv), o_lo=olo)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
-            bl.bwd(q, k, v, o, do, lse, md, causal=causal, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+            bl.bwd(q, k, v, o, do, lse, md, causal=causal, window=win, workspace=ws, out=(dq, dk, dv), o_lo=olo)
         e1.record()
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / args.steps
@@ -251,7 +265,7 @@ def main():
                             "rel_l2": float((a_ - r_).norm() / r_.norm())}
         del sparse_grads
 
-    pairs_dense = (n * (n + 1) / 2) if causal else float(n) * n
+    pairs_dense = visible_pairs(n, win) if causal else float(n) * n
     f_dense_bwd = 10.0 * d * B * H * pairs_dense
     f_fwd = 4.0 * d * B * H * pairs_dense
     tile_bwd_flop = 10.0 * TILE * TILE * d
@@ -299,7 +313,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "H_k": Hk, "n": n, "d": d, "causal": causal,
-                   "negl_prob": negl, "tile": TILE},
+                   "window": win, "negl_prob": negl, "tile": TILE},
         "bwd_ms": bwd_ms,
         "fwd_ms": fwd_ms,
         "mask_ms": mask_ms,
@@ -330,7 +344,7 @@ def main():
     if args.cpu_baseline == "on":
         del q, k, v, do, tl, ws, dq, dk, dv
         log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows of head 0 ...")
-        out["cpu_baseline"] = cpu_baseline(w, x_h0, negl, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, x_h0, negl, args.cpu_rows, win)
     print(json.dumps(out), flush=True)
 
 

@@ -46,11 +46,11 @@ def _load():
     lib.backlite_bwd_workspace_bytes_stored.restype = Z
     lib.backlite_bwd_state_offset.argtypes = [I, I, I, I, I]
     lib.backlite_bwd_state_offset.restype = Z
-    lib.backlite_fwd.argtypes = [P, P, P, I, I, I, I, I, F, I, P, P, P, P, P]
+    lib.backlite_fwd.argtypes = [P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P]
     lib.backlite_fwd.restype = I
-    lib.backlite_mask.argtypes = [P, P, I, I, I, I, F, P, P, P, P, P, P, P]
+    lib.backlite_mask.argtypes = [P, P, I, I, I, I, I, F, P, P, P, P, P, P, P]
     lib.backlite_mask.restype = I
-    lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, P, P, P, Z, P]
+    lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, Z, P]
     lib.backlite_bwd.restype = I
     lib.backlite_profile_enable.argtypes = [I]
     lib.backlite_profile_enable.restype = I
@@ -105,9 +105,10 @@ def tile_lse_elems(B, H, n, causal) -> int:
     return int(_load().backlite_tile_lse_elems(B, H, n, 1 if causal else 0))
 
 
-def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_residual=False):
+def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_residual=False, window=0):
     """O, lse_row [B,H,n] fp32, tile_lse (flat fp32 or None); with
-    with_residual=True a fourth value, O_lo (bf16 rounding residual of O)."""
+    with_residual=True a fourth value, O_lo (bf16 rounding residual of O).
+    window > 0 (causal only): key j visible to query i iff i - window < j <= i."""
     B, n, H, d = q.shape
     Hk = k.shape[2]
     _need(q, "q", torch.bfloat16)
@@ -122,14 +123,14 @@ def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_
     if tile_lse is not None:
         _need(tile_lse, "tile_lse", torch.float32, (tile_lse_elems(B, H, n, causal),))
     rc = _load().backlite_fwd(_ptr(q), _ptr(k), _ptr(v), B, n, H, Hk, d, scale, int(causal),
-                              _ptr(o), _ptr(olo), _ptr(lse), _ptr(tile_lse), _stream(q.device))
+                              int(window), _ptr(o), _ptr(olo), _ptr(lse), _ptr(tile_lse), _stream(q.device))
     _check(rc, "backlite_fwd")
     if with_residual:
         return o, lse, tile_lse, olo
     return o, lse, tile_lse
 
 
-def mask(tile_lse, lse, n, causal, negl_prob, stats=None):
+def mask(tile_lse, lse, n, causal, negl_prob, stats=None, window=0):
     """keep [B,H,T,T] u8, qcnt [B,H,T] i32, qidx [B,H,T,T] i16 (uint16 bits), kcnt, kidx."""
     B, H, nn = lse.shape
     assert nn == n
@@ -147,7 +148,7 @@ def mask(tile_lse, lse, n, causal, negl_prob, stats=None):
     }
     if stats is not None:
         _need(stats, "stats", torch.int64, (2,))
-    rc = _load().backlite_mask(_ptr(tile_lse), _ptr(lse), B, H, n, int(causal), float(negl_prob),
+    rc = _load().backlite_mask(_ptr(tile_lse), _ptr(lse), B, H, n, int(causal), int(window), float(negl_prob),
                                _ptr(out["keep"]), _ptr(out["qcnt"]), _ptr(out["qidx"]),
                                _ptr(out["kcnt"]), _ptr(out["kidx"]), _ptr(stats), _stream(dev))
     _check(rc, "backlite_mask")
@@ -200,7 +201,7 @@ def bwd_workspace(q, k, lists, stored_tiles="auto") -> torch.Tensor:
 
 
 def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, out=None, o_lo=None,
-        stored_tiles="auto"):
+        stored_tiles="auto", window=0):
     """G_Q, G_K, G_V (bf16) for the tile set in `lists` (qcnt/qidx/kcnt/kidx).
     o_lo: the forward's residual output (recommended; D then uses O + O_lo).
     workspace: reused if given (a larger one enables the stored-G_S path);
@@ -228,7 +229,7 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
     rc = _load().backlite_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
                               _ptr(lists["qcnt"]), _ptr(lists["qidx"]), _ptr(lists["kcnt"]),
                               _ptr(lists["kidx"]), B, n, H, Hk, d, scale, int(causal),
-                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                              int(window), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                               _stream(q.device))
     _check(rc, "backlite_bwd")
     return dq, dk, dv

@@ -8,7 +8,8 @@ With ``negl_prob > 0`` the forward records the tile statistics in
 ``tile_stats`` (allocated here unless the caller passes one) and hands them to
 the backward, which builds the tile mask and skips the masked tiles; with
 ``negl_prob == 0`` no statistics are recorded and the backward is dense.  A
-``causal`` flag is added (the pages' LLM use is causal).
+``causal`` flag is added (the pages' LLM use is causal), and a ``window`` for
+sliding-window layers (key j visible to query i iff i - window < j <= i).
 
 Every step runs in the HIP library through ``_lib``; torch supplies device
 memory, streams and autograd plumbing only.
@@ -25,13 +26,14 @@ from . import _lib
 
 class _BackLiteFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, scale, causal, negl_prob, tile_stats, stats_out):
+    def forward(ctx, q, k, v, scale, causal, negl_prob, tile_stats, stats_out, window):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         o, lse, tl, olo = _lib.fwd(q, k, v, scale=scale, causal=causal, with_stats=negl_prob > 0,
-                                   tile_lse=tile_stats if negl_prob > 0 else None, with_residual=True)
+                                   tile_lse=tile_stats if negl_prob > 0 else None, with_residual=True,
+                                   window=window)
         ctx.save_for_backward(q, k, v, o, olo, lse)
         ctx.tl = tl
-        ctx.scale, ctx.causal, ctx.negl = scale, causal, negl_prob
+        ctx.scale, ctx.causal, ctx.negl, ctx.window = scale, causal, negl_prob, window
         ctx.stats_out = stats_out
         ctx.mark_non_differentiable(lse)
         return o, lse
@@ -40,11 +42,11 @@ class _BackLiteFn(torch.autograd.Function):
     def backward(ctx, do, _dlse):
         q, k, v, o, olo, lse = ctx.saved_tensors
         n = q.shape[1]
-        lists = _lib.mask(ctx.tl, lse, n, ctx.causal, ctx.negl, stats=ctx.stats_out)
+        lists = _lib.mask(ctx.tl, lse, n, ctx.causal, ctx.negl, stats=ctx.stats_out, window=ctx.window)
         dq, dk, dv = _lib.bwd(q, k, v, o, do.contiguous(), lse, lists, scale=ctx.scale,
-                              causal=ctx.causal, o_lo=olo)
+                              causal=ctx.causal, o_lo=olo, window=ctx.window)
         ctx.tl = None
-        return dq, dk, dv, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None
 
 
 class BackLite(torch.nn.Module):
@@ -54,12 +56,15 @@ class BackLite(torch.nn.Module):
     their cumulative weight stays below this value (0 = dense backward).
     """
 
-    def __init__(self, negl_prob: float = 0.05, causal: bool = False):
+    def __init__(self, negl_prob: float = 0.05, causal: bool = False, window: int = 0):
         super().__init__()
         if not (0.0 <= negl_prob < 1.0) or math.isnan(negl_prob):
             raise ValueError("negl_prob must be in [0, 1)")
+        if window < 0 or (window > 0 and not causal):
+            raise ValueError("window must be >= 0, and a window needs causal=True")
         self.negl_prob = float(negl_prob)
         self.causal = bool(causal)
+        self.window = int(window)
         self.verbose = os.environ.get("BACKLITE_VERBOSE", "0") not in ("", "0")
         self.last_stats = None
 
@@ -72,13 +77,14 @@ class BackLite(torch.nn.Module):
         if self.verbose:
             stats = torch.zeros(2, dtype=torch.int64, device=query.device)
             self.last_stats = stats
-        o, lse = _BackLiteFn.apply(query, key, value, scale, causal, self.negl_prob, tile_stats, stats)
+        o, lse = _BackLiteFn.apply(query, key, value, scale, causal, self.negl_prob, tile_stats, stats,
+                                   self.window if causal else 0)
         if return_softmax_lse:
             return o, lse
         return o
 
     def extra_repr(self) -> str:
-        return f"negl_prob={self.negl_prob}, causal={self.causal}"
+        return f"negl_prob={self.negl_prob}, causal={self.causal}, window={self.window}"
 
 
 def sparsity(stats: torch.Tensor) -> float:

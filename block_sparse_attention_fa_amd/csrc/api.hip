@@ -13,16 +13,16 @@
 
 namespace backlite {
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int n, int H,
-                      int Hk, int d, float scale, int causal, uint16_t* o, uint16_t* olo, float* lse,
-                      float* tlse, hipStream_t st);
+                      int Hk, int d, float scale, int causal, int window, uint16_t* o, uint16_t* olo,
+                      float* lse, float* tlse, hipStream_t st);
 hipError_t launch_mask(const float* tlse, const float* lse, int B, int H, int n, int causal,
-                       double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
+                       int window, double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
                        uint16_t* kidx, int64_t* stats, hipStream_t st);
 hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                       const uint16_t* olo, const uint16_t* dout, const float* lse, const int32_t* qcnt,
                       const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
-                      int H, int Hk, int d, float scale, int causal, uint16_t* dq, uint16_t* dk,
-                      uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
+                      int H, int Hk, int d, float scale, int causal, int window, uint16_t* dq,
+                      uint16_t* dk, uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
                       uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
                       float* dkpart, int dk_chmin, hipStream_t st);
 }  // namespace backlite
@@ -77,6 +77,14 @@ int check_ptr(const void* p, const char* name, bool allow_null = false) {
 int check_scale(float scale) {
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(BACKLITE_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+  return BACKLITE_OK;
+}
+
+// Sliding window: 0 = none; w > 0 lets query i see keys i - w < j <= i, so it
+// needs causal attention.
+int check_window(int causal, int window) {
+  if (window < 0) return fail(BACKLITE_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
+  if (window > 0 && !causal) return fail(BACKLITE_ERR_INVALID_ARG, "a sliding window (%d) requires causal", window);
   return BACKLITE_OK;
 }
 
@@ -158,10 +166,11 @@ size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d) {
 }
 
 int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int n, int H,
-                 int H_k, int d, float scale, int causal, uint16_t* O, uint16_t* O_lo,
+                 int H_k, int d, float scale, int causal, int window, uint16_t* O, uint16_t* O_lo,
                  float* lse_row, float* tile_lse, void* stream) {
   TRY(check_shape(B, n, H, H_k, d));
   TRY(check_scale(scale));
+  TRY(check_window(causal, window));
   TRY(check_ptr(Q, "Q"));
   TRY(check_ptr(K, "K"));
   TRY(check_ptr(V, "V"));
@@ -169,19 +178,20 @@ int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B,
   TRY(check_ptr(O_lo, "O_lo", true));
   TRY(check_ptr(lse_row, "lse_row"));
   TRY(check_ptr(tile_lse, "tile_lse", true));
-  return hip_status(backlite::launch_fwd(Q, K, V, B, n, H, H_k, d, scale, causal ? 1 : 0, O, O_lo,
+  return hip_status(backlite::launch_fwd(Q, K, V, B, n, H, H_k, d, scale, causal ? 1 : 0, window, O, O_lo,
                                          lse_row, tile_lse, (hipStream_t)stream),
                     "backlite_fwd launch");
 }
 
 int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int n, int causal,
-                  float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
+                  int window, float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
                   uint16_t* kidx, int64_t* stats, void* stream) {
   if (B < 1 || n < 1 || H < 1)
     return fail(BACKLITE_ERR_INVALID_ARG, "B, n, H must be >= 1 (got B=%d n=%d H=%d)", B, n, H);
   if (n > kMaxN) return fail(BACKLITE_ERR_UNSUPPORTED, "n = %d exceeds the supported maximum %d", n, kMaxN);
   if ((long long)B * H * ntiles(n) > 0x7fffffffLL)
     return fail(BACKLITE_ERR_INVALID_ARG, "B*H*ceil(n/128) exceeds 2^31");
+  TRY(check_window(causal, window));
   if (!std::isfinite(negl_prob) || negl_prob < 0.f || negl_prob >= 1.f)
     return fail(BACKLITE_ERR_INVALID_ARG, "negl_prob must be finite and in [0, 1) (got %g)",
                 (double)negl_prob);
@@ -195,7 +205,7 @@ int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int
   TRY(check_ptr(kcnt, "kcnt"));
   TRY(check_ptr(kidx, "kidx"));
   TRY(check_ptr(stats, "stats", true));
-  hipError_t e = backlite::launch_mask(tile_lse, lse_row, B, H, n, causal ? 1 : 0, (double)negl_prob,
+  hipError_t e = backlite::launch_mask(tile_lse, lse_row, B, H, n, causal ? 1 : 0, window, (double)negl_prob,
                                        keep, qcnt, qidx, kcnt, kidx, stats, (hipStream_t)stream);
   int r = hip_status(e, "backlite_mask launch");
   if (r == BACKLITE_OK && stats) {
@@ -218,10 +228,11 @@ int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int
 int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
                  const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt, const uint16_t* qidx,
                  const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k, int d,
-                 float scale, int causal, uint16_t* dQ, uint16_t* dK, uint16_t* dV, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 float scale, int causal, int window, uint16_t* dQ, uint16_t* dK, uint16_t* dV,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_shape(B, n, H, H_k, d));
   TRY(check_scale(scale));
+  TRY(check_window(causal, window));
   TRY(check_ptr(Q, "Q"));
   TRY(check_ptr(K, "K"));
   TRY(check_ptr(V, "V"));
@@ -268,7 +279,7 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
     if (v >= 1) chmin = v;
   }
   return hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d,
-                                         scale, causal ? 1 : 0, dQ, dK, dV, (float*)ws,
+                                         scale, causal ? 1 : 0, window, dQ, dK, dV, (float*)ws,
                                          (float*)(ws + delta_bytes(B, H, n)), (float*)(ws + kbar_off), gsinfo,
                                          qbase, kslot, gs, gsl, cap, (int32_t*)(ws + plan_off),
                                          (float*)(ws + part_off), chmin, (hipStream_t)stream),

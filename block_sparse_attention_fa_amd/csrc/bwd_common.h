@@ -39,6 +39,7 @@ struct BwdArgs {
   float* dkpart;       // partial G_K, G_V of split key tiles: [slot][2][128][d] fp32, NK slots
   int dk_chmin;        // smallest chunk length
   int B, n, H, Hk, T;
+  int window;          // sliding window (causal only): key j visible to row i iff i - window < j; 0 = none
   float scale;
   float scale_log2;
 };

@@ -251,6 +251,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     const int q0 = qt * TILE;
     // on the diagonal tile a query row drops keys after it
     const bool diag = CAUSAL && qt == kt;
+    // with a sliding window, a tile holding keys <= some row - window drops them
+    const bool wedge = CAUSAL && a.window != 0 && kt * TILE <= q0 + TILE - 1 - a.window;
     const int lim0 = key - (q0 + 4 * h32);
     // the tile's slot; a slot index past the capacity (lists that disagree)
     // gets empty ranges, so its stores are dropped
@@ -371,9 +373,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
           if constexpr (CAUSAL) {
             // on the diagonal tile a query drops the keys after it: score -inf,
             // so P = 0 there; only that tile takes this branch
-            if (diag) {
+            if (diag || wedge) {
+              // keep query offsets in [lim0, limw) - 32cs: at or after the key, and
+              // before key + window
+              const int limw = wedge ? lim0 + a.window : (1 << 30);
 #pragma unroll
-              for (int r = 0; r < 16; ++r) sv[r] = (8 * (r >> 2) + (r & 3) >= lim0 - cs * 32) ? sv[r] : -INFINITY;
+              for (int r = 0; r < 16; ++r) {
+                const int off = 8 * (r >> 2) + (r & 3);
+                sv[r] = (off >= lim0 - cs * 32 && off < limw - cs * 32) ? sv[r] : -INFINITY;
+              }
             }
           } else if constexpr (GS) {
             // padded keys of a ragged last tile: P = 0, so their G_S and

@@ -148,6 +148,9 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
     // is dropped when it is padding (>= n) or, on the diagonal, after the row
     const bool diag = CAUSAL && (qt == kt);
     const bool edge = key0 + TILE > n;
+    // with a sliding window, tiles reaching down to a row's window edge also drop
+    // the keys <= row - window
+    const bool wedge = CAUSAL && a.window != 0 && key0 <= qt * TILE + TILE - 1 - a.window;
     const int lim0 = (diag ? min(n - 1, qrow) : n - 1) - (key0 + 4 * h32);  // keep offsets <= lim0 - 32kb
     auto fetch = [&](auto kc) -> bf16x8 {
       constexpr int k = decltype(kc)::value, ph = SC::phase_of(k), st = k - SC::start(ph), cb = SC::chunk(ph);
@@ -181,10 +184,14 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
         if constexpr (SC::soft_begin(c4) == k) {
           // masked keys (padding, or after the row on the diagonal) get score
           // -inf, so P = 0 there; only diagonal and ragged tiles take this branch
-          if (diag || edge) {
+          if (diag || edge || wedge) {
+            // and offsets > limw - 32kb
+            const int limw = wedge ? (qrow - a.window) - (key0 + 4 * h32) : -(1 << 30);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              sacc[c4 & 1][r] = (8 * (r >> 2) + (r & 3) <= lim0 - 32 * c4) ? sacc[c4 & 1][r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+              const int off = 8 * (r >> 2) + (r & 3);
+              sacc[c4 & 1][r] = (off <= lim0 - 32 * c4 && off > limw - 32 * c4) ? sacc[c4 & 1][r] : -INFINITY;
+            }
           }
         }
         static_for<0, 16>([&](auto ec) {

@@ -19,6 +19,8 @@
 // plus one exchange between the two lane halves.  O^T += V^T P^T takes P^T
 // straight from the S^T accumulators and V^T from the row-major V tile with the
 // LDS transpose read.
+#include <cfloat>
+
 #include "bl_device.h"
 #include "prof.h"
 
@@ -33,8 +35,16 @@ struct FwdArgs {
   float* lse;
   float* tlse;
   int B, n, H, Hk, T;
+  int window;        // sliding window (causal only): key j visible to row i iff i - window < j; 0 = none
   float scale_log2;  // scale * log2(e)
 };
+
+// First key tile with a key inside the window of some row of query tile qt:
+// the tile holding key qt*128 - window + 1 (0 without a window).
+__device__ __forceinline__ int window_kt_lo(int qt, int window) {
+  const int first = qt * TILE - window + 1;
+  return (window == 0 || first <= 0) ? 0 : first / TILE;
+}
 
 // Stage one K and one V tile of keys key0 .. key0+127 into LDS: asynchronously
 // when the tile is full, else synchronously with zero-filled padding rows.
@@ -96,14 +106,22 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max, in scaled log2 units
+  // running max, in scaled log2 units.  It starts at the lowest finite float, not
+  // -inf: a row that has seen only masked scores so far (possible with a sliding
+  // window) then gets probabilities exp2(-inf) = 0 rather than exp2(-inf + inf).
+  float m_run = -FLT_MAX;
   float l_run = 0.f;
 
   const long kvstride = (long)a.Hk * D;
   const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
   const uint16_t* vbase = a.v + ((long)b * n) * kvstride + (long)g * D;
   const int qt_hi = min(2 * p + 1, T - 1);
-  const int nkt = CAUSAL ? qt_hi + 1 : T;        // key tiles the workgroup visits
+  const int nkt = CAUSAL ? qt_hi + 1 : T;        // key tiles the workgroup visits: kt0 .. nkt-1
+  const int kt0 = CAUSAL ? window_kt_lo(2 * p, a.window) : 0;
+  const int kt_lo = CAUSAL ? window_kt_lo(qt, a.window) : 0;  // this wave's first key tile
+  // rows of this wave's tile see only keys > row - window: tiles that reach below
+  // the last row's window edge are masked per element
+  const int wedge_kt = a.window ? (qt * TILE + TILE - 1 - a.window) : -1;  // mask if key0 <= wedge_kt
   float* tl_row = nullptr;
   if (a.tlse) {
     const long pairs = CAUSAL ? (long)T * (T + 1) / 2 : (long)T * T;
@@ -122,7 +140,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     wait_vmem();
     __syncthreads();  // tile kt is in (Kc, Vc); nobody reads (Kn, Vn) any more
     if (kt + 1 < nkt) stage_kv<D, NT>(Kn, Vn, kbase, vbase, kvstride, dmo, (kt + 1) * TILE, n, tid);
-    if (!active || (CAUSAL && kt > qt)) return;  // wave-uniform
+    if (!active || (CAUSAL && (kt > qt || kt < kt_lo))) return;  // wave-uniform
     const int key0 = kt * TILE;
 
     // S^T for the 4 key blocks of 32
@@ -135,15 +153,19 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < 4; ++kb)  // four independent accumulators back to back
         s[kb] = mfma32(rd_row<D>(Kc, lo, kb, ks), qf[ks], s[kb]);
     // mask padded keys (last tile) and, on the diagonal tile, keys after the row
-    const bool need_mask = (key0 + TILE > n) || (CAUSAL && kt == qt);
+    // (and, with a sliding window, keys at or below row - window)
+    const bool need_mask = (key0 + TILE > n) || (CAUSAL && (kt == qt || key0 <= wedge_kt));
     if (need_mask) {
+      // register r of block kb holds key key0 + 4*h32 + off, off = 32kb + 8(r/4) + r%4;
+      // it is kept iff lo_off < off <= hi_off
+      const int hi_off = (CAUSAL ? min(qrow, n - 1) : n - 1) - (key0 + 4 * h32);
+      const int lo_off = (CAUSAL && a.window) ? (qrow - a.window) - (key0 + 4 * h32) : -(1 << 30);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          const bool bad = (key >= n) || (CAUSAL && key > qrow);
-          s[kb][r] = bad ? -INFINITY : s[kb][r];
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = (off <= hi_off && off > lo_off) ? s[kb][r] : -INFINITY;
         }
     }
     float mt = -INFINITY;
@@ -193,8 +215,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       }
   };
 
-  stage_kv<D, NT>(Ks0, Vs0, kbase, vbase, kvstride, dmo, 0, n, tid);
-  for (int kt = 0; kt < nkt; kt += 2) {
+  stage_kv<D, NT>(Ks0, Vs0, kbase, vbase, kvstride, dmo, kt0 * TILE, n, tid);
+  for (int kt = kt0; kt < nkt; kt += 2) {
     visit(kt, Ks0, Vs0, Ks1, Vs1);
     if (kt + 1 < nkt) visit(kt + 1, Ks1, Vs1, Ks0, Vs0);
   }
@@ -254,9 +276,11 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int n, int H,
-                      int Hk, int d, float scale, int causal, uint16_t* o, uint16_t* olo, float* lse,
-                      float* tlse, hipStream_t st) {
-  FwdArgs a{q, k, v, o, olo, lse, tlse, B, n, H, Hk, (n + TILE - 1) / TILE, scale * LOG2E};
+                      int Hk, int d, float scale, int causal, int window, uint16_t* o, uint16_t* olo,
+                      float* lse, float* tlse, hipStream_t st) {
+  // a window of n keys or more hides nothing beyond the causal rule
+  FwdArgs a{q, k, v, o, olo, lse, tlse, B, n, H, Hk, (n + TILE - 1) / TILE, window < n ? window : 0,
+            scale * LOG2E};
   if (d == 64) return causal ? launch_fwd_t<64, true>(a, st) : launch_fwd_t<64, false>(a, st);
   return causal ? launch_fwd_t<128, true>(a, st) : launch_fwd_t<128, false>(a, st);
 }

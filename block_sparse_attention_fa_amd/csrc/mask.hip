@@ -60,6 +60,7 @@ struct MaskArgs {
   uint16_t* kidx;
   unsigned long long* stats;
   int B, H, n, T, causal;
+  int window;  // sliding window (causal only), 0 = none
   double negl;
 };
 
@@ -75,7 +76,11 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
   const int qt = L % T;
   const int bh = L / T;
   const int tid = threadIdx.x;
-  const int nc = a.causal ? qt + 1 : T;  // candidates are kt = 0 .. nc-1
+  // candidates are kt = kt0 .. kt0+nc-1: causal tiles up to the diagonal and, with
+  // a sliding window, from the tile holding key qt*128 - window + 1
+  const int first = qt * TILE - a.window + 1;
+  const int kt0 = (a.window == 0 || first <= 0) ? 0 : first / TILE;
+  const int nc = a.causal ? qt + 1 - kt0 : T;
   int P2 = 1;
   while (P2 < nc) P2 <<= 1;
 
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
 #pragma unroll
       for (int x = 0; x < UN; ++x) {
         const int kt = kb + x * NG;
-        v[x] = kt < nc ? *reinterpret_cast<const f32x4*>(tl + pair_index(qt, kt, T, a.causal) * TILE + gl * 4)
+        v[x] = kt < nc ? *reinterpret_cast<const f32x4*>(tl + pair_index(qt, kt0 + kt, T, a.causal) * TILE + gl * 4)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
         for (int o = 16; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 32));
         if (gl == 0 && kt < nc) {
           sa[kt] = m;
-          sk[kt] = kt;
+          sk[kt] = kt0 + kt;
         }
       }
     }
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
     const int skip = s_skip;
     for (int r = skip + tid; r < nc; r += MASK_NT) flag[sk[r]] = 1;
   } else {
-    for (int i = tid; i < nc; i += MASK_NT) flag[i] = 1;
+    for (int i = tid; i < nc; i += MASK_NT) flag[kt0 + i] = 1;
   }
   __syncthreads();
 
@@ -215,12 +220,12 @@ __global__ __launch_bounds__(MASK_NT) void mask_transpose_kernel(MaskArgs a) {
   if (tid == 0) a.kcnt[(long)bh * T + kt] = tot;
 }
 
-hipError_t launch_mask(const float* tlse, const float* lse, int B, int H, int n, int causal,
+hipError_t launch_mask(const float* tlse, const float* lse, int B, int H, int n, int causal, int window,
                        double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
                        uint16_t* kidx, int64_t* stats, hipStream_t st) {
   const int T = (n + TILE - 1) / TILE;
   MaskArgs a{tlse, lse, keep, qcnt, qidx, kcnt, kidx, reinterpret_cast<unsigned long long*>(stats),
-             B, H, n, T, causal, negl};
+             B, H, n, T, causal, window < n ? window : 0, negl};
   const int total = B * H * T;
   {
     ProfScope ps(PK_MASK_SELECT, st);

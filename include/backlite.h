@@ -100,6 +100,13 @@ size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d);
  *
  *   Q [B,n,H,d], K, V [B,n,H_k,d] bf16 in; scale > 0 and finite (the usual
  *   choice is 1/sqrt(d)); causal 0/1.
+ *   window >= 0: 0 = none; w > 0 (causal only, else BACKLITE_ERR_INVALID_ARG)
+ *     is a sliding window, key j visible to query i iff i - w < j <= i (the
+ *     blog's Nanochat runs, "Training Nanochat", mix such window layers with
+ *     full causal ones).  tile_lse keeps the causal layout; entries of tile
+ *     pairs wholly outside the window are left unwritten, and rows of a
+ *     candidate tile that see none of its keys get -inf.  backlite_mask and
+ *     backlite_bwd must be given the same window.  w >= n equals causal.
  *   O [B,n,H,d] bf16 out.
  *   O_lo [B,n,H,d] bf16 out, optional (may be NULL): the rounding residual
  *     bf16(O_fp32 - O) of the output, so that O + O_lo carries about 16
@@ -114,13 +121,14 @@ size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d);
  *     written (the negl_prob = 0 dense mode).
  * Requires B, n, H, H_k >= 1, H % H_k == 0, d in {64, 128}. */
 int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
-                 int B, int n, int H, int H_k, int d, float scale, int causal,
+                 int B, int n, int H, int H_k, int d, float scale, int causal, int window,
                  uint16_t* O, uint16_t* O_lo, float* lse_row, float* tile_lse, void* stream);
 
 /* Mask from statistics (README phase 2; "Using Sparsity").
  *
  * For every (b, h, query tile qt) and candidate key tile kt (all kt, or
- * kt <= qt when causal):
+ * kt <= qt when causal; with a sliding window w also kt >= the tile holding
+ * key 128*qt - w + 1, i.e. the tiles with a key inside some row's window):
  *   a(qt,kt) = max over valid rows i of tile qt of (tile_lse[i,kt] - lse_row[i]),
  *              computed in fp64 from the fp32 inputs; the tile weight is
  *              w = exp(a) = the largest p_tile = exp(LSE_tile - LSE_row) of the
@@ -140,7 +148,7 @@ int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
  * negl_prob must be finite and in [0, 1); with negl_prob <= 1 every query tile
  * keeps at least one key tile. */
 int backlite_mask(const float* tile_lse, const float* lse_row,
-                  int B, int H, int n, int causal, float negl_prob,
+                  int B, int H, int n, int causal, int window, float negl_prob,
                   uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
                   int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream);
 
@@ -172,7 +180,7 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
                  const int32_t* qcnt, const uint16_t* qidx,
                  const int32_t* kcnt, const uint16_t* kidx,
-                 int B, int n, int H, int H_k, int d, float scale, int causal,
+                 int B, int n, int H, int H_k, int d, float scale, int causal, int window,
                  uint16_t* dQ, uint16_t* dK, uint16_t* dV,
                  void* workspace, size_t workspace_bytes, void* stream);
 

@@ -59,34 +59,36 @@ FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced
 MIS = ctypes.c_void_p((1 << 20) + 2)     # misaligned
 
 
-def _fwd(L, B=1, n=128, H=2, Hk=2, d=64, scale=0.125, q=FAKE, tl=FAKE):
-    return L.backlite_fwd(q, FAKE, FAKE, B, n, H, Hk, d, scale, 0, FAKE, None, FAKE, tl, None)
+def _fwd(L, B=1, n=128, H=2, Hk=2, d=64, scale=0.125, q=FAKE, tl=FAKE, causal=0, window=0):
+    return L.backlite_fwd(q, FAKE, FAKE, B, n, H, Hk, d, scale, causal, window, FAKE, None, FAKE, tl, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(H=3, Hk=2), -1), (dict(n=0), -1), (dict(B=0), -1), (dict(d=96), -2), (dict(d=256), -2),
     (dict(n=131073), -2), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
     (dict(scale=float("inf")), -1), (dict(q=None), -1), (dict(q=MIS), -1), (dict(tl=MIS), -1),
+    (dict(window=64), -1), (dict(causal=1, window=-1), -1),
 ])
 def test_fwd_validation(L, kw, code):
     assert _fwd(L, **kw) == code
     assert L.backlite_last_error()
 
 
-def _mask(L, negl=0.05, tl=FAKE, keep=FAKE, n=256):
-    return L.backlite_mask(tl, FAKE, 1, 2, n, 0, negl, keep, FAKE, FAKE, FAKE, FAKE, None, None)
+def _mask(L, negl=0.05, tl=FAKE, keep=FAKE, n=256, causal=0, window=0):
+    return L.backlite_mask(tl, FAKE, 1, 2, n, causal, window, negl, keep, FAKE, FAKE, FAKE, FAKE, None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(negl=-0.1), -1), (dict(negl=1.0), -1), (dict(negl=float("nan")), -1),
     (dict(tl=None), -1), (dict(keep=None), -1), (dict(keep=MIS), -1), (dict(n=0), -1),
+    (dict(window=64), -1), (dict(causal=1, window=-5), -1),
 ])
 def test_mask_validation(L, kw, code):
     assert _mask(L, **kw) == code
 
 
 def test_bwd_validation(L):
-    args = [FAKE] * 11 + [1, 256, 4, 2, 128, 0.1, 0, FAKE, FAKE, FAKE]
+    args = [FAKE] * 11 + [1, 256, 4, 2, 128, 0.1, 0, 0, FAKE, FAKE, FAKE]
     # workspace too small / missing
     assert L.backlite_bwd(*args, FAKE, 16, None) == -3
     assert L.backlite_bwd(*args, None, 1 << 20, None) == -3
@@ -96,6 +98,9 @@ def test_bwd_validation(L):
     bad = list(args)
     bad[15] = 80                                  # head_dim
     assert L.backlite_bwd(*bad, FAKE, 1 << 20, None) == -2
+    bad = list(args)
+    bad[18] = 64                                  # a window without causal
+    assert L.backlite_bwd(*bad, FAKE, 1 << 20, None) == -1
 
 
 def test_status_strings(L):
