@@ -85,6 +85,7 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
   while (P2 < nc) P2 <<= 1;
 
   for (int i = tid; i < T; i += MASK_NT) flag[i] = 0;
+  __syncthreads();  // flags are set below by other threads than the one that cleared them (kt0 > 0)
 
   if (a.tlse != nullptr) {
     // ---- 1. log-weights

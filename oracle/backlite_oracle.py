@@ -309,7 +309,7 @@ def cosine(a, ref):
 # sampled evaluation for long sequences
 # ----------------------------------------------------------------------------
 def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), k_tiles=(),
-                       scale=None, tile=TILE, block=TILE, all_rows=True, stats=None):
+                       scale=None, tile=TILE, block=TILE, all_rows=True, stats=None, window=0):
     """The same definitions as forward / mask_from_stats / backward, evaluated
     for one group of query heads sharing a kv head, but only for selected
     outputs, so that long sequences stay tractable on the CPU.
@@ -323,7 +323,8 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
       * the head's contribution to G_K, G_V of the key rows of `k_tiles`
         (requires all_rows), summed over `heads`.
     `stats` (the "stats" entry of a previous call with the same inputs) skips
-    pass 1, e.g. to evaluate several negl_prob values.
+    pass 1, e.g. to evaluate several negl_prob values.  `window` is the sliding
+    window of `candidates` / `forward` (causal only).
     """
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     B, n, H, d = q.shape
@@ -334,7 +335,7 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
     g = kv_head(heads[0], H, Hk)
     assert all(kv_head(h, H, Hk) == g for h in heads)
     T = ntiles(n, tile)
-    cand = candidates(n, causal, tile)
+    cand = candidates(n, causal, tile, window)
     kh, vh = k[0, :, g], v[0, :, g]
     q_tiles, k_tiles = list(q_tiles), list(k_tiles)
     out = {"keep": [], "lse": [], "tile_lse": [], "D": [], "O": [], "dQ": [], "stats": []}
@@ -351,7 +352,7 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
             Oq = {}
             for qt in p1_tiles:
                 r = np.arange(qt * tile, min(n, (qt + 1) * tile))
-                S = _score_block(qh, kh, r, scale, causal)
+                S = _score_block(qh, kh, r, scale, causal, window)
                 L[r] = _row_lse(S)
                 TL[r] = _tile_lse(S, n, tile)
                 O = np.exp(S - L[r][:, None]) @ vh
@@ -365,7 +366,7 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
         out["stats"].append(st)
         # mask of the visited query tiles
         a = tile_log_weights(np.where(np.isfinite(TL), TL, -np.inf)[None, None],
-                             np.where(np.isfinite(L), L, 0.0)[None, None], n, causal, tile)
+                             np.where(np.isfinite(L), L, 0.0)[None, None], n, causal, tile, window)
         cv = cand.copy()
         visited = np.zeros(T, bool)
         visited[list(p1_tiles)] = True
@@ -379,7 +380,7 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
         # pass 2: G_Q rows of q_tiles, G_K/G_V contributions to k_tiles
         for qt in q_tiles:
             r = np.arange(qt * tile, min(n, (qt + 1) * tile))
-            S = _score_block(qh, kh, r, scale, causal)
+            S = _score_block(qh, kh, r, scale, causal, window)
             P = np.exp(S - L[r][:, None])
             M = kp[qt][np.arange(n) // tile][None, :]
             dS = np.where(M, P, 0.0) * (doh[r] @ vh.T - Dr[r][:, None])
@@ -390,7 +391,10 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
                 r = np.arange(qt * tile, min(n, (qt + 1) * tile))
                 Sc = scale * (qh[r] @ kh[c].T)
                 if causal:
-                    Sc = np.where(c[None, :] <= r[:, None], Sc, -np.inf)
+                    ok = c[None, :] <= r[:, None]
+                    if window:
+                        ok &= c[None, :] > r[:, None] - window
+                    Sc = np.where(ok, Sc, -np.inf)
                 Pc = np.exp(Sc - L[r][:, None])
                 dSc = Pc * (doh[r] @ vh[c].T - Dr[r][:, None])
                 dK[kt] += scale * (dSc.T @ qh[r])

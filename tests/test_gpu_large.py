@@ -1,6 +1,6 @@
 """Parity at the full workload sizes, in the launch configuration the bench
 times: the 8k causal GQA LLM, the 32k and 75k video-DiT grids and the 128k
-causal LLM.  The oracle evaluates sampled heads and tiles (rows of sampled
+causal LLM, and the two LLM shapes with sliding windows of 1024 and 2048 keys.  The oracle evaluates sampled heads and tiles (rows of sampled
 query tiles: forward outputs, mask rows, G_Q; columns of sampled key tiles:
 G_K, G_V, where every row's statistics are affordable); properties that hold
 at any size are checked on every head.  GPU only."""
@@ -24,6 +24,10 @@ LARGE = {
     "dit-480p-32k": dict(w=DIT480, heads=[0], q_tiles=[0, 128, 255], k_tiles=[0, 128, 255], all_rows=True),
     "dit-720p-75k": dict(w=DIT720, heads=[0], q_tiles=[0, 295, 590], k_tiles=[0, 295, 590], all_rows=True),
     "llm-128k-causal": dict(w=LLM128K, heads=[0], q_tiles=[0, 511, 1023], k_tiles=[], all_rows=False),
+    "llm-8k-causal-gqa-window1024": dict(w=LLM8K, heads=[0, 1, 2, 3], q_tiles=[0, 8, 31, 63],
+                                         k_tiles=[0, 1, 31, 62, 63], all_rows=True, window=1024),
+    "llm-128k-causal-window2048": dict(w=LLM128K, heads=[0], q_tiles=[0, 15, 16, 511, 1023], k_tiles=[],
+                                       all_rows=False, window=2048),
 }
 
 
@@ -49,12 +53,13 @@ def test_full_size(name):
     B, H, Hk, n, d, causal = w.B, w.H, w.Hk, w.n, w.d, w.causal
     T = (n + TILE - 1) // TILE
     heads, q_tiles, k_tiles = cfg["heads"], cfg["q_tiles"], cfg["k_tiles"]
-    flush_print(f"[case] {name}: B={B} H={H} Hk={Hk} n={n} d={d} causal={causal}")
+    win = cfg.get("window", 0)
+    flush_print(f"[case] {name}: B={B} H={H} Hk={Hk} n={n} d={d} causal={causal} window={win}")
     t0 = time.time()
     x = make_inputs(w)
     dev = torch.device("cuda:0")
     xg = {k_: v_.to(dev) for k_, v_ in x.items()}
-    o, lse, tl, olo = bl.fwd(xg["q"], xg["k"], xg["v"], causal=causal, with_residual=True)
+    o, lse, tl, olo = bl.fwd(xg["q"], xg["k"], xg["v"], causal=causal, with_residual=True, window=win)
     torch.cuda.synchronize()
     flush_print(f"  inputs + forward {time.time() - t0:.1f} s")
 
@@ -65,11 +70,12 @@ def test_full_size(name):
     stats = None
     for negl in w.negl_probs:
         t1 = time.time()
-        m = bl.mask(tl if negl > 0 else None, lse, n, causal, negl)
-        dq, dk, dv = bl.bwd(xg["q"], xg["k"], xg["v"], o, xg["do"], lse, m, causal=causal, o_lo=olo)
+        m = bl.mask(tl if negl > 0 else None, lse, n, causal, negl, window=win)
+        dq, dk, dv = bl.bwd(xg["q"], xg["k"], xg["v"], o, xg["do"], lse, m, causal=causal, o_lo=olo, window=win)
         torch.cuda.synchronize()
         ref = orc.sampled_head_group(sl["q"], sl["k"], sl["v"], sl["do"], hidx, negl, causal,
-                                     q_tiles=q_tiles, k_tiles=k_tiles, all_rows=cfg["all_rows"], stats=stats)
+                                     q_tiles=q_tiles, k_tiles=k_tiles, all_rows=cfg["all_rows"], stats=stats,
+                                     window=win)
         first = stats is None
         stats = ref["stats"]
         keep_all = m["keep"].cpu().numpy().astype(bool)
@@ -78,9 +84,9 @@ def test_full_size(name):
         qcnt, kcnt = m["qcnt"].cpu().numpy(), m["kcnt"].cpu().numpy()
         assert (qcnt == keep_all.sum(axis=3)).all() and (kcnt == keep_all.sum(axis=2)).all()
         assert qcnt.min() >= 1
-        if causal:
-            assert not np.triu(keep_all, 1).any()
-        cand_total = orc.candidates(n, causal).sum() * B * H
+        cand = orc.candidates(n, causal, window=win)
+        assert not (keep_all & ~cand).any()      # causal (and window) non-candidates are never kept
+        cand_total = cand.sum() * B * H
         flush_print(f"  negl={negl}: sparsity {1 - keep_all.sum() / cand_total:.4f}")
         # ---- forward rows (once)
         if first:
@@ -102,7 +108,6 @@ def test_full_size(name):
             assert_close_out("tile_lse", np.concatenate(TLg), np.concatenate(TLr))
         # ---- mask of the sampled heads
         visited = np.arange(T) if cfg["all_rows"] else np.array(sorted(set(q_tiles)))
-        cand = orc.candidates(n, causal)
         nexc = 0
         for hi, h in enumerate(heads):
             kg = keep_all[0, h]
@@ -113,7 +118,7 @@ def test_full_size(name):
             L = ref["lse"][hi]
             TL = ref["tile_lse"][hi]
             a = orc.tile_log_weights(np.where(np.isfinite(TL), TL, -np.inf)[None, None],
-                                     np.where(np.isfinite(L), L, 0.0)[None, None], n, causal)
+                                     np.where(np.isfinite(L), L, 0.0)[None, None], n, causal, window=win)
             bad, exc = excused_mismatches(kg[visited][None, None], kr[visited][None, None],
                                           a[:, :, visited], cand[visited], negl)
             assert not bad, f"head {h}: unexcused mask mismatches {bad[:5]}"

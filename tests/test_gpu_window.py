@@ -193,3 +193,17 @@ def test_window_requires_causal():
     q = torch.zeros((1, 128, 1, 64), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(bl.BackliteError):
         bl.fwd(q, q, q, causal=False, window=64)
+
+
+@pytest.mark.parametrize("n,win", [(131072, 2048), (65536, 300), (20000, 129)])
+def test_window_dense_mask_many_tiles(n, win):
+    """negl_prob = 0 with a window on sequences of many tiles: the keep bitmap is
+    exactly the window's candidate set (the candidate range then starts far from
+    tile 0, so the flags are set by other threads than those that cleared them)."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_fa_amd as bl
+    lse = torch.zeros((1, 2, n), dtype=torch.float32, device="cuda:0")
+    m = bl.mask(None, lse, n, True, 0.0, window=win)
+    T = m["keep"].shape[-1]
+    check_lists(m, np.broadcast_to(orc.candidates(n, True, window=win), (1, 2, T, T)))

@@ -374,16 +374,17 @@ def test_metrics():
 
 
 def test_sampled_head_group_matches_full_oracle():
-    """The sampled evaluation reproduces the full oracle's rows and tiles."""
-    for causal, (H, Hk) in ((False, (2, 1)), (True, (3, 3))):
+    """The sampled evaluation reproduces the full oracle's rows and tiles (also
+    with a sliding window of 90 keys, which cuts 64-wide tiles mid-way)."""
+    for causal, (H, Hk), win in ((False, (2, 1), 0), (True, (3, 3), 0), (True, (2, 1), 90)):
         n, d = 300, 16
         q, k, v, do = _rand((1, n, H, d), 60, 1.5), _rand((1, n, Hk, d), 61, 1.5), _rand((1, n, Hk, d), 62), _rand((1, n, H, d), 63)
         heads = [0, 1] if Hk == 1 else [1]
-        f = orc.forward(q, k, v, causal=causal, tile=64)
-        keep = orc.mask_from_stats(f["tile_lse"], f["lse"], n, causal, 0.2, tile=64)
-        g = orc.backward(q, k, v, do, keep=keep, causal=causal, tile=64, heads=heads)
+        f = orc.forward(q, k, v, causal=causal, tile=64, window=win)
+        keep = orc.mask_from_stats(f["tile_lse"], f["lse"], n, causal, 0.2, tile=64, window=win)
+        g = orc.backward(q, k, v, do, keep=keep, causal=causal, tile=64, heads=heads, window=win)
         sp = orc.sampled_head_group(q, k, v, do, heads, 0.2, causal, q_tiles=[0, 2, 4], k_tiles=[0, 3, 4],
-                                    tile=64, block=64)
+                                    tile=64, block=64, window=win)
         for hi, h in enumerate(heads):
             assert (sp["keep"][hi] == keep[0, h]).all()
             np.testing.assert_allclose(sp["lse"][hi], f["lse"][0, h], atol=1e-12)
