@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dit-480p-32k")
     ap.add_argument("--negl", type=float, default=None, help="negl_prob (default: the workload's first)")
+    ap.add_argument("--stats", choices=["rows", "compact"], default="rows",
+                    help="statistics the mask reads: per-row tile LSEs, or the forward's compact per-pair log-weights")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window of a causal workload (key j visible to query i iff i - window < j <= i)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
@@ -177,6 +179,8 @@ def main():
 
     # every buffer allocated once, outside the timed region
     tl = torch.empty(_lib.tile_lse_elems(B, H, n, causal), dtype=torch.float32, device=dev)
+    compact = args.stats == "compact"
+    tw = torch.empty(_lib.tile_w_elems(B, H, n, causal), dtype=torch.float64, device=dev) if compact else None
     stats = torch.zeros(2, dtype=torch.int64, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     stored = args.gq_path == "stored"
@@ -191,10 +195,13 @@ def main():
     del o0, lse0
 
     def step(rec=None):
-        o, lse, _, olo = bl.fwd(q, k, v, causal=causal, window=win, tile_lse=tl, with_residual=True)
+        o, lse, _, olo = bl.fwd(q, k, v, causal=causal, window=win, tile_lse=tl, with_residual=True, tile_w=tw)
         if rec is not None:
             rec[0].record()
-        m = bl.mask(tl, lse, n, causal, negl, window=win, stats=stats)
+        if compact:
+            m = _lib.mask_compact(tw, B, H, n, causal, negl, stats=stats, window=win)
+        else:
+            m = bl.mask(tl, lse, n, causal, negl, window=win, stats=stats)
         if rec is not None:
             rec[1].record()
         bl.bwd(q, k, v, o, do, lse, m, causal=causal, window=win, workspace=ws, out=(dq, dk, dv), o_lo=olo)
@@ -313,7 +320,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "H_k": Hk, "n": n, "d": d, "causal": causal,
-                   "window": win, "negl_prob": negl, "tile": TILE},
+                   "window": win, "negl_prob": negl, "tile": TILE, "stats": args.stats},
         "bwd_ms": bwd_ms,
         "fwd_ms": fwd_ms,
         "mask_ms": mask_ms,

@@ -46,10 +46,12 @@ def _load():
     lib.backlite_bwd_workspace_bytes_stored.restype = Z
     lib.backlite_bwd_state_offset.argtypes = [I, I, I, I, I]
     lib.backlite_bwd_state_offset.restype = Z
-    lib.backlite_fwd.argtypes = [P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P]
+    lib.backlite_fwd.argtypes = [P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P, P]
     lib.backlite_fwd.restype = I
     lib.backlite_mask.argtypes = [P, P, I, I, I, I, I, F, P, P, P, P, P, P, P]
     lib.backlite_mask.restype = I
+    lib.backlite_mask_compact.argtypes = [P, I, I, I, I, I, F, P, P, P, P, P, P, P]
+    lib.backlite_mask_compact.restype = I
     lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, Z, P]
     lib.backlite_bwd.restype = I
     lib.backlite_profile_enable.argtypes = [I]
@@ -105,10 +107,18 @@ def tile_lse_elems(B, H, n, causal) -> int:
     return int(_load().backlite_tile_lse_elems(B, H, n, 1 if causal else 0))
 
 
-def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_residual=False, window=0):
+def tile_w_elems(B, H, n, causal) -> int:
+    """fp64 entries of the compact statistics: one per (b, h, tile pair)."""
+    return tile_lse_elems(B, H, n, causal) // TILE
+
+
+def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_residual=False, window=0,
+        tile_w=None):
     """O, lse_row [B,H,n] fp32, tile_lse (flat fp32 or None); with
     with_residual=True a fourth value, O_lo (bf16 rounding residual of O).
-    window > 0 (causal only): key j visible to query i iff i - window < j <= i."""
+    window > 0 (causal only): key j visible to query i iff i - window < j <= i.
+    tile_w: optional flat fp64 tensor of tile_w_elems() that receives the
+    compact statistics (one log-weight per tile pair) for mask_compact."""
     B, n, H, d = q.shape
     Hk = k.shape[2]
     _need(q, "q", torch.bfloat16)
@@ -122,8 +132,11 @@ def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_
         tile_lse = torch.empty(tile_lse_elems(B, H, n, causal), dtype=torch.float32, device=q.device)
     if tile_lse is not None:
         _need(tile_lse, "tile_lse", torch.float32, (tile_lse_elems(B, H, n, causal),))
+    if tile_w is not None:
+        _need(tile_w, "tile_w", torch.float64, (tile_w_elems(B, H, n, causal),))
     rc = _load().backlite_fwd(_ptr(q), _ptr(k), _ptr(v), B, n, H, Hk, d, scale, int(causal),
-                              int(window), _ptr(o), _ptr(olo), _ptr(lse), _ptr(tile_lse), _stream(q.device))
+                              int(window), _ptr(o), _ptr(olo), _ptr(lse), _ptr(tile_lse), _ptr(tile_w),
+                              _stream(q.device))
     _check(rc, "backlite_fwd")
     if with_residual:
         return o, lse, tile_lse, olo
@@ -152,6 +165,28 @@ def mask(tile_lse, lse, n, causal, negl_prob, stats=None, window=0):
                                _ptr(out["keep"]), _ptr(out["qcnt"]), _ptr(out["qidx"]),
                                _ptr(out["kcnt"]), _ptr(out["kidx"]), _ptr(stats), _stream(dev))
     _check(rc, "backlite_mask")
+    return out
+
+
+def mask_compact(tile_w, B, H, n, causal, negl_prob, stats=None, window=0, device=None):
+    """As mask(), from the compact statistics fwd(..., tile_w=) wrote."""
+    dev = tile_w.device if tile_w is not None else device
+    if tile_w is not None:
+        _need(tile_w, "tile_w", torch.float64, (tile_w_elems(B, H, n, causal),))
+    T = ntiles(n)
+    out = {
+        "keep": torch.empty((B, H, T, T), dtype=torch.uint8, device=dev),
+        "qcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
+        "qidx": torch.empty((B, H, T, T), dtype=torch.int16, device=dev),
+        "kcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
+        "kidx": torch.empty((B, H, T, T), dtype=torch.int16, device=dev),
+    }
+    if stats is not None:
+        _need(stats, "stats", torch.int64, (2,))
+    rc = _load().backlite_mask_compact(_ptr(tile_w), B, H, n, int(causal), int(window), float(negl_prob),
+                                       _ptr(out["keep"]), _ptr(out["qcnt"]), _ptr(out["qidx"]),
+                                       _ptr(out["kcnt"]), _ptr(out["kidx"]), _ptr(stats), _stream(dev))
+    _check(rc, "backlite_mask_compact")
     return out
 
 

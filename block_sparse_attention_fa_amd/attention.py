@@ -4,9 +4,11 @@ Mirrors the interface the BackLite README describes ("Usage"):
 ``BackLite(negl_prob=0.05)`` is called as ``attn(query, key, value, scale=None,
 return_softmax_lse=False, tile_stats=None)`` on (batch, seq_len, heads,
 head_dim) bf16 tensors, with ``key``/``value`` carrying ``heads_k <= heads``.
-With ``negl_prob > 0`` the forward records the tile statistics in
-``tile_stats`` (allocated here unless the caller passes one) and hands them to
-the backward, which builds the tile mask and skips the masked tiles; with
+With ``negl_prob > 0`` the forward records the per-row tile statistics in
+``tile_stats`` (allocated here unless the caller passes one; it is only staging)
+and reduces them to one log-weight per tile pair, which is all the module keeps
+for the backward (128 rows to one value, 64x fewer bytes).  The backward builds
+the tile mask from those and skips the masked tiles; with
 ``negl_prob == 0`` no statistics are recorded and the backward is dense.  A
 ``causal`` flag is added (the pages' LLM use is causal), and a ``window`` for
 sliding-window layers (key j visible to query i iff i - window < j <= i).
@@ -28,11 +30,15 @@ class _BackLiteFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, scale, causal, negl_prob, tile_stats, stats_out, window):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, lse, tl, olo = _lib.fwd(q, k, v, scale=scale, causal=causal, with_stats=negl_prob > 0,
-                                   tile_lse=tile_stats if negl_prob > 0 else None, with_residual=True,
-                                   window=window)
+        tw = None
+        if negl_prob > 0:
+            B, n, H, _ = q.shape
+            tw = torch.empty(_lib.tile_w_elems(B, H, n, causal), dtype=torch.float64, device=q.device)
+        o, lse, _, olo = _lib.fwd(q, k, v, scale=scale, causal=causal, with_stats=negl_prob > 0,
+                                  tile_lse=tile_stats if negl_prob > 0 else None, with_residual=True,
+                                  window=window, tile_w=tw)
         ctx.save_for_backward(q, k, v, o, olo, lse)
-        ctx.tl = tl
+        ctx.tw = tw
         ctx.scale, ctx.causal, ctx.negl, ctx.window = scale, causal, negl_prob, window
         ctx.stats_out = stats_out
         ctx.mark_non_differentiable(lse)
@@ -42,10 +48,12 @@ class _BackLiteFn(torch.autograd.Function):
     def backward(ctx, do, _dlse):
         q, k, v, o, olo, lse = ctx.saved_tensors
         n = q.shape[1]
-        lists = _lib.mask(ctx.tl, lse, n, ctx.causal, ctx.negl, stats=ctx.stats_out, window=ctx.window)
+        B, _, H, _ = q.shape
+        lists = _lib.mask_compact(ctx.tw, B, H, n, ctx.causal, ctx.negl, stats=ctx.stats_out,
+                                  window=ctx.window, device=q.device)
         dq, dk, dv = _lib.bwd(q, k, v, o, do.contiguous(), lse, lists, scale=ctx.scale,
                               causal=ctx.causal, o_lo=olo, window=ctx.window)
-        ctx.tl = None
+        ctx.tw = None
         return dq, dk, dv, None, None, None, None, None, None
 
 

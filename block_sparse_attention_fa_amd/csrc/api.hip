@@ -14,8 +14,8 @@
 namespace backlite {
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int n, int H,
                       int Hk, int d, float scale, int causal, int window, uint16_t* o, uint16_t* olo,
-                      float* lse, float* tlse, hipStream_t st);
-hipError_t launch_mask(const float* tlse, const float* lse, int B, int H, int n, int causal,
+                      float* lse, float* tlse, double* tw, hipStream_t st);
+hipError_t launch_mask(const float* tlse, const double* tw, const float* lse, int B, int H, int n, int causal,
                        int window, double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
                        uint16_t* kidx, int64_t* stats, hipStream_t st);
 hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
@@ -167,7 +167,7 @@ size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d) {
 
 int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B, int n, int H,
                  int H_k, int d, float scale, int causal, int window, uint16_t* O, uint16_t* O_lo,
-                 float* lse_row, float* tile_lse, void* stream) {
+                 float* lse_row, float* tile_lse, double* tile_w, void* stream) {
   TRY(check_shape(B, n, H, H_k, d));
   TRY(check_scale(scale));
   TRY(check_window(causal, window));
@@ -178,14 +178,22 @@ int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int B,
   TRY(check_ptr(O_lo, "O_lo", true));
   TRY(check_ptr(lse_row, "lse_row"));
   TRY(check_ptr(tile_lse, "tile_lse", true));
+  TRY(check_ptr(tile_w, "tile_w", true));
+  if (tile_w != nullptr && tile_lse == nullptr)
+    return fail(BACKLITE_ERR_INVALID_ARG, "tile_w needs tile_lse (the per-row statistics it is reduced from)");
   return hip_status(backlite::launch_fwd(Q, K, V, B, n, H, H_k, d, scale, causal ? 1 : 0, window, O, O_lo,
-                                         lse_row, tile_lse, (hipStream_t)stream),
+                                         lse_row, tile_lse, tile_w, (hipStream_t)stream),
                     "backlite_fwd launch");
 }
 
-int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int n, int causal,
-                  int window, float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
-                  uint16_t* kidx, int64_t* stats, void* stream) {
+}  // extern "C"
+
+namespace {
+// Shared by backlite_mask (per-row statistics) and backlite_mask_compact
+// (tile_w); exactly one of tile_lse / tile_w is used, or neither with negl 0.
+int mask_impl(bool compact, const float* tile_lse, const double* tile_w, const float* lse_row, int B, int H,
+              int n, int causal, int window, float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
+              int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream) {
   if (B < 1 || n < 1 || H < 1)
     return fail(BACKLITE_ERR_INVALID_ARG, "B, n, H must be >= 1 (got B=%d n=%d H=%d)", B, n, H);
   if (n > kMaxN) return fail(BACKLITE_ERR_UNSUPPORTED, "n = %d exceeds the supported maximum %d", n, kMaxN);
@@ -195,17 +203,18 @@ int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int
   if (!std::isfinite(negl_prob) || negl_prob < 0.f || negl_prob >= 1.f)
     return fail(BACKLITE_ERR_INVALID_ARG, "negl_prob must be finite and in [0, 1) (got %g)",
                 (double)negl_prob);
-  if (tile_lse == nullptr && negl_prob != 0.f)
-    return fail(BACKLITE_ERR_INVALID_ARG, "tile_lse may be NULL only with negl_prob == 0");
+  if (tile_lse == nullptr && tile_w == nullptr && negl_prob != 0.f)
+    return fail(BACKLITE_ERR_INVALID_ARG, "the statistics may be NULL only with negl_prob == 0");
   TRY(check_ptr(tile_lse, "tile_lse", true));
-  TRY(check_ptr(lse_row, "lse_row"));
+  TRY(check_ptr(tile_w, "tile_w", true));
+  if (!compact) TRY(check_ptr(lse_row, "lse_row"));
   TRY(check_ptr(keep, "keep"));
   TRY(check_ptr(qcnt, "qcnt"));
   TRY(check_ptr(qidx, "qidx"));
   TRY(check_ptr(kcnt, "kcnt"));
   TRY(check_ptr(kidx, "kidx"));
   TRY(check_ptr(stats, "stats", true));
-  hipError_t e = backlite::launch_mask(tile_lse, lse_row, B, H, n, causal ? 1 : 0, window, (double)negl_prob,
+  hipError_t e = backlite::launch_mask(tile_w ? nullptr : tile_lse, tile_w, lse_row, B, H, n, causal ? 1 : 0, window, (double)negl_prob,
                                        keep, qcnt, qidx, kcnt, kidx, stats, (hipStream_t)stream);
   int r = hip_status(e, "backlite_mask launch");
   if (r == BACKLITE_OK && stats) {
@@ -223,6 +232,23 @@ int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int
     }
   }
   return r;
+}
+}  // namespace
+
+extern "C" {
+
+int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int n, int causal,
+                  int window, float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
+                  uint16_t* kidx, int64_t* stats, void* stream) {
+  return mask_impl(false, tile_lse, nullptr, lse_row, B, H, n, causal, window, negl_prob, keep, qcnt, qidx, kcnt,
+                   kidx, stats, stream);
+}
+
+int backlite_mask_compact(const double* tile_w, int B, int H, int n, int causal, int window,
+                          float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
+                          uint16_t* kidx, int64_t* stats, void* stream) {
+  return mask_impl(true, nullptr, tile_w, nullptr, B, H, n, causal, window, negl_prob, keep, qcnt, qidx, kcnt,
+                   kidx, stats, stream);
 }
 
 int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,

@@ -34,6 +34,7 @@ struct FwdArgs {
   uint16_t* olo;  // optional: bf16 rounding residual of O
   float* lse;
   float* tlse;
+  double* tw;  // optional compact statistics: per tile pair, max over rows of (tile LSE - row LSE)
   int B, n, H, Hk, T;
   int window;        // sliding window (causal only): key j visible to row i iff i - window < j; 0 = none
   float scale_log2;  // scale * log2(e)
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Vs0[TILE * D];
   __shared__ __attribute__((aligned(16))) bf16 Ks1[TILE * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE * D];
+  __shared__ float lse_s[2 * TILE];  // row LSEs of both query tiles (compact statistics)
 
   const int T = a.T;
   const int T2 = (T + 1) / 2;
@@ -243,7 +245,9 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
         *reinterpret_cast<bf16x4*>(Os + tile_off<D>(lrow, dim >> 3) + (dim & 7)) = w4;
         *reinterpret_cast<bf16x4*>(Rs + tile_off<D>(lrow, dim >> 3) + (dim & 7)) = r4;
       }
-    if (h32 == 0 && qrow < n) a.lse[(long)bh * n + qrow] = (m_run + __log2f(l_run)) * LN2;
+    const float lse_row = (m_run + __log2f(l_run)) * LN2;
+    if (h32 == 0 && qrow < n) a.lse[(long)bh * n + qrow] = lse_row;
+    if (h32 == 0) lse_s[(wave >> 2) * TILE + lrow] = lse_row;
   }
   __syncthreads();
   {
@@ -265,6 +269,36 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       }
     }
   }
+
+  // Compact statistics: for each (query tile, key tile) the workgroup visited,
+  // a = max over the tile's valid rows of (tile LSE - row LSE), in fp64 from the
+  // fp32 values just written (the mask's own arithmetic, so the selection from
+  // a is the same as from the per-row values).  One wave per tile pair: 64
+  // lanes read the pair's 128 row values (512 contiguous bytes, still in L2).
+  if (a.tw) {
+    wait_vmem();      // this wave's tile-LSE stores have completed
+    __syncthreads();  // ... and every other wave's, and lse_s is written
+    const long pairs = CAUSAL ? (long)T * (T + 1) / 2 : (long)T * T;
+    for (int j = 0; j < 2; ++j) {
+      const int qj = 2 * p + j;
+      if (qj >= T) break;
+      const int lo = CAUSAL ? window_kt_lo(qj, a.window) : 0;
+      const int hi = CAUSAL ? qj : T - 1;
+      for (int kt = lo + wave; kt <= hi; kt += NT / 64) {
+        const long pi = (long)bh * pairs + pair_index(qj, kt, T, CAUSAL);
+        const float* src = a.tlse + pi * TILE;
+        double m = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int row = lane + 64 * u;
+          if (qj * TILE + row < n) m = fmax(m, (double)src[row] - (double)lse_s[j * TILE + row]);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+        if (lane == 0) a.tw[pi] = m;
+      }
+    }
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -277,9 +311,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
 
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int B, int n, int H,
                       int Hk, int d, float scale, int causal, int window, uint16_t* o, uint16_t* olo,
-                      float* lse, float* tlse, hipStream_t st) {
+                      float* lse, float* tlse, double* tw, hipStream_t st) {
   // a window of n keys or more hides nothing beyond the causal rule
-  FwdArgs a{q, k, v, o, olo, lse, tlse, B, n, H, Hk, (n + TILE - 1) / TILE, window < n ? window : 0,
+  FwdArgs a{q, k, v, o, olo, lse, tlse, tw, B, n, H, Hk, (n + TILE - 1) / TILE, window < n ? window : 0,
             scale * LOG2E};
   if (d == 64) return causal ? launch_fwd_t<64, true>(a, st) : launch_fwd_t<64, false>(a, st);
   return causal ? launch_fwd_t<128, true>(a, st) : launch_fwd_t<128, false>(a, st);

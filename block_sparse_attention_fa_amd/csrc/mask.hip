@@ -61,6 +61,7 @@ struct MaskArgs {
   unsigned long long* stats;
   int B, H, n, T, causal;
   int window;  // sliding window (causal only), 0 = none
+  const double* tw;  // compact statistics [B, H, pairs] (log-weight per tile pair), or NULL
   double negl;
 };
 
@@ -87,7 +88,16 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
   for (int i = tid; i < T; i += MASK_NT) flag[i] = 0;
   __syncthreads();  // flags are set below by other threads than the one that cleared them (kt0 > 0)
 
-  if (a.tlse != nullptr) {
+  if (a.tw != nullptr || a.tlse != nullptr) {
+   if (a.tw != nullptr) {
+    // ---- 1. log-weights, already reduced over the rows by the forward
+    const long pairs = a.causal ? (long)T * (T + 1) / 2 : (long)T * T;
+    const double* tw = a.tw + (long)bh * pairs;
+    for (int i = tid; i < nc; i += MASK_NT) {
+      sa[i] = tw[pair_index(qt, kt0 + i, T, a.causal)];
+      sk[i] = kt0 + i;
+    }
+   } else {
     // ---- 1. log-weights
     const int grp = tid >> 5, gl = tid & 31;
     const int r0 = qt * TILE + gl * 4;
@@ -122,6 +132,7 @@ __global__ __launch_bounds__(MASK_NT) void mask_select_kernel(MaskArgs a) {
         }
       }
     }
+   }
     for (int i = nc + tid; i < P2; i += MASK_NT) {
       sa[i] = INFINITY;
       sk[i] = 0x7fffffff;
@@ -221,12 +232,12 @@ __global__ __launch_bounds__(MASK_NT) void mask_transpose_kernel(MaskArgs a) {
   if (tid == 0) a.kcnt[(long)bh * T + kt] = tot;
 }
 
-hipError_t launch_mask(const float* tlse, const float* lse, int B, int H, int n, int causal, int window,
-                       double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
+hipError_t launch_mask(const float* tlse, const double* tw, const float* lse, int B, int H, int n, int causal,
+                       int window, double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
                        uint16_t* kidx, int64_t* stats, hipStream_t st) {
   const int T = (n + TILE - 1) / TILE;
   MaskArgs a{tlse, lse, keep, qcnt, qidx, kcnt, kidx, reinterpret_cast<unsigned long long*>(stats),
-             B, H, n, T, causal, window < n ? window : 0, negl};
+             B, H, n, T, causal, window < n ? window : 0, tw, negl};
   const int total = B * H * T;
   {
     ProfScope ps(PK_MASK_SELECT, st);

@@ -119,10 +119,21 @@ size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d);
  *     natural-log LSE of each row over one key tile.  Rows >= n of the last
  *     query tile are written as -inf.  May be NULL: then no statistics are
  *     written (the negl_prob = 0 dense mode).
+ *   tile_w: fp64 out, optional (may be NULL; needs tile_lse): the compact
+ *     statistics, backlite_tile_lse_elems() / 128 doubles in the pair layout
+ *     of tile_lse without the row index.  Entry (qt, kt) is the mask's
+ *     log-weight a(qt, kt) = max over the valid rows i of tile qt of
+ *     (tile_lse[i, kt] - lse_row[i]), formed in fp64 from the fp32 values the
+ *     call writes, exactly as backlite_mask forms it; so backlite_mask_compact
+ *     on tile_w selects the same tiles as backlite_mask on (tile_lse, lse_row).
+ *     tile_lse is then only staging: it may be reused once the call has run,
+ *     and tile_w (128 rows reduced to one value, 64x fewer bytes) is what is
+ *     kept until the backward.  Written for candidate pairs only.
  * Requires B, n, H, H_k >= 1, H % H_k == 0, d in {64, 128}. */
 int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  int B, int n, int H, int H_k, int d, float scale, int causal, int window,
-                 uint16_t* O, uint16_t* O_lo, float* lse_row, float* tile_lse, void* stream);
+                 uint16_t* O, uint16_t* O_lo, float* lse_row, float* tile_lse, double* tile_w,
+                 void* stream);
 
 /* Mask from statistics (README phase 2; "Using Sparsity").
  *
@@ -183,6 +194,17 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  int B, int n, int H, int H_k, int d, float scale, int causal, int window,
                  uint16_t* dQ, uint16_t* dK, uint16_t* dV,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Mask from compact statistics: the tile_w output of backlite_fwd in place of
+ * (tile_lse, lse_row); everything else as backlite_mask, and the same keep
+ * bitmap and lists for the same forward.  tile_w may be NULL only with
+ * negl_prob == 0.  The pages speak of statistics per (query tile, key tile)
+ * ("Using Sparsity") and report the method's small extra peak memory
+ * ("Training Nanochat"); tile_w is that per-pair form, reduced inside the
+ * forward from the per-row values. */
+int backlite_mask_compact(const double* tile_w, int B, int H, int n, int causal, int window,
+                          float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
+                          int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream);
 
 /* Per-kernel timing (opt-in).  While enabled, every kernel the library
  * launches is bracketed by two hipEvents recorded on its launch stream.

@@ -59,8 +59,8 @@ FAKE = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced
 MIS = ctypes.c_void_p((1 << 20) + 2)     # misaligned
 
 
-def _fwd(L, B=1, n=128, H=2, Hk=2, d=64, scale=0.125, q=FAKE, tl=FAKE, causal=0, window=0):
-    return L.backlite_fwd(q, FAKE, FAKE, B, n, H, Hk, d, scale, causal, window, FAKE, None, FAKE, tl, None)
+def _fwd(L, B=1, n=128, H=2, Hk=2, d=64, scale=0.125, q=FAKE, tl=FAKE, causal=0, window=0, tw=None):
+    return L.backlite_fwd(q, FAKE, FAKE, B, n, H, Hk, d, scale, causal, window, FAKE, None, FAKE, tl, tw, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -68,6 +68,7 @@ def _fwd(L, B=1, n=128, H=2, Hk=2, d=64, scale=0.125, q=FAKE, tl=FAKE, causal=0,
     (dict(n=131073), -2), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
     (dict(scale=float("inf")), -1), (dict(q=None), -1), (dict(q=MIS), -1), (dict(tl=MIS), -1),
     (dict(window=64), -1), (dict(causal=1, window=-1), -1),
+    (dict(tl=None, tw=FAKE), -1), (dict(tw=MIS), -1),
 ])
 def test_fwd_validation(L, kw, code):
     assert _fwd(L, **kw) == code
@@ -85,6 +86,17 @@ def _mask(L, negl=0.05, tl=FAKE, keep=FAKE, n=256, causal=0, window=0):
 ])
 def test_mask_validation(L, kw, code):
     assert _mask(L, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tw=None), -1), (dict(negl=1.0), -1), (dict(tw=MIS), -1), (dict(causal=0, window=8), -1),
+    (dict(n=131073), -2),
+])
+def test_mask_compact_validation(L, kw, code):
+    a = dict(tw=FAKE, n=256, causal=1, window=0, negl=0.05)
+    a.update(kw)
+    assert L.backlite_mask_compact(a["tw"], 1, 2, a["n"], a["causal"], a["window"], a["negl"], FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, None, None) == code
 
 
 def test_bwd_validation(L):
