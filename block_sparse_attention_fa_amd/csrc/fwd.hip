@@ -284,18 +284,32 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
       if (qj >= T) break;
       const int lo = CAUSAL ? window_kt_lo(qj, a.window) : 0;
       const int hi = CAUSAL ? qj : T - 1;
-      for (int kt = lo + wave; kt <= hi; kt += NT / 64) {
-        const long pi = (long)bh * pairs + pair_index(qj, kt, T, CAUSAL);
-        const float* src = a.tlse + pi * TILE;
-        double m = -INFINITY;
+      // rows lane and lane + 64 of the query tile; padded rows do not count
+      const bool v0 = qj * TILE + lane < n, v1 = qj * TILE + lane + 64 < n;
+      const double l0 = lse_s[j * TILE + lane], l1 = lse_s[j * TILE + lane + 64];
+      constexpr int UN = 4;  // tile pairs per pass: their loads are issued together (8 spills at d=128)
+      for (int kb = lo + wave; kb <= hi; kb += UN * (NT / 64)) {
+        float x0[UN], x1[UN];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int row = lane + 64 * u;
-          if (qj * TILE + row < n) m = fmax(m, (double)src[row] - (double)lse_s[j * TILE + row]);
+        for (int u = 0; u < UN; ++u) {
+          const int kt = kb + u * (NT / 64);
+          x0[u] = x1[u] = -INFINITY;
+          if (kt <= hi) {
+            const float* src = a.tlse + ((long)bh * pairs + pair_index(qj, kt, T, CAUSAL)) * TILE;
+            x0[u] = src[lane];
+            x1[u] = src[lane + 64];
+          }
         }
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o));
-        if (lane == 0) a.tw[pi] = m;
+        for (int u = 0; u < UN; ++u) {
+          const int kt = kb + u * (NT / 64);
+          double m = -INFINITY;
+          if (v0) m = fmax(m, (double)x0[u] - l0);
+          if (v1) m = fmax(m, (double)x1[u] - l1);
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+          if (lane == 0 && kt <= hi) a.tw[(long)bh * pairs + pair_index(qj, kt, T, CAUSAL)] = m;
+        }
       }
     }
   }
