@@ -40,7 +40,7 @@ def _within(agree, cos_min, rel_max) -> bool:
 
 
 def calibrate_negl_prob(q, k, v, do, causal=False, scale=None, cos_min=0.99, rel_max=0.1, pi_max=0.5,
-                        iters=8) -> dict:
+                        iters=8, window=0) -> dict:
     """The largest negl_prob in [0, pi_max] (to pi_max / 2^iters) whose sparse
     gradients G_Q, G_K, G_V all have cosine > cos_min and rel-L2 < rel_max
     against the dense ones, for this batch (q, k, v [B, n, H(_k), d] bf16 and
@@ -49,22 +49,24 @@ def calibrate_negl_prob(q, k, v, do, causal=False, scale=None, cos_min=0.99, rel
     Returns negl_prob, upper (the smallest value tried outside the targets, or
     pi_max), agreement {name: (cosine, rel-L2)} at negl_prob, sparsity at
     negl_prob, and the probes [(negl_prob, within targets)] in order.
+    window > 0 (causal only): a sliding-window layer; the dense reference has
+    the same window.
     """
     if not (0.0 < pi_max < 1.0) or iters < 0:
         raise ValueError("pi_max must be in (0, 1) and iters >= 0")
     B, n, H, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o, lse, tl, olo = _lib.fwd(q, k, v, scale=scale, causal=causal, with_residual=True)
-    dense_lists = _lib.mask(None, lse, n, causal, 0.0)
+    o, lse, tl, olo = _lib.fwd(q, k, v, scale=scale, causal=causal, with_residual=True, window=window)
+    dense_lists = _lib.mask(None, lse, n, causal, 0.0, window=window)
     ws = _lib.bwd_workspace(q, k, dense_lists)  # slots for the dense tile set when they fit
     ref = tuple(t.clone() for t in _lib.bwd(q, k, v, o, do, lse, dense_lists, scale=scale, causal=causal,
-                                            workspace=ws, o_lo=olo))
+                                            workspace=ws, o_lo=olo, window=window))
     stats = torch.zeros(2, dtype=torch.int64, device=q.device)
 
     def probe(pi):
         stats.zero_()
-        m = _lib.mask(tl, lse, n, causal, pi, stats=stats)
-        g = _lib.bwd(q, k, v, o, do, lse, m, scale=scale, causal=causal, workspace=ws, o_lo=olo)
+        m = _lib.mask(tl, lse, n, causal, pi, stats=stats, window=window)
+        g = _lib.bwd(q, k, v, o, do, lse, m, scale=scale, causal=causal, workspace=ws, o_lo=olo, window=window)
         agree = _agreement(g, ref)
         s = stats.tolist()
         return _within(agree, cos_min, rel_max), agree, 1.0 - s[1] / s[0]

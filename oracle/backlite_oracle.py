@@ -426,7 +426,7 @@ def within_targets(agree, cos_min, rel_max):
 
 
 def calibrate(q, k, v, do, causal=False, scale=None, cos_min=0.99, rel_max=0.1, pi_max=0.5, iters=8,
-              tile=TILE):
+              tile=TILE, window=0):
     """The largest negl_prob in [0, pi_max] (to the bisection's resolution) whose
     masked gradients stay within the targets of the dense (negl_prob = 0) ones.
 
@@ -441,18 +441,19 @@ def calibrate(q, k, v, do, causal=False, scale=None, cos_min=0.99, rel_max=0.1, 
     Returns negl_prob (the last value within the targets), upper (the smallest
     value tried that was not, or pi_max), its keep mask, the gradient agreement
     and the sparsity (1 - kept / candidate tile pairs), plus every probe
-    (negl_prob, within) in order.
+    (negl_prob, within) in order.  `window`: a sliding window (causal only),
+    as in `candidates`; the dense reference then has the same window.
     """
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     B, n, H, _ = q.shape
-    f = forward(q, k, v, scale=scale, causal=causal, tile=tile)
-    dense = backward(q, k, v, do, keep=None, scale=scale, causal=causal, tile=tile)
-    cand = candidates(n, causal, tile)
+    f = forward(q, k, v, scale=scale, causal=causal, tile=tile, window=window)
+    dense = backward(q, k, v, do, keep=None, scale=scale, causal=causal, tile=tile, window=window)
+    cand = candidates(n, causal, tile, window)
     ncand = B * H * int(cand.sum())
 
     def probe(pi):
-        keep = mask_from_stats(f["tile_lse"], f["lse"], n, causal, pi, tile)
-        g = backward(q, k, v, do, keep=keep, scale=scale, causal=causal, tile=tile)
+        keep = mask_from_stats(f["tile_lse"], f["lse"], n, causal, pi, tile, window)
+        g = backward(q, k, v, do, keep=keep, scale=scale, causal=causal, tile=tile, window=window)
         agree = gradient_agreement(g, dense)
         return within_targets(agree, cos_min, rel_max), keep, agree
 

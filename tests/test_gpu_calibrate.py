@@ -19,14 +19,15 @@ def _gpu(w):
     return bl, x, {k: v.to(dev) for k, v in x.items()}
 
 
-@pytest.mark.parametrize("w", [small(640, H=2, Hk=1, d=64, causal=True, kind="gaussian", seed=22),
-                               small(768, H=4, Hk=2, d=128, causal=False, kind="gaussian", seed=23)],
-                         ids=lambda w: w.name)
-def test_calibration_matches_oracle(w):
+@pytest.mark.parametrize("w,win", [(small(640, H=2, Hk=1, d=64, causal=True, kind="gaussian", seed=22), 0),
+                                   (small(768, H=4, Hk=2, d=128, causal=False, kind="gaussian", seed=23), 0),
+                                   (small(900, H=2, Hk=1, d=64, causal=True, kind="gaussian", seed=24), 256)],
+                         ids=["causal-gqa", "noncausal-gqa", "causal-window256"])
+def test_calibration_matches_oracle(w, win):
     bl, x, xg = _gpu(w)
     iters = 6
-    got = bl.calibrate_negl_prob(xg["q"], xg["k"], xg["v"], xg["do"], causal=w.causal, iters=iters)
-    ref = orc.calibrate(x["q"], x["k"], x["v"], x["do"], causal=w.causal, iters=iters)
+    got = bl.calibrate_negl_prob(xg["q"], xg["k"], xg["v"], xg["do"], causal=w.causal, iters=iters, window=win)
+    ref = orc.calibrate(x["q"], x["k"], x["v"], x["do"], causal=w.causal, iters=iters, window=win)
     flush_print(f"  gpu {got['negl_prob']} (sparsity {got['sparsity']:.3f}) oracle {ref['negl_prob']} "
                 f"(sparsity {ref['sparsity']:.3f}); probes {got['probes']} / {ref['probes']}")
     # the probes decide identically unless an oracle metric sits within the GPU's

@@ -446,6 +446,38 @@ def test_calibrate_trivial_targets():
     assert [p for p, _ in r["probes"]] == [0.5, 0.25, 0.125, 0.0625]
 
 
+def test_calibrate_with_window():
+    """With a sliding window the bisection uses the windowed forward, mask and
+    dense backward: negl_prob and `upper` re-checked with those functions, the
+    kept tiles inside the window's candidates, and the sparsity counted over
+    them."""
+    w = small(900, H=2, Hk=1, d=64, causal=True, kind="gaussian", seed=24)
+    x = make_inputs(w)
+    win, iters = 256, 6
+    r = orc.calibrate(x["q"], x["k"], x["v"], x["do"], causal=True, iters=iters, window=win)
+    f = orc.forward(x["q"], x["k"], x["v"], causal=True, window=win)
+    dense = orc.backward(x["q"], x["k"], x["v"], x["do"], causal=True, window=win)
+
+    def within(pi):
+        keep = orc.mask_from_stats(f["tile_lse"], f["lse"], w.n, True, pi, window=win)
+        g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=True, window=win)
+        ok = True
+        for nm in ("dQ", "dK", "dV"):
+            a, b = g[nm].ravel(), dense[nm].ravel()
+            cos = float(a @ b / np.linalg.norm(a) / np.linalg.norm(b))
+            rel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+            ok &= cos > 0.99 and rel < 0.1
+        return keep, ok
+
+    keep, ok = within(r["negl_prob"])
+    assert ok and (keep == r["keep"]).all()
+    if r["upper"] > r["negl_prob"]:
+        assert not within(r["upper"])[1]
+    cand = orc.candidates(w.n, True, window=win)
+    assert not (r["keep"] & ~cand[None, None]).any()
+    assert r["sparsity"] == pytest.approx(1.0 - r["keep"].sum() / (w.B * w.H * cand.sum()), abs=1e-15)
+
+
 def test_calibrate_brackets_the_largest_value_within_targets():
     """On unstructured inputs the bisection ends with negl_prob within the
     targets and `upper` (pi_max / 2^iters above it) outside them, each checked
