@@ -104,3 +104,29 @@ def test_compact_mask_full_size(w, win):
                 assert torch.equal(m1[key], m2[key]), key
         flush_print(f"  negl={negl}: kept {int(m1['qcnt'].sum())} tiles, identical")
     flush_print(f"  tile_lse {tl.numel() * 4 / 1e9:.3f} GB, tile_w {tw.numel() * 8 / 1e9:.4f} GB")
+
+
+@pytest.mark.parametrize("causal,win", [(False, 0), (True, 0), (True, 300)], ids=["noncausal", "causal", "window300"])
+def test_module_compact_path_equals_per_row_path(causal, win):
+    """The autograd module (which keeps only the compact statistics) gives the
+    same gradients, bit for bit, as fwd -> mask on the per-row statistics ->
+    bwd through the C ABI."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_fa_amd as bl
+    w = small(1000, H=4, Hk=2, d=128, causal=causal, kind="blocks", seed=31)
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[nm].to(dev) for nm in ("q", "k", "v", "do"))
+    qg, kg, vg = (t.clone().requires_grad_(True) for t in (q, k, v))
+    attn = bl.BackLite(negl_prob=0.05, causal=causal, window=win)
+    attn(qg, kg, vg).backward(do)
+    o, lse, tl, olo = bl.fwd(q, k, v, causal=causal, with_residual=True, window=win)
+    m = bl.mask(tl, lse, w.n, causal, 0.05, window=win)
+    ws = bl._lib.bwd_workspace(q, k, m)
+    dq, dk, dv = bl.bwd(q, k, v, o, do, lse, m, causal=causal, o_lo=olo, window=win, workspace=ws)
+    kept = int(m["qcnt"].sum())
+    flush_print(f"  kept {kept} tiles")
+    assert kept < m["keep"].numel()
+    for name, a, b in (("dQ", qg.grad, dq), ("dK", kg.grad, dk), ("dV", vg.grad, dv)):
+        assert torch.equal(a, b), name
