@@ -54,7 +54,10 @@ def parse():
     ap.add_argument("--grad-check", action="store_true",
                     help="report cosine and rel-L2 of the sparse gradients against the dense (negl_prob = 0) ones")
     ap.add_argument("--gq-path", choices=["stored", "recompute"], default="stored",
-                    help="G_Q from stored bf16 G_S tiles (workspace slots for every kept tile) or by recomputation")
+                    help="G_Q from stored bf16 G_S tiles (workspace slots) or by recomputation")
+    ap.add_argument("--gs-budget-gb", type=float, default=None,
+                    help="device memory for G_S slots (default: a slot for every kept tile when they fit); "
+                         "query tiles past the budget recompute G_Q")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for memory counters)")
     return ap.parse_args()
@@ -186,9 +189,17 @@ def main():
     stored = args.gq_path == "stored"
 
     def workspace(lists):
-        # slots for every kept tile when they fit in device memory (sized once,
-        # outside the timed region: the kept count is read back here)
-        return _lib.bwd_workspace(q, k, lists, stored_tiles="auto" if stored else 0)
+        # G_S slots: a budget, or one slot per kept tile when they fit in free
+        # device memory (counted once here, outside the timed region)
+        if not stored:
+            return _lib.bwd_workspace(q, k, lists, stored_tiles=0)
+        if args.gs_budget_gb is not None:
+            return _lib.bwd_workspace(q, k, lists, stored_tiles="auto", causal=causal, window=win,
+                                      gs_budget_bytes=int(args.gs_budget_gb * 1e9))
+        tiles = int(lists["qcnt"].sum().item())
+        free, _ = torch.cuda.mem_get_info(dev)
+        tiles = min(tiles, max(0, (free - (4 << 30)) // _lib.SLOT_BYTES))
+        return _lib.bwd_workspace(q, k, lists, stored_tiles=tiles)
 
     o0, lse0, _, _ = bl.fwd(q, k, v, causal=causal, window=win, tile_lse=tl, with_residual=True)
     ws = workspace(bl.mask(tl, lse0, n, causal, negl, window=win))
@@ -236,9 +247,11 @@ def main():
     st = stats.cpu().tolist()
     cand, kept = st[0] / args.steps, st[1] / args.steps
     sparsity = 1.0 - kept / cand if cand else 0.0
-    gq_stored = _lib.bwd_stored_taken(ws, B, H, Hk, n, d)[0] if ws.numel() > _lib.bwd_workspace_bytes(
-        B, H, Hk, n, d) else False
+    has_slots = ws.numel() > _lib.bwd_workspace_bytes(B, H, Hk, n, d)
+    gq_state = _lib.bwd_state(ws, B, H, Hk, n, d) if has_slots else (False, int(kept), 0)
+    gq_stored = gq_state[0]
     ws_bytes = ws.numel()
+    peak_mem = torch.cuda.max_memory_allocated(dev)
 
     # the same library's dense backward (negl_prob = 0: every candidate tile)
     dense_ms = None
@@ -327,7 +340,9 @@ def main():
         "dense_bwd_ms": dense_ms,
         "bwd_speedup_vs_dense": (dense_ms / bwd_ms) if dense_ms else None,
         "dense_vs_sparse_grads": grad_cmp,
-        "gq_path": "stored" if gq_stored else "recompute",
+        "gq_path": "stored" if gq_stored else ("partly stored" if gq_state[2] else "recompute"),
+        "gq_stored_tiles": gq_state[2],
+        "peak_mem_gb": peak_mem / 1e9,
         "dense_gq_path": None if dense_stored is None else ("stored" if dense_stored else "recompute"),
         "bwd_workspace_gb": ws_bytes / 1e9,
         "sparsity": sparsity,

@@ -61,6 +61,12 @@ def _load():
     lib.backlite_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64)]
     lib.backlite_profile_read.restype = I
+    lib.backlite_check_lists.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_char_p, Z]
+    lib.backlite_check_lists.restype = I
+    lib.backlite_similarity_elems.argtypes = []
+    lib.backlite_similarity_elems.restype = Z
+    lib.backlite_similarity_sums.argtypes = [P, P, ctypes.c_int64, P, P]
+    lib.backlite_similarity_sums.restype = I
     lib.backlite_status_string.argtypes = [I]
     lib.backlite_status_string.restype = ctypes.c_char_p
     lib.backlite_last_error.argtypes = []
@@ -203,34 +209,77 @@ def bwd_state_offset(B, H, Hk, n, d) -> int:
 
 
 def bwd_stored_taken(workspace, B, H, Hk, n, d) -> tuple:
-    """(stored path taken, kept tile pairs) from the state words of a workspace
-    the last backward used (synchronises with the device)."""
+    """(every kept tile had a G_S slot, kept tile pairs) from the state words of
+    a workspace the last backward used (synchronises with the device)."""
+    w = bwd_state(workspace, B, H, Hk, n, d)
+    return w[0], w[1]
+
+
+def bwd_state(workspace, B, H, Hk, n, d) -> tuple:
+    """(all kept tiles had a slot, kept tile pairs, kept tiles with a slot) from
+    the state words of a workspace the last backward used (synchronises)."""
     off = bwd_state_offset(B, H, Hk, n, d)
-    w = workspace[off:off + 8].view(torch.int32).tolist()
-    return bool(w[0]), int(w[1])
+    w = workspace[off:off + 12].view(torch.int32).tolist()
+    return bool(w[0]), int(w[1]), int(w[2])
 
 
-# Device memory left free when sizing a stored-G_S workspace automatically.
-STORED_MARGIN_BYTES = 4 << 30
+def check_lists(qcnt, qidx, kcnt, kidx, B, H, n, causal, window=0, q_tile=TILE):
+    """Validate work lists held in host memory (numpy int32 / uint16 arrays)
+    with backlite_check_lists; raises BackliteError with the first violation."""
+    import numpy as np
+    arrs = [np.ascontiguousarray(qcnt, dtype=np.int32), np.ascontiguousarray(qidx).view(np.uint16),
+            np.ascontiguousarray(kcnt, dtype=np.int32), np.ascontiguousarray(kidx).view(np.uint16)]
+    msg = ctypes.create_string_buffer(400)
+    rc = _load().backlite_check_lists(*[a.ctypes.data_as(ctypes.c_void_p) for a in arrs], B, H, n, int(causal),
+                                      int(window), int(q_tile), msg, 400)
+    if rc != 0:
+        raise BackliteError(f"backlite_check_lists: {msg.value.decode()}")
 
 
-def bwd_workspace(q, k, lists, stored_tiles="auto") -> torch.Tensor:
-    """A backward workspace.  stored_tiles: "auto" sizes the stored-G_S slots
-    for the tiles the lists keep (their count is read back from the device)
-    when that fits in free device memory, else no slots; an int gives that many
-    slots; 0 gives the base workspace (G_Q recomputes P and G_S)."""
+def candidate_pairs(n: int, causal: bool, window: int = 0) -> int:
+    """Candidate (query tile, key tile) pairs of one (batch, head): all T*T, or
+    the causal triangle, or its band under a sliding window (integer bookkeeping
+    for workspace sizes)."""
+    T = ntiles(n)
+    if not causal:
+        return T * T
+    w = window if 0 < window < n else 0
+    tot = 0
+    for qt in range(T):
+        first = qt * TILE - w + 1
+        lo = first // TILE if (w and first > 0) else 0
+        tot += qt - lo + 1
+    return tot
+
+
+# Default share of device memory given to stored-G_S slots when the caller
+# sets no budget.
+GS_BUDGET_FRACTION = 1 / 8
+SLOT_BYTES = TILE * TILE * 2 + 4 * TILE * 4
+
+
+def gs_slots_for_budget(B, H, n, causal, window, budget_bytes, device) -> int:
+    """Slots for a G_S budget in bytes (None: GS_BUDGET_FRACTION of the device's
+    memory), never more than the candidate pairs: no device readback."""
+    if budget_bytes is None:
+        budget_bytes = int(torch.cuda.get_device_properties(device).total_memory * GS_BUDGET_FRACTION)
+    return max(0, min(B * H * candidate_pairs(n, causal, window), int(budget_bytes) // SLOT_BYTES))
+
+
+def bwd_workspace(q, k, lists=None, stored_tiles="auto", causal=False, window=0, gs_budget_bytes=None) -> torch.Tensor:
+    """A backward workspace.  stored_tiles: "auto" gives G_S slots for every
+    candidate tile pair, capped by gs_budget_bytes (default: an eighth of the
+    device's memory), without reading anything back from the device; an int
+    gives that many slots; 0 gives the base workspace (G_Q recomputes P and
+    G_S).  When the kept tiles outnumber the slots, the query tiles past the
+    slots recompute their G_Q (decided on the device)."""
     B, n, H, d = q.shape
     Hk = k.shape[2]
     base = bwd_workspace_bytes(B, H, Hk, n, d)
-    tiles = 0
     if stored_tiles == "auto":
-        tiles = int(lists["qcnt"].sum().item())
-        need = bwd_workspace_bytes_stored(B, H, Hk, n, d, tiles)
-        free, _ = torch.cuda.mem_get_info(q.device)
-        if need - base > free - STORED_MARGIN_BYTES:
-            tiles = 0
-    elif stored_tiles:
-        tiles = int(stored_tiles)
+        tiles = gs_slots_for_budget(B, H, n, causal, window, gs_budget_bytes, q.device)
+    else:
+        tiles = int(stored_tiles or 0)
     size = bwd_workspace_bytes_stored(B, H, Hk, n, d, tiles) if tiles > 0 else base
     return torch.empty(size, dtype=torch.uint8, device=q.device)
 
@@ -240,7 +289,8 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
     """G_Q, G_K, G_V (bf16) for the tile set in `lists` (qcnt/qidx/kcnt/kidx).
     o_lo: the forward's residual output (recommended; D then uses O + O_lo).
     workspace: reused if given (a larger one enables the stored-G_S path);
-    otherwise one is allocated by bwd_workspace(stored_tiles=...)."""
+    otherwise one is allocated by bwd_workspace(stored_tiles=...), which reads
+    nothing back from the device."""
     B, n, H, d = q.shape
     Hk = k.shape[2]
     for name, t, shp in (("q", q, (B, n, H, d)), ("k", k, (B, n, Hk, d)), ("v", v, (B, n, Hk, d)),
@@ -260,7 +310,7 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
     else:
         dq, dk, dv = out
     if workspace is None:
-        workspace = bwd_workspace(q, k, lists, stored_tiles)
+        workspace = bwd_workspace(q, k, lists, stored_tiles, causal=causal, window=window)
     rc = _load().backlite_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
                               _ptr(lists["qcnt"]), _ptr(lists["qidx"]), _ptr(lists["kcnt"]),
                               _ptr(lists["kidx"]), B, n, H, Hk, d, scale, int(causal),
@@ -268,6 +318,19 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
                               _stream(q.device))
     _check(rc, "backlite_bwd")
     return dq, dk, dv
+
+
+def similarity_sums(a, b, out=None):
+    """Device fp64 tensor whose first 4 entries become (sum a*b, sum a*a,
+    sum b*b, sum (a-b)^2) of two bf16 tensors of equal size (the rest is the
+    kernel's scratch)."""
+    _need(a, "a", torch.bfloat16)
+    _need(b, "b", torch.bfloat16, tuple(a.shape))
+    if out is None:
+        out = torch.empty(int(_load().backlite_similarity_elems()), dtype=torch.float64, device=a.device)
+    _check(_load().backlite_similarity_sums(_ptr(a), _ptr(b), a.numel(), _ptr(out), _stream(a.device)),
+           "backlite_similarity_sums")
+    return out
 
 
 PROFILE_KERNELS = ("fwd", "mask_select", "mask_transpose", "delta", "kmean", "dk_plan", "dkdv", "dk_reduce", "dq",

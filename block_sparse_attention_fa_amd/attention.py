@@ -28,7 +28,7 @@ from . import _lib
 
 class _BackLiteFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, scale, causal, negl_prob, tile_stats, stats_out, window):
+    def forward(ctx, q, k, v, scale, causal, negl_prob, tile_stats, stats_out, window, ws_cache):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         tw = None
         if negl_prob > 0:
@@ -37,24 +37,50 @@ class _BackLiteFn(torch.autograd.Function):
         o, lse, _, olo = _lib.fwd(q, k, v, scale=scale, causal=causal, with_stats=negl_prob > 0,
                                   tile_lse=tile_stats if negl_prob > 0 else None, with_residual=True,
                                   window=window, tile_w=tw)
-        ctx.save_for_backward(q, k, v, o, olo, lse)
-        ctx.tw = tw
+        # the compact statistics live as long as the graph (autograd frees them
+        # with it), so a second backward through the same graph finds them too
+        ctx.save_for_backward(q, k, v, o, olo, lse, tw)
         ctx.scale, ctx.causal, ctx.negl, ctx.window = scale, causal, negl_prob, window
         ctx.stats_out = stats_out
+        ctx.ws_cache = ws_cache
         ctx.mark_non_differentiable(lse)
         return o, lse
 
     @staticmethod
     def backward(ctx, do, _dlse):
-        q, k, v, o, olo, lse = ctx.saved_tensors
+        q, k, v, o, olo, lse, tw = ctx.saved_tensors
         n = q.shape[1]
         B, _, H, _ = q.shape
-        lists = _lib.mask_compact(ctx.tw, B, H, n, ctx.causal, ctx.negl, stats=ctx.stats_out,
+        lists = _lib.mask_compact(tw, B, H, n, ctx.causal, ctx.negl, stats=ctx.stats_out,
                                   window=ctx.window, device=q.device)
+        ws = ctx.ws_cache.get(q, k, ctx.causal, ctx.window) if ctx.ws_cache is not None else None
         dq, dk, dv = _lib.bwd(q, k, v, o, do.contiguous(), lse, lists, scale=ctx.scale,
-                              causal=ctx.causal, o_lo=olo, window=ctx.window)
-        ctx.tw = None
-        return dq, dk, dv, None, None, None, None, None, None
+                              causal=ctx.causal, o_lo=olo, window=ctx.window, workspace=ws)
+        return dq, dk, dv, None, None, None, None, None, None, None
+
+
+class _WorkspaceCache:
+    """One backward workspace per (device, shape), allocated on first use and
+    reused by every later backward of that shape: no allocation and no device
+    readback inside the backward.  Its G_S slots are sized from the candidate
+    tile pairs, capped by a byte budget (None: an eighth of the device's
+    memory); query tiles whose kept tiles do not all fit recompute G_Q."""
+
+    def __init__(self, gs_budget_bytes=None):
+        self.gs_budget_bytes = gs_budget_bytes
+        self._ws = {}
+
+    def get(self, q, k, causal, window):
+        key = (q.device, tuple(q.shape), k.shape[2], bool(causal), int(window))
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = _lib.bwd_workspace(q, k, None, "auto", causal=causal, window=window,
+                                    gs_budget_bytes=self.gs_budget_bytes)
+            self._ws[key] = ws
+        return ws
+
+    def clear(self):
+        self._ws.clear()
 
 
 class BackLite(torch.nn.Module):
@@ -62,9 +88,14 @@ class BackLite(torch.nn.Module):
 
     negl_prob: tiles are skipped in the backward, smallest weight first, while
     their cumulative weight stays below this value (0 = dense backward).
+    gs_budget_bytes: device memory for the stored-G_S slots of the backward
+    workspace (None: an eighth of the device's memory, at most one slot per
+    candidate tile pair).  The workspace is allocated on the first backward of
+    a shape and reused.
     """
 
-    def __init__(self, negl_prob: float = 0.05, causal: bool = False, window: int = 0):
+    def __init__(self, negl_prob: float = 0.05, causal: bool = False, window: int = 0,
+                 gs_budget_bytes: int | None = None):
         super().__init__()
         if not (0.0 <= negl_prob < 1.0) or math.isnan(negl_prob):
             raise ValueError("negl_prob must be in [0, 1)")
@@ -75,6 +106,8 @@ class BackLite(torch.nn.Module):
         self.window = int(window)
         self.verbose = os.environ.get("BACKLITE_VERBOSE", "0") not in ("", "0")
         self.last_stats = None
+        # the backward workspace, kept across steps (see _WorkspaceCache)
+        self.workspaces = _WorkspaceCache(gs_budget_bytes)
 
     def forward(self, query, key, value, scale=None, return_softmax_lse=False, tile_stats=None,
                 causal=None):
@@ -86,7 +119,7 @@ class BackLite(torch.nn.Module):
             stats = torch.zeros(2, dtype=torch.int64, device=query.device)
             self.last_stats = stats
         o, lse = _BackLiteFn.apply(query, key, value, scale, causal, self.negl_prob, tile_stats, stats,
-                                   self.window if causal else 0)
+                                   self.window if causal else 0, self.workspaces)
         if return_softmax_lse:
             return o, lse
         return o

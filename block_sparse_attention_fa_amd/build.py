@@ -2,8 +2,9 @@
 
     python -m block_sparse_attention_fa_amd.build
 
-Every .hip file under csrc/ is compiled to an object under _build/ (in
-parallel), then linked into block_sparse_attention_fa_amd/libbacklite.so.
+Every .hip file under csrc/ is compiled by hipcc for gfx950, and every .cpp
+file (host-only C++) by the host compiler, to an object under _build/ (in
+parallel); the objects are linked into block_sparse_attention_fa_amd/libbacklite.so.
 """
 from __future__ import annotations
 
@@ -50,14 +51,34 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", f"-I{os.path.join(ROOT, 'include')}"]
+
+
+def host_cxx() -> str:
+    for c in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if c and shutil.which(c):
+            return c
+    raise RuntimeError("no host C++ compiler found")
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile and link.  incremental=True (development only) skips sources
+    whose object is newer than the source and every header."""
     cc = hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    objs = [os.path.join(BUILD, f[:-4] + ".o") for f in srcs]
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+    objs = [os.path.join(BUILD, os.path.splitext(f)[0] + ".o") for f in srcs]
+    hdr_time = max([os.path.getmtime(os.path.join(d, f)) for d in (CSRC, os.path.join(ROOT, "include"))
+                    for f in os.listdir(d) if f.endswith(".h")] or [0.0])
 
     def comp(i):
-        return _run([cc, *FLAGS, *FILE_FLAGS.get(srcs[i], []), "-c", os.path.join(CSRC, srcs[i]), "-o", objs[i]])
+        if incremental and os.path.exists(objs[i]) and os.path.getmtime(objs[i]) > max(
+                hdr_time, os.path.getmtime(os.path.join(CSRC, srcs[i]))):
+            return ""
+        src = os.path.join(CSRC, srcs[i])
+        if srcs[i].endswith(".cpp"):
+            return _run([host_cxx(), *HOST_FLAGS, "-c", src, "-o", objs[i]])
+        return _run([cc, *FLAGS, *FILE_FLAGS.get(srcs[i], []), "-c", src, "-o", objs[i]])
 
     jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with ThreadPoolExecutor(jobs) as ex:
@@ -73,5 +94,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))
     sys.exit(0)

@@ -10,8 +10,10 @@ grows: pi_max is tried first, then `iters` halvings of [lo, hi] with lo always
 within the targets (lo = 0 is the dense backward).
 
 Every forward, mask and backward runs in the library's kernels; the dense
-reference is the same library at negl_prob = 0.  The similarity numbers are
-reductions over the gradients in fp32 on the GPU.
+reference is the same library at negl_prob = 0.  The similarity numbers come
+from the library's reduction kernel (backlite_similarity_sums: fp64 sums of
+a*b, a*a, b*b and (a-b)^2); only the final square roots and divisions of those
+four scalars are taken on the host.
 """
 from __future__ import annotations
 
@@ -25,12 +27,13 @@ GRADS = ("dQ", "dK", "dV")
 
 
 def _agreement(g, ref) -> dict:
+    """{name: (cosine, rel-L2)} of each gradient against the reference."""
+    sums = [_lib.similarity_sums(a, r) for a, r in zip(g, ref)]
     out = {}
-    for nm, a, r in zip(GRADS, g, ref):
-        a32, r32 = a.float().flatten(), r.float().flatten()
-        na, nr = a32.norm(), r32.norm()
-        cos = 1.0 if float(na) == 0.0 and float(nr) == 0.0 else float(torch.dot(a32, r32) / (na * nr))
-        rel = float((a32 - r32).norm() / (nr if float(nr) > 0 else 1.0))
+    for nm, s in zip(GRADS, sums):
+        ab, aa, bb, dd = s[:4].tolist()
+        cos = 1.0 if aa == 0.0 and bb == 0.0 else ab / math.sqrt(aa * bb) if aa > 0 and bb > 0 else 0.0
+        rel = math.sqrt(dd / bb) if bb > 0 else math.sqrt(dd)
         out[nm] = (cos, rel)
     return out
 
@@ -58,7 +61,7 @@ def calibrate_negl_prob(q, k, v, do, causal=False, scale=None, cos_min=0.99, rel
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o, lse, tl, olo = _lib.fwd(q, k, v, scale=scale, causal=causal, with_residual=True, window=window)
     dense_lists = _lib.mask(None, lse, n, causal, 0.0, window=window)
-    ws = _lib.bwd_workspace(q, k, dense_lists)  # slots for the dense tile set when they fit
+    ws = _lib.bwd_workspace(q, k, dense_lists, causal=causal, window=window)
     ref = tuple(t.clone() for t in _lib.bwd(q, k, v, o, do, lse, dense_lists, scale=scale, causal=causal,
                                             workspace=ws, o_lo=olo, window=window))
     stats = torch.zeros(2, dtype=torch.int64, device=q.device)

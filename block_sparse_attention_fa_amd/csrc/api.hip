@@ -3,11 +3,13 @@
 // entry point are in include/backlite.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "../../include/backlite.h"
 
@@ -25,6 +27,8 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       uint16_t* dk, uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
                       uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
                       float* dkpart, int dk_chmin, hipStream_t st);
+size_t similarity_elems();
+hipError_t launch_similarity(const uint16_t* a, const uint16_t* b, long m, double* out, hipStream_t st);
 }  // namespace backlite
 
 namespace {
@@ -87,6 +91,12 @@ int check_window(int causal, int window) {
   if (window > 0 && !causal) return fail(BACKLITE_ERR_INVALID_ARG, "a sliding window (%d) requires causal", window);
   return BACKLITE_OK;
 }
+
+bool env_on(const char* name) {
+  const char* env = std::getenv(name);
+  return env && env[0] && env[0] != '0';
+}
+bool verbose() { return env_on("BACKLITE_VERBOSE"); }
 
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(BACKLITE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -217,19 +227,42 @@ int mask_impl(bool compact, const float* tile_lse, const double* tile_w, const f
   hipError_t e = backlite::launch_mask(tile_w ? nullptr : tile_lse, tile_w, lse_row, B, H, n, causal ? 1 : 0, window, (double)negl_prob,
                                        keep, qcnt, qidx, kcnt, kidx, stats, (hipStream_t)stream);
   int r = hip_status(e, "backlite_mask launch");
-  if (r == BACKLITE_OK && stats) {
-    const char* env = std::getenv("BACKLITE_VERBOSE");
-    if (env && env[0] && env[0] != '0') {
-      long long hs[2] = {0, 0};
-      e = hipMemcpyAsync(hs, stats, sizeof(hs), hipMemcpyDeviceToHost, (hipStream_t)stream);
-      if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
-      if (e != hipSuccess) return hip_status(e, "BACKLITE_VERBOSE stats readback");
-      std::fprintf(stderr,
-                   "[backlite] mask B=%d H=%d n=%d causal=%d negl_prob=%g: candidate tiles %lld, kept %lld, "
-                   "sparsity %.4f (accumulated)\n",
-                   B, H, n, causal ? 1 : 0, (double)negl_prob, hs[0], hs[1],
-                   hs[0] ? 1.0 - (double)hs[1] / (double)hs[0] : 0.0);
+  if (r == BACKLITE_OK && verbose()) {
+    // synchronous readback of the counts: a debugging aid, off by default
+    const size_t nq = (size_t)B * H * ntiles(n);
+    std::vector<int32_t> qc(nq), kc(nq);
+    long long hs[2] = {0, 0};
+    e = hipMemcpyAsync(qc.data(), qcnt, nq * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(kc.data(), kcnt, nq * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess && stats) e = hipMemcpyAsync(hs, stats, sizeof(hs), hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "BACKLITE_VERBOSE readback");
+    long long kept = 0, cand = 0;
+    int qmin = 1 << 30, qmax = 0, kmin = 1 << 30, kmax = 0;
+    for (size_t i = 0; i < nq; ++i) {
+      kept += qc[i];
+      qmin = std::min(qmin, (int)qc[i]);
+      qmax = std::max(qmax, (int)qc[i]);
+      kmin = std::min(kmin, (int)kc[i]);
+      kmax = std::max(kmax, (int)kc[i]);
     }
+    const int T = ntiles(n), w = (window > 0 && window < n) ? window : 0;
+    for (int qt = 0; qt < T; ++qt) {  // candidate key tiles per query tile
+      int lo = 0, hi = T - 1;
+      if (causal) hi = qt;
+      if (w && qt * kTile - w + 1 > 0) lo = (qt * kTile - w + 1) / kTile;
+      cand += hi - lo + 1;
+    }
+    cand *= (long long)B * H;
+    std::fprintf(stderr,
+                 "[backlite] mask B=%d H=%d n=%d causal=%d window=%d negl_prob=%g: kept %lld of %lld candidate "
+                 "tiles (density %.4f, sparsity %.4f); q-list length min %d mean %.1f max %d; k-list length min %d "
+                 "mean %.1f max %d",
+                 B, H, n, causal ? 1 : 0, w, (double)negl_prob, kept, cand, cand ? (double)kept / cand : 0.0,
+                 cand ? 1.0 - (double)kept / cand : 0.0, qmin, (double)kept / nq, qmax, kmin, (double)kept / nq,
+                 kmax);
+    if (stats) std::fprintf(stderr, "; stats buffer (accumulated) %lld / %lld", hs[1], hs[0]);
+    std::fprintf(stderr, "\n");
   }
   return r;
 }
@@ -273,6 +306,22 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
   TRY(check_ptr(dQ, "dQ"));
   TRY(check_ptr(dK, "dK"));
   TRY(check_ptr(dV, "dV"));
+  if (env_on("BACKLITE_CHECK")) {
+    // validate copies of the lists on the host before anything is launched
+    const size_t T = (size_t)ntiles(n), nc = (size_t)B * H * T;
+    std::vector<int32_t> qc(nc), kc(nc);
+    std::vector<uint16_t> qi(nc * T), ki(nc * T);
+    hipError_t e = hipMemcpyAsync(qc.data(), qcnt, nc * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(kc.data(), kcnt, nc * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(qi.data(), qidx, nc * T * 2, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(ki.data(), kidx, nc * T * 2, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "BACKLITE_CHECK list readback");
+    char msg[400];
+    if (backlite_check_lists(qc.data(), qi.data(), kc.data(), ki.data(), B, H, n, causal, window, kTile, msg,
+                             sizeof(msg)) != BACKLITE_OK)
+      return fail(BACKLITE_ERR_INVALID_ARG, "BACKLITE_CHECK: %s", msg);
+  }
   const size_t need = backlite_bwd_workspace_bytes(B, H, H_k, n, d);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(BACKLITE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, workspace_bytes,
@@ -304,12 +353,39 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
     const int v = std::atoi(env);
     if (v >= 1) chmin = v;
   }
-  return hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d,
-                                         scale, causal ? 1 : 0, window, dQ, dK, dV, (float*)ws,
-                                         (float*)(ws + delta_bytes(B, H, n)), (float*)(ws + kbar_off), gsinfo,
-                                         qbase, kslot, gs, gsl, cap, (int32_t*)(ws + plan_off),
-                                         (float*)(ws + part_off), chmin, (hipStream_t)stream),
-                    "backlite_bwd launch");
+  const int r = hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k,
+                                               d, scale, causal ? 1 : 0, window, dQ, dK, dV, (float*)ws,
+                                               (float*)(ws + delta_bytes(B, H, n)), (float*)(ws + kbar_off), gsinfo,
+                                               qbase, kslot, gs, gsl, cap, (int32_t*)(ws + plan_off),
+                                               (float*)(ws + part_off), chmin, (hipStream_t)stream),
+                           "backlite_bwd launch");
+  if (r == BACKLITE_OK && verbose()) {
+    // which G_Q path served the kept tiles (a synchronous readback, debugging only)
+    int32_t st[3] = {0, 0, 0};
+    if (gsinfo) {
+      hipError_t e = hipMemcpyAsync(st, gsinfo, sizeof(st), hipMemcpyDeviceToHost, (hipStream_t)stream);
+      if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+      if (e != hipSuccess) return hip_status(e, "BACKLITE_VERBOSE readback");
+      std::fprintf(stderr,
+                   "[backlite] bwd B=%d H=%d H_k=%d n=%d d=%d: %lld G_S slots; %d kept tiles, %d with a slot; G_Q "
+                   "from stored G_S for %s query tiles, recomputed for the rest\n",
+                   B, H, H_k, n, d, cap, st[1], st[2], st[0] ? "all" : "a prefix of the");
+    } else {
+      std::fprintf(stderr, "[backlite] bwd B=%d H=%d H_k=%d n=%d d=%d: no G_S slots, G_Q recomputed\n", B, H, H_k,
+                   n, d);
+    }
+  }
+  return r;
+}
+
+size_t backlite_similarity_elems(void) { return backlite::similarity_elems(); }
+
+int backlite_similarity_sums(const uint16_t* a, const uint16_t* b, int64_t m, double* out, void* stream) {
+  if (m < 0) return fail(BACKLITE_ERR_INVALID_ARG, "element count must be >= 0 (got %lld)", (long long)m);
+  TRY(check_ptr(a, "a"));
+  TRY(check_ptr(b, "b"));
+  TRY(check_ptr(out, "out"));
+  return hip_status(backlite::launch_similarity(a, b, (long)m, out, (hipStream_t)stream), "backlite_similarity_sums");
 }
 
 const char* backlite_status_string(int status) {

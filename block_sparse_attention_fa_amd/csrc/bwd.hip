@@ -14,9 +14,10 @@
 //   as row operands, G_V and G_K read them through the LDS transpose read.
 // dq_kernel (bwd_dq.hip): one workgroup per (b, h, query tile qt) walks the
 //   tile's list of kept key tiles with K, V row-major in LDS.
-// Stored-G_S path (bwd_gs.hip), taken when the workspace has a slot for every
-//   kept tile: the G_K/G_V pass also writes each tile's bf16 G_S, and the G_Q
-//   pass multiplies the stored G_S by K instead of rebuilding P and G_S.
+// Stored-G_S path (bwd_gs.hip), when the workspace has G_S slots: the G_K/G_V
+//   pass also writes each kept tile's bf16 G_S, and the G_Q pass multiplies the
+//   stored G_S by K instead of rebuilding P and G_S, for every query tile whose
+//   kept tiles all found a slot (the rest are recomputed).
 // Every pass is free of atomics, so results are bit-reproducible.
 #include "bl_device.h"
 #include "bwd_common.h"
@@ -280,17 +281,17 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // With slots in the workspace, the slot pass decides on the device whether
-  // every kept tile fits; the variant of each pass that does not apply returns
-  // at once.
+  // With slots in the workspace the G_K/G_V pass stores G_S for every kept
+  // tile that has a slot (slots are dealt in query-tile order); each query tile
+  // whose kept tiles all have one takes its G_Q from the stored tiles
+  // (dqs_kernel), the others are recomputed (dq_kernel).  The choice per query
+  // tile is made on the device, so the host reads nothing back.
   if (a.gsinfo) {
     e = launch_gs_slots(a, st);
     if (e != hipSuccess) return e;
     ProfScope ps(PK_DKDV, st);
     e = D == 64 ? launch_dkdv_d64_gs(a, CAUSAL, st) : launch_dkdv_d128_gs(a, CAUSAL, st);
-    if (e != hipSuccess) return e;
-  }
-  {
+  } else {
     ProfScope ps(PK_DKDV, st);
     e = D == 64 ? launch_dkdv_d64(a, CAUSAL, st) : launch_dkdv_d128(a, CAUSAL, st);
   }

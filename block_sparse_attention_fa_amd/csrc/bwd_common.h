@@ -24,7 +24,7 @@ struct BwdArgs {
   float* lse2;  // row LSE in log2 units (LSE * log2 e), [B, H, n]
   float* kbar;  // per key tile mean of K over its valid keys, [B, Hk, T, d]
   // Stored-G_S state (all NULL when the workspace holds no slots).
-  int32_t* gsinfo;     // [0] 1 = stored path taken, [1] kept tiles, [2..3] slot capacity (int64)
+  int32_t* gsinfo;     // [0] 1 = every kept tile had a slot, [1] kept tiles, [2] kept tiles with a slot
   uint32_t* qbase;     // [B, H, T]: first slot of each query tile's kept tiles
   uint32_t* kslot;     // [B, H, T, T]: slot of each k-list entry, laid out like kidx
   uint16_t* gs;        // slots of 128 x 128 bf16 G_S

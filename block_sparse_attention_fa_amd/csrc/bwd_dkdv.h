@@ -29,7 +29,8 @@ __device__ __forceinline__ QgSrc qg_src(const BwdArgs& a, long bh, int b, int h,
   const int n = a.n;
   const long qstride = (long)a.H * D;
   const int q0 = qt * TILE;
-  const uint32_t rows = valid ? (uint32_t)min(TILE, n - q0) : 0u;
+  // list entries past the last tile (a malformed list) read as empty tiles
+  const uint32_t rows = (valid && q0 < n) ? (uint32_t)min(TILE, n - q0) : 0u;
   const long off = ((long)b * n + q0) * qstride + (long)h * D;
   const uint32_t bytes = rows * (uint32_t)qstride * 2u;
   return QgSrc{buffer_rsrc(a.q + off, bytes), buffer_rsrc(a.dout + off, bytes),
@@ -80,12 +81,11 @@ constexpr int DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141, DPP_XOR2 = 0x
 // The next listed query tile is copied into the other LDS stage while the
 // current one is consumed.
 //
-// When the workspace carries the stored-G_S state (a.gsinfo != NULL), the
-// device-side flag gsinfo[0] says which variant of the pass runs: the other
-// one returns at once, so the host needs no readback to choose.
+// The GS variant runs whenever the workspace carries G_S slots (a.gsinfo !=
+// NULL); tiles whose slot index is past the capacity are computed without
+// storing their G_S (their query tile's G_Q is recomputed by dq_kernel).
 template <int D, bool CAUSAL, bool GS>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
-  if (a.gsinfo != nullptr && ((a.gsinfo[0] != 0) != GS)) return;
   constexpr int NT = 256;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     int p0 = 0;
     for (int hh = 0; hh < G && p0 < f1; ++hh) {
       const long row = ((bh0 + hh) * T + kt);
-      const int c = a.kcnt[row];
+      const int c = max(0, min(a.kcnt[row], T));  // as dk_plan_kernel counts it
       const int lo_p = max(f0, p0), hi_p = min(f1, p0 + c);
       for (int p = lo_p + tid; p < hi_p; p += NT) {
         itab[p - f0] = ((uint32_t)hh << 16) | a.kidx[row * T + (p - p0)];

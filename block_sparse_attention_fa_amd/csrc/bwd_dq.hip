@@ -23,7 +23,8 @@ template <int D>
 __device__ __forceinline__ KvSrc kv_src(const uint16_t* kbase, const uint16_t* vbase, const float* kbar, long stride,
                                         int n, int kt, bool valid) {
   const int key0 = kt * TILE;
-  const uint32_t rows = valid ? (uint32_t)min(TILE, n - key0) : 0u;
+  // list entries past the last tile (a malformed list) read as empty tiles
+  const uint32_t rows = (valid && key0 < n) ? (uint32_t)min(TILE, n - key0) : 0u;
   const uint32_t bytes = rows * (uint32_t)stride * 2u;
   return KvSrc{buffer_rsrc(kbase + (long)key0 * stride, bytes), buffer_rsrc(vbase + (long)key0 * stride, bytes),
                buffer_rsrc(kbar + (long)kt * D, valid ? (uint32_t)D * 4u : 0u)};
@@ -52,7 +53,6 @@ __device__ __forceinline__ void stage_kbar(float* Bd, const KvSrc& s, int wave, 
 // stage while the current one is consumed.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
-  if (a.gsinfo != nullptr && a.gsinfo[0] != 0) return;  // the stored-G_S pass computes G_Q
   constexpr int NT = 256;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -102,7 +102,11 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
   const uint16_t* vbase = a.v + ((long)b * n) * kvstride + (long)g * D;
   const float* kbar = a.kbar + (long)(b * a.Hk + g) * T * D;
-  const int cnt = a.qcnt[(long)bh * T + qt];
+  // with G_S slots, the query tiles whose kept tiles all have a slot take G_Q
+  // from the stored tiles (dqs_kernel); only the others are recomputed here
+  if (a.gsinfo != nullptr && a.gsinfo[0] != 0) return;  // every tile had a slot
+  const int cnt = max(0, min(a.qcnt[(long)bh * T + qt], T));
+  if (a.gsinfo != nullptr && (long long)a.qbase[(long)bh * T + qt] + cnt <= a.gs_cap) return;
   {
     // the q-list in LDS: reading the next key tile is then an LDS read, not a
     // global load whose latency would stall the wave before the next copy

@@ -11,9 +11,12 @@
 // over (b, h, qt).  kslot gives the same slot to each k-list entry, which is
 // what the G_K/G_V pass (walking k-lists) needs.
 //
-// Whether the path is taken is decided on the device: the scan compares the
-// number of kept tiles with the slot capacity and writes gsinfo[0]; the
-// kernels of the path not taken return at once.
+// Which query tiles take the path is decided on the device: tile (b, h, qt) is
+// stored iff qbase + qcnt <= the slot capacity, i.e. all of its kept tiles have
+// a slot.  dqs_kernel serves those tiles and dq_kernel the others, each
+// returning at once for a tile that is not its own; the G_K/G_V pass drops the
+// stores of slots past the capacity.  A budget smaller than the kept tiles
+// thus stores a prefix of the query tiles instead of giving up the path.
 #include "bl_device.h"
 #include "bwd_common.h"
 #include "bwd_dkdv.h"  // CPOL_NT
@@ -22,7 +25,8 @@
 namespace backlite {
 
 // qbase = exclusive prefix sum of qcnt over the B*H*T query tiles; gsinfo[0] =
-// (kept tiles <= capacity), gsinfo[1] = kept tiles (clamped to int32).  One
+// (kept tiles <= capacity), gsinfo[1] = kept tiles, gsinfo[2] = kept tiles
+// with a slot (both clamped to int32).  One
 // workgroup: each thread sums a contiguous run, the run totals are scanned in
 // LDS, then each thread writes its run's prefix values.
 __global__ __launch_bounds__(1024) void gs_scan_kernel(BwdArgs a) {
@@ -50,6 +54,7 @@ __global__ __launch_bounds__(1024) void gs_scan_kernel(BwdArgs a) {
     const long long total = part[1023];
     a.gsinfo[1] = (int32_t)min(total, 0x7fffffffLL);
     a.gsinfo[0] = total <= a.gs_cap ? 1 : 0;
+    a.gsinfo[2] = (int32_t)min(min(total, a.gs_cap), 0x7fffffffLL);
   }
 }
 
@@ -57,7 +62,6 @@ __global__ __launch_bounds__(1024) void gs_scan_kernel(BwdArgs a) {
 // kt's k-list.  One workgroup per (b, h, qt): each kept kt of the q-list finds
 // qt in kt's ascending k-list by binary search.
 __global__ __launch_bounds__(256) void gs_slot_kernel(BwdArgs a) {
-  if (a.gsinfo[0] == 0) return;
   const int T = a.T;
   const long bq = blockIdx.x;  // (b * H + h) * T + qt
   const int qt = (int)(bq % T);
@@ -107,7 +111,6 @@ __device__ __forceinline__ void stage_k_part(bf16* Kd, const __amdgpu_buffer_rsr
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
-  if (a.gsinfo[0] == 0) return;
   constexpr int NT = 256;
   constexpr int NDB = D / 32;
   constexpr int NKS = TILE / 16;  // 16-key contraction steps per key tile
@@ -147,6 +150,8 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   const long bq = (long)bh * T + qt;
   const int cnt = max(0, min(a.qcnt[bq], T));
   const uint32_t sbase = a.qbase[bq];
+  // only query tiles whose kept tiles all have a slot; dq_kernel recomputes the rest
+  if ((long long)sbase + cnt > a.gs_cap) return;
   {
     const uint16_t* list = a.qidx + bq * T;
     for (int i = tid; i < cnt; i += NT) itab[i] = list[i];
@@ -179,8 +184,10 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     return S == 0 ? Kb0 : S == 1 ? Kb1 : Kb2;
   };
   auto stage_k = [&](int i, auto st) {
-    const bool valid = i < cnt;
-    const int kt = valid ? (int)__builtin_amdgcn_readfirstlane(itab[i]) : 0, key0 = kt * TILE;
+    int kt = i < cnt ? (int)__builtin_amdgcn_readfirstlane(itab[i]) : 0;
+    const bool valid = i < cnt && kt < T;  // entries past the last tile read as empty
+    if (!valid) kt = 0;
+    const int key0 = kt * TILE;
     const uint32_t rows = valid ? (uint32_t)min(TILE, n - key0) : 0u;
     const size_t slot = (size_t)sbase + (size_t)i;
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + (long)key0 * kvstride, rows * (uint32_t)kvstride * 2u);

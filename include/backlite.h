@@ -80,15 +80,20 @@ size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d);
  * query tile uint32 [B, H, T], slots per k-list entry uint32 [B, H, T, T],
  * then the slots (each 32 KB of bf16 G_S plus 2 KB of fp32 sums of its
  * rounding residual).  Any workspace of at least the base size plus the state
- * and index arrays plus one slot enables the path; the device takes it only
- * when the mask's kept tile pairs fit the slots, and falls back to the
- * recomputing G_Q pass otherwise.  max_tiles < 1 returns the base size. */
+ * and index arrays plus one slot enables the path.  Slots are dealt to the
+ * kept tiles in query-tile order (b, h, qt, then q-list order); every query
+ * tile whose kept tiles all received a slot takes its G_Q from the stored
+ * tiles, and the remaining query tiles are recomputed.  So a slot budget
+ * smaller than the kept tiles still serves a prefix of the query tiles, and
+ * the choice is made on the device: the host reads nothing back.
+ * max_tiles < 1 returns the base size. */
 size_t backlite_bwd_workspace_bytes_stored(int B, int H, int H_k, int n, int d, int64_t max_tiles);
 
 /* Byte offset, within a workspace enabling the stored path, of its state
- * words (int32): [0] = 1 if the last backlite_bwd on it took the stored path,
- * [1] = the kept tile pairs it counted.  Valid once that call has completed
- * on its stream. */
+ * words (int32): [0] = 1 if every kept tile of the last backlite_bwd on it had
+ * a slot (G_Q came from stored G_S for every query tile), [1] = the kept tile
+ * pairs it counted, [2] = how many of them had a slot.  Valid once that call
+ * has completed on its stream. */
 size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d);
 
 /* Forward: exact attention plus per-(row, key tile) statistics.
@@ -155,6 +160,9 @@ int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
  *   kcnt, kidx: the same per key tile kt (kept query tiles, ascending).
  *   stats: optional (may be NULL) int64[2], ACCUMULATED into (not cleared):
  *     [0] += candidate tile pairs, [1] += kept tile pairs.
+ *   With the environment variable BACKLITE_VERBOSE=1 the call synchronises and
+ *   prints the kept and candidate tile counts, the density, and the minimum,
+ *   mean and maximum q-list and k-list lengths to stderr.
  * tile_lse may be NULL only with negl_prob == 0 (every candidate is kept).
  * negl_prob must be finite and in [0, 1); with negl_prob <= 1 every query tile
  * keeps at least one key tile. */
@@ -186,7 +194,15 @@ int backlite_mask(const float* tile_lse, const float* lse_row,
  * several workgroups whose fp32 partial sums are added in a fixed order; the
  * environment variable BACKLITE_DKDV_MIN_CHUNK (default 16) sets the smallest
  * chunk length in tiles.
- * The result is deterministic (no atomics): repeated calls give identical bits. */
+ * The result is deterministic (no atomics): repeated calls give identical bits.
+ * Lists: the kernels read counts clamped to [0, T] and treat entries >= T as
+ * empty tiles, so malformed lists cannot address memory outside the tensors;
+ * they can still give wrong gradients.  With the environment variable
+ * BACKLITE_CHECK=1 the call first copies the four lists to the host (a
+ * synchronous readback) and validates them with backlite_check_lists, returning
+ * BACKLITE_ERR_INVALID_ARG with the reason before launching anything.  With
+ * BACKLITE_VERBOSE=1 it reports, after a synchronising readback, how many kept
+ * tiles had a G_S slot. */
 int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
                  const int32_t* qcnt, const uint16_t* qidx,
@@ -220,6 +236,31 @@ int backlite_mask_compact(const double* tile_w, int B, int H, int n, int causal,
 int backlite_profile_enable(int on);
 int backlite_profile_reset(void);
 int backlite_profile_read(const char* kernel, double* total_ms, int64_t* launches);
+
+/* Validation of work lists held in HOST memory (plain C++, no GPU needed):
+ * the form backlite_mask writes and backlite_bwd expects.  qcnt [B, H, Tq],
+ * qidx [B, H, Tq, Tk], kcnt [B, H, Tk], kidx [B, H, Tk, Tq], with Tq =
+ * ceil(n / q_tile) query tiles of q_tile rows (64 or 128) and Tk = ceil(n / 128)
+ * key tiles.  Checks: counts within [0, Tq] / [0, Tk]; lists strictly
+ * ascending with entries below Tk / Tq; every q-list pair a candidate (causal:
+ * the key tile's first key <= the query tile's last row; window w > 0: its
+ * last key > the query tile's first row - w, as in "Introducing BackLite",
+ * "Training Nanochat", sliding-window layers); the k-lists holding exactly the
+ * q-lists' pairs.  Returns BACKLITE_OK, or BACKLITE_ERR_INVALID_ARG with the
+ * first violation described in msg (msg_len bytes, may be NULL / 0). */
+int backlite_check_lists(const int32_t* qcnt, const uint16_t* qidx, const int32_t* kcnt,
+                         const uint16_t* kidx, int B, int H, int n, int causal, int window,
+                         int q_tile, char* msg, size_t msg_len);
+
+/* Sums behind the gradient-similarity metrics of negl_prob calibration
+ * ("Introducing BackLite", "Experiments": BackLite's gradients are compared
+ * with exact attention's by cosine similarity and relative L2): for bf16
+ * device tensors a, b of m elements, out[0..3] = sum a*b, sum a*a, sum b*b,
+ * sum (a-b)^2, in fp64 (each product in fp32).  out is a device fp64 buffer of
+ * backlite_similarity_elems() doubles; past out[3] it is scratch.  Deterministic
+ * (fixed partial sums, added in order); asynchronous on stream. */
+size_t backlite_similarity_elems(void);
+int backlite_similarity_sums(const uint16_t* a, const uint16_t* b, int64_t m, double* out, void* stream);
 
 /* Static text for a status code. */
 const char* backlite_status_string(int status);

@@ -309,7 +309,7 @@ def cosine(a, ref):
 # sampled evaluation for long sequences
 # ----------------------------------------------------------------------------
 def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), k_tiles=(),
-                       scale=None, tile=TILE, block=TILE, all_rows=True, stats=None, window=0):
+                       scale=None, tile=TILE, block=TILE, all_rows=True, stats=None, window=0, threads=1):
     """The same definitions as forward / mask_from_stats / backward, evaluated
     for one group of query heads sharing a kv head, but only for selected
     outputs, so that long sequences stay tractable on the CPU.
@@ -324,7 +324,9 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
         (requires all_rows), summed over `heads`.
     `stats` (the "stats" entry of a previous call with the same inputs) skips
     pass 1, e.g. to evaluate several negl_prob values.  `window` is the sliding
-    window of `candidates` / `forward` (causal only).
+    window of `candidates` / `forward` (causal only).  `threads` > 1 runs the
+    query tiles of pass 1 on that many threads (each tile's arithmetic is the
+    same; numpy releases the interpreter lock inside its array operations).
     """
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     B, n, H, d = q.shape
@@ -350,7 +352,8 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
             TL = np.full((n, T), -np.inf)
             Dr = np.full(n, np.nan)
             Oq = {}
-            for qt in p1_tiles:
+
+            def pass1(qt):
                 r = np.arange(qt * tile, min(n, (qt + 1) * tile))
                 S = _score_block(qh, kh, r, scale, causal, window)
                 L[r] = _row_lse(S)
@@ -359,6 +362,16 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
                 Dr[r] = (doh[r] * O).sum(axis=1)
                 if qt in q_tiles:
                     Oq[qt] = O
+
+            if threads > 1:
+                from concurrent.futures import ThreadPoolExecutor
+
+                from threadpoolctl import threadpool_limits
+                with threadpool_limits(1), ThreadPoolExecutor(threads) as ex:  # one BLAS thread per tile
+                    list(ex.map(pass1, p1_tiles))
+            else:
+                for qt in p1_tiles:
+                    pass1(qt)
             st = {"L": L, "TL": TL, "D": Dr, "O": Oq}
         else:
             st = stats[hi]

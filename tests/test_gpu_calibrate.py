@@ -1,5 +1,6 @@
 """negl_prob calibration on the GPU path against the oracle's calibration
 (the same bisection over the oracle's fp64 forward, mask and backward).  GPU only."""
+import numpy as np
 import pytest
 import torch
 
@@ -30,17 +31,32 @@ def test_calibration_matches_oracle(w, win):
     ref = orc.calibrate(x["q"], x["k"], x["v"], x["do"], causal=w.causal, iters=iters, window=win)
     flush_print(f"  gpu {got['negl_prob']} (sparsity {got['sparsity']:.3f}) oracle {ref['negl_prob']} "
                 f"(sparsity {ref['sparsity']:.3f}); probes {got['probes']} / {ref['probes']}")
-    # the probes decide identically unless an oracle metric sits within the GPU's
-    # gradient error (<= 1e-2 rel-L2, far less in cosine) of a target
-    margin = min(min(abs(c - 0.99), abs(r - 0.1)) for c, r in ref["agreement"].values())
-    if got["probes"] != ref["probes"]:
-        assert margin < 1e-2, f"probe decisions differ with margin {margin}"
-    else:
+    # The probes must decide identically, except where the two bisections first
+    # part: there an oracle metric must lie within the GPU's own gradient error
+    # of its target (cosine within 2e-3 of 0.99 or rel-L2 within 1e-2 of 0.1; the
+    # GPU's gradients sit ~5e-3 rel-L2 from the oracle's on each side of the
+    # comparison).  Later probes bisect different intervals and are not compared.
+    split = next((i for i, (a, b) in enumerate(zip(got["probes"], ref["probes"])) if a != b), None)
+    if split is None:
+        assert len(got["probes"]) == len(ref["probes"])
         assert got["negl_prob"] == ref["negl_prob"] and abs(got["sparsity"] - ref["sparsity"]) < 1e-12
-    for nm in ("dQ", "dK", "dV"):
-        cg, rg = got["agreement"][nm]
-        co, ro = ref["agreement"][nm]
-        assert abs(cg - co) < 2e-3 and abs(rg - ro) < 1e-2, (nm, cg, co, rg, ro)
+    else:
+        pi = got["probes"][split][0]
+        assert pi == ref["probes"][split][0]          # same value probed, different verdict
+        f = orc.forward(x["q"], x["k"], x["v"], causal=w.causal, window=win)
+        keep = orc.mask_from_stats(f["tile_lse"], f["lse"], w.n, w.causal, pi, window=win)
+        dense = orc.backward(x["q"], x["k"], x["v"], x["do"], causal=w.causal, window=win)
+        g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal, window=win)
+        at = orc.gradient_agreement(g, dense)
+        near = [nm for nm, (c, r) in at.items() if abs(c - 0.99) < 2e-3 or abs(r - 0.1) < 1e-2]
+        flush_print(f"  decisions part at probe {split} (negl_prob {pi}): oracle metrics {at}")
+        assert near, f"probe {split} (negl_prob {pi}) decided differently with every metric clear of its target"
+    if split is None:
+        # the same negl_prob: the GPU's similarity metrics match the oracle's
+        for nm in ("dQ", "dK", "dV"):
+            cg, rg = got["agreement"][nm]
+            co, ro = ref["agreement"][nm]
+            assert abs(cg - co) < 2e-3 and abs(rg - ro) < 1e-2, (nm, cg, co, rg, ro)
 
 
 def test_calibration_block_diagonal_takes_pi_max():
@@ -48,3 +64,20 @@ def test_calibration_block_diagonal_takes_pi_max():
     got = bl.calibrate_negl_prob(xg["q"], xg["k"], xg["v"], xg["do"], causal=False, pi_max=0.9, iters=4)
     assert got["negl_prob"] == 0.9 and got["probes"] == [(0.9, True)]
     assert abs(got["sparsity"] - (1.0 - 1.0 / 8)) < 1e-12
+
+
+@pytest.mark.parametrize("m", [1, 7, 4096 + 5, 3 * 1024 * 1024 + 3])
+def test_similarity_sums_match_numpy(m):
+    """The library's similarity reduction against fp64 numpy sums of the same
+    bf16 values, including a length that is not a multiple of 8 (tail path)."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_fa_amd as bl
+    g = torch.Generator().manual_seed(m)
+    a = torch.randn(m, generator=g).to(torch.bfloat16)
+    b = (a.float() + 0.1 * torch.randn(m, generator=g)).to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    s = bl._lib.similarity_sums(a.to(dev), b.to(dev))[:4].cpu().numpy()
+    x, y = orc.to_f64(a), orc.to_f64(b)
+    want = np.array([x @ y, x @ x, y @ y, (x - y) @ (x - y)])
+    np.testing.assert_allclose(s, want, rtol=1e-6, atol=1e-9)

@@ -180,21 +180,109 @@ def test_stored_path_matches_recompute(w):
     assert rl <= 2e-3
 
 
-def test_stored_path_falls_back_when_slots_run_out():
-    """A workspace with fewer slots than kept tiles: the device takes the
-    recompute path (state word 0) and the result equals the base workspace's."""
+@pytest.mark.parametrize("frac", [0.0, 0.4, 0.999])
+def test_stored_path_with_a_slot_budget(frac):
+    """Fewer G_S slots than kept tiles (a byte budget): slots go to the kept
+    tiles in query-tile order, the query tiles whose kept tiles all got one take
+    G_Q from the stored tiles and the rest recompute, decided on the device.
+    State words: not all stored, kept count, slotted count.  G_K/G_V equal the
+    recompute path's bit for bit; G_Q of the recomputed query tiles equals it
+    bit for bit, the stored ones agree to fp32 summation order; all match the
+    oracle."""
     r = _setup(CASES[1])
-    bl, xg, w = r["bl"], r["xg"], r["w"]
-    m = bl.mask(r["tl"], r["lse"], w.n, w.causal, NEGL)
-    kept = int(m["qcnt"].sum().item())
-    ws = bl._lib.bwd_workspace(xg["q"], xg["k"], m, stored_tiles=kept - 1)
+    bl, x, xg, w = r["bl"], r["x"], r["xg"], r["w"]
+    keep = orc.mask_from_stats(r["ref"]["tile_lse"], r["ref"]["lse"], w.n, w.causal, NEGL)
+    m = lists_to_torch(keep, r["dev"])
+    qcnt = m["qcnt"].cpu().numpy().reshape(-1)
+    kept = int(qcnt.sum())
+    slots = max(1, int(frac * kept))
+    ws = bl._lib.bwd_workspace(xg["q"], xg["k"], m, stored_tiles=slots)
     a = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=True, o_lo=r["olo"],
                workspace=ws)
-    taken, counted = bl._lib.bwd_stored_taken(ws, w.B, w.H, w.Hk, w.n, w.d)
-    assert not taken and counted == kept
+    all_in, counted, slotted = bl._lib.bwd_state(ws, w.B, w.H, w.Hk, w.n, w.d)
+    assert not all_in and counted == kept and slotted == slots
     b = _bwd_path(r, m, "recompute")
-    for u, v in zip(a, b):
-        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+    assert torch.equal(a[2].view(torch.int16), b[2].view(torch.int16))
+    # query tiles (b, h, qt) in slot order; stored iff exclusive prefix + count <= slots
+    stored = (np.cumsum(qcnt) <= slots).reshape(w.B, w.H, -1)
+    T = stored.shape[-1]
+    ga, gb = a[0].cpu(), b[0].cpu()
+    for bb in range(w.B):
+        for h in range(w.H):
+            for qt in range(T):
+                rows = slice(qt * 128, min(w.n, qt * 128 + 128))
+                u, v = ga[bb, rows, h], gb[bb, rows, h]
+                if stored[bb, h, qt]:
+                    assert orc.rel_l2(u, orc.to_f64(v)) <= 2e-3
+                else:
+                    assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+    flush_print(f"  slots {slots}/{kept}: {int(stored.sum())} of {stored.size} query tiles stored")
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal)
+    for name, got, ref in (("dQ", a[0], g["dQ"]), ("dK", a[1], g["dK"]), ("dV", a[2], g["dV"])):
+        assert_close_grad(name, got.cpu(), ref)
+
+
+@pytest.mark.parametrize("w", [CASES[0], CASES[1], CASES[2], CASES[5]], ids=[IDS[0], IDS[1], IDS[2], IDS[5]])
+def test_delta_buffer(w):
+    """The D preprocess on its own: the backward leaves D = rowsum(G_O * O) in
+    fp32 at the start of its workspace ([B, H, n]).  Against the oracle's
+    delta() of the same bf16 operands (O + O_lo when the residual is passed, O
+    alone when not) it agrees to fp32 rounding; against the oracle's fp64 D from
+    its own forward, the residual brings it closer."""
+    r = _setup(w)
+    bl, x, xg = r["bl"], r["x"], r["xg"]
+    m = bl.mask(r["tl"], r["lse"], w.n, w.causal, NEGL)
+    B, H, n = w.B, w.H, w.n
+    ref64 = orc.delta(x["do"], r["ref"]["O"])
+    errs = {}
+    for with_lo in (True, False):
+        ws = bl._lib.bwd_workspace(xg["q"], xg["k"], m, stored_tiles=0)
+        bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], m, causal=w.causal,
+               o_lo=r["olo"] if with_lo else None, workspace=ws)
+        D = ws[:B * H * n * 4].view(torch.float32).view(B, H, n).cpu().numpy().astype(np.float64)
+        o_used = orc.to_f64(r["o"].cpu()) + (orc.to_f64(r["olo"].cpu()) if with_lo else 0.0)
+        want = orc.delta(x["do"], o_used)
+        scale = orc.delta(np.abs(orc.to_f64(x["do"])), np.abs(o_used))  # sum of |terms| per row
+        assert np.all(np.abs(D - want) <= 2e-6 * scale + 1e-30), f"O_lo={with_lo}: D off by more than fp32 rounding"
+        errs[with_lo] = orc.rel_l2(D, ref64)
+    flush_print(f"  D rel-L2 vs fp64 oracle: with O_lo {errs[True]:.2e}, O alone {errs[False]:.2e}")
+    assert errs[True] <= 1e-2 and errs[False] <= 1e-2
+    if n > 1:
+        assert errs[True] < errs[False]
+
+
+# 128 query heads on one kv head: every key tile's G_K/G_V list holds 128 x 17 =
+# 2176 items, more than the 2048-item window the G_K/G_V pass keeps in LDS
+WIDE = small(2176, H=128, Hk=1, d=64, causal=False, kind="gaussian", seed=12)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_item_window_refill(path, monkeypatch):
+    """A G_K/G_V chunk longer than the LDS item window (2048 items): with the
+    minimum chunk set above the list length no list is split and the pass
+    refills its item window mid-chunk.  Gradients match the oracle (dense, every
+    pair kept) and the split run (chunks of 16); G_Q, untouched by the chunking,
+    is identical bit for bit."""
+    w = WIDE
+    r = _setup(w)
+    bl, x, xg = r["bl"], r["x"], r["xg"]
+    m = bl.mask(None, r["lse"], w.n, w.causal, 0.0)
+    T = orc.ntiles(w.n)
+    items = int(m["kcnt"].cpu().numpy().reshape(w.B, w.Hk, w.H // w.Hk, T).sum(axis=2).max())
+    assert items > 2048
+    monkeypatch.setenv("BACKLITE_DKDV_MIN_CHUNK", "4096")
+    whole = _bwd_path(r, m, path)
+    monkeypatch.setenv("BACKLITE_DKDV_MIN_CHUNK", "16")
+    split = _bwd_path(r, m, path)
+    assert torch.equal(whole[0].view(torch.int16), split[0].view(torch.int16))
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], causal=w.causal)
+    for name, got, alt, ref in (("dQ", whole[0], split[0], g["dQ"]), ("dK", whole[1], split[1], g["dK"]),
+                                ("dV", whole[2], split[2], g["dV"])):
+        rl, cs = assert_close_grad(name, got.cpu(), ref)
+        assert_close_grad(name + " (split)", alt.cpu(), ref)
+        flush_print(f"  {path} {name}: rel-L2 {rl:.2e} cos {cs:.6f}; whole vs split "
+                    f"{orc.rel_l2(got.cpu(), orc.to_f64(alt.cpu())):.1e}")
 
 
 # attention sinks: every query tile keeps key tile 0, whose list (48 items over
@@ -264,6 +352,29 @@ def test_module_autograd_matches_oracle():
     assert_close_out("lse", lse.cpu(), ref["lse"])
     for name, got, rr in (("dQ", q.grad, g["dQ"]), ("dK", k.grad, g["dK"]), ("dV", v.grad, g["dV"])):
         assert_close_grad(name, got.cpu(), rr)
+
+
+def test_module_backward_twice_with_retained_graph():
+    """Two backward passes through one graph (retain_graph=True): the compact
+    statistics live with the graph, so the second pass runs the same sparse
+    backward and accumulates exactly the first one's gradients again."""
+    w = small(500, H=4, Hk=2, d=128, causal=True, kind="blocks", seed=7)
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_fa_amd as bl
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev).requires_grad_() for n in ("q", "k", "v"))
+    attn = bl.BackLite(negl_prob=NEGL, causal=True)
+    o = attn(q, k, v)
+    do = x["do"].to(dev)
+    o.backward(do, retain_graph=True)
+    first = [t.grad.clone() for t in (q, k, v)]
+    for t in (q, k, v):
+        t.grad = None
+    o.backward(do)
+    for a, t in zip(first, (q, k, v)):
+        assert torch.equal(a.view(torch.int16), t.grad.view(torch.int16))
 
 
 def test_backward_without_residual_gaussian():

@@ -366,6 +366,35 @@ def test_lists_from_keep():
     assert kidx[0, 0, 0, :2].tolist() == [0, 2] and kidx[0, 0, 2, :3].tolist() == [0, 1, 2]
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_delta_brute_force_identity(causal):
+    """D_i = sum_c G_O[i,c] O[i,c] must equal sum_j P_ij (G_O_i . V_j), since
+    O_i = sum_j P_ij V_j: the FlashAttention tutorial's row sum
+    ("Flash Attention Backward Pass") written out with Python loops over the
+    oracle's own P on a tiny GQA input.  A transposed operand, a sum over the
+    wrong axis or a head mix-up in delta() fails it."""
+    B, n, H, Hk, d = 2, 7, 4, 2, 3
+    q, k, v, do = (_rand((B, n, hh, d), s) for s, hh in ((1, H), (2, Hk), (3, Hk), (4, H)))
+    f = orc.forward(q, k, v, causal=causal, tile=4)
+    D = orc.delta(do, f["O"])
+    assert D.shape == (B, H, n)
+    scale = 1.0 / math.sqrt(d)
+    for b in range(B):
+        for h in range(H):
+            g = orc.kv_head(h, H, Hk)
+            for i in range(n):
+                s = [scale * sum(q[b, i, h, c] * k[b, j, g, c] for c in range(d)) if (not causal or j <= i)
+                     else -math.inf for j in range(n)]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                z = sum(e)
+                want = sum(e[j] / z * sum(do[b, i, h, c] * v[b, j, g, c] for c in range(d)) for j in range(n))
+                assert D[b, h, i] == pytest.approx(want, rel=1e-12, abs=1e-13)
+    # the backward's own full-row D is the same definition
+    g = orc.backward(q, k, v, do, causal=causal, tile=4)
+    np.testing.assert_allclose(g["D"], D, rtol=1e-12, atol=1e-13)
+
+
 def test_metrics():
     a = np.array([1.0, 2.0, 3.0])
     assert orc.rel_l2(a, a) == 0.0 and orc.cosine(a, a) == pytest.approx(1.0)
@@ -400,6 +429,15 @@ def test_sampled_head_group_matches_full_oracle():
             r = slice(kt * 64, min(n, kt * 64 + 64))
             np.testing.assert_allclose(sp["dK"][kt], g["dK"][0, r, gk], atol=1e-11)
             np.testing.assert_allclose(sp["dV"][kt], g["dV"][0, r, gk], atol=1e-11)
+        # pass 1 spread over threads: the same numbers, bit for bit
+        sp4 = orc.sampled_head_group(q, k, v, do, heads, 0.2, causal, q_tiles=[0, 2, 4], k_tiles=[0, 3, 4],
+                                     tile=64, block=64, window=win, threads=4)
+        for hi in range(len(heads)):
+            assert np.array_equal(sp4["lse"][hi], sp["lse"][hi])
+            assert np.array_equal(sp4["tile_lse"][hi], sp["tile_lse"][hi])
+            assert np.array_equal(sp4["D"][hi], sp["D"][hi]) and (sp4["keep"][hi] == sp["keep"][hi]).all()
+        for kt in (0, 3, 4):
+            assert np.array_equal(sp4["dK"][kt], sp["dK"][kt]) and np.array_equal(sp4["dV"][kt], sp["dV"][kt])
 
 
 def test_sampled_rows_only_mode_and_stats_reuse():
