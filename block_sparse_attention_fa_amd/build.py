@@ -32,7 +32,9 @@ FLAGS = [
 
 # per-file extra flags: the G_Q pass keeps MFMA results in arithmetic registers
 # (its S / G_P accumulators feed VALU work; measured 11% faster on MI355X),
-# while the G_K/G_V pass keeps its long-lived accumulators in AGPRs.
+# while the G_K/G_V pass keeps its accumulators in AGPRs: with arithmetic-
+# register results its 128 long-lived G_K/G_V accumulators plus the S / G_P
+# chunks exceed the 256 VGPRs and spill.
 FILE_FLAGS = {"bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

@@ -84,8 +84,15 @@ constexpr int DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141, DPP_XOR2 = 0x
 // The GS variant runs whenever the workspace carries G_S slots (a.gsinfo !=
 // NULL); tiles whose slot index is past the capacity are computed without
 // storing their G_S (their query tile's G_Q is recomputed by dq_kernel).
-template <int D, bool CAUSAL, bool GS>
+//
+// RAGGED (stored variant, non-causal, n % 128 != 0 only): this instance serves
+// only the last key tile, whose padded keys need masking; the main instance
+// skips that tile, so its loop carries no per-element mask at all.  (Causal
+// attention masks them through the diagonal, and without G_S stores their
+// rows are simply never written.)
+template <int D, bool CAUSAL, bool GS, bool RAGGED>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
+  static_assert(!RAGGED || (GS && !CAUSAL), "the ragged instance is the stored non-causal one");
   constexpr int NT = 256;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -109,6 +116,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   if ((int)blockIdx.x >= nchunks) return;
   const int4 chunk = reinterpret_cast<const int4*>(a.dkplan + 4)[work_index(blockIdx.x)];
   const int kt = chunk.x % T;
+  if constexpr (GS && !CAUSAL) {
+    // the ragged last key tile belongs to the RAGGED instance
+    if (RAGGED != (kt == T - 1 && T * TILE != n)) return;
+  }
   const int bg = chunk.x / T;
   const int g = bg % a.Hk, b = bg / a.Hk;
   const int G = a.H / a.Hk;
@@ -195,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   // next tile's barrier (or after the last tile): issued at the end of a tile
   // they would still be in flight at the next tile's wait for its staged
   // operands, which counts stores too.
-  const bool kragged = (kt + 1) * TILE > n;
+
   const uint32_t gs_voff = (uint32_t)(2 * l32 + h32) * 16u;
   const uint32_t ls_q = 16 * ((lane >> 3) & 1) + 8 * ((lane >> 2) & 1) + 4 * (lane >> 5) + 2 * ((lane >> 1) & 1) +
                         ((lane >> 4) & 1);
@@ -282,7 +293,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         return rd_row<D>((st & 1) ? Gc : Qc, lo, c4, st >> 1);
       }
     };
-    f32x16 sacc[2], gacc[2];  // S and G_P (later P and G_S) of the two chunks in flight
+    f32x16 sacc[2], gacc[2];  // S and G_P of the two chunks in flight
+    f32x16 pv16[2], gs16[2];  // P and G_S formed from them (fresh registers, not the accumulators)
     f32x4 l4[4], d4[4];         // LSE (log2 units) and D of the chunk in softmax
     float bt[8], bu[4], bv[2], bw;  // row-sum butterfly of the chunk in its B phase
     bf16x8 ring[RING];
@@ -331,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         // (mirror, half mirror, xor 2), each lane keeping the half its lane bit
         // selects.  Group 15: the xor-1 sum and the store (chunks 0-2) or its
         // deferral (chunk 3).
-        f32x16& gv = gacc[c4 & 1];
+        f32x16& gv = gs16[c4 & 1];
         static_for<0, 16>([&](auto gc) {
           constexpr int gi = decltype(gc)::value;
           if constexpr (gi * LB / 16 == st) {
@@ -383,13 +395,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
                 sv[r] = (off >= lim0 - cs * 32 && off < limw - cs * 32) ? sv[r] : -INFINITY;
               }
             }
-          } else if constexpr (GS) {
-            // padded keys of a ragged last tile: P = 0, so their G_S and
-            // residuals are zero in the stored slot (G_K / G_V drop them anyway)
-            if (kragged) {
+          } else if constexpr (RAGGED) {
+            // padded keys of the ragged last tile: P = 0, so their G_S and its
+            // rounding residuals are zero in the stored slot (their zero K rows
+            // would otherwise give P = exp(-LSE))
 #pragma unroll
-              for (int r = 0; r < 16; ++r) sv[r] = key < n ? sv[r] : -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r) sv[r] = key < n ? sv[r] : -INFINITY;
           }
         }
         static_for<0, 16>([&](auto ec) {
@@ -397,15 +408,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
           constexpr int r = decltype(ec)::value, j4 = r >> 2, t = r & 3;
           if constexpr (SC::elem_step(cs, r) == k) {
             const float pv = fast_exp2(fmaf(sv[r], c, -l4[j4][t]));
-            sv[r] = pv;
-            gv[r] = pv * (gv[r] - d4[j4][t]);
+            pv16[cs & 1][r] = pv;
+            gs16[cs & 1][r] = pv * (gv[r] - d4[j4][t]);
           }
         });
         if constexpr (SC::soft_end(cs) - 1 == k) {
-          pk[cs & 1][0] = pack8(sv, 0);
-          pk[cs & 1][1] = pack8(sv, 1);
-          sk[cs & 1][0] = pack8(gv, 0);
-          sk[cs & 1][1] = pack8(gv, 1);
+          pk[cs & 1][0] = pack8(pv16[cs & 1], 0);
+          pk[cs & 1][1] = pack8(pv16[cs & 1], 1);
+          sk[cs & 1][0] = pack8(gs16[cs & 1], 0);
+          sk[cs & 1][1] = pack8(gs16[cs & 1], 1);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
