@@ -54,6 +54,10 @@ def _load():
     lib.backlite_mask_compact.restype = I
     lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, Z, P]
     lib.backlite_bwd.restype = I
+    lib.backlite_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, P, P, P]
+    lib.backlite_bwd_noalloc.restype = I
+    lib.backlite_bwd_noalloc_scratch_bytes.argtypes = []
+    lib.backlite_bwd_noalloc_scratch_bytes.restype = Z
     lib.backlite_profile_enable.argtypes = [I]
     lib.backlite_profile_enable.restype = I
     lib.backlite_profile_reset.argtypes = []
@@ -331,6 +335,30 @@ def similarity_sums(a, b, out=None):
     _check(_load().backlite_similarity_sums(_ptr(a), _ptr(b), a.numel(), _ptr(out), _stream(a.device)),
            "backlite_similarity_sums")
     return out
+
+
+def bwd_noalloc(q, k, v, o, do, lse, lists, out, scale=None, causal=False, o_lo=None, window=0):
+    """The allocation-free backward (backlite_bwd_noalloc): the library's fixed
+    per-GPU scratch serves as workspace and the caller supplies the outputs
+    out = (dq, dk, dv); nothing is allocated by this call."""
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    for name, t, shp in (("q", q, (B, n, H, d)), ("k", k, (B, n, Hk, d)), ("v", v, (B, n, Hk, d)),
+                         ("o", o, (B, n, H, d)), ("do", do, (B, n, H, d))):
+        _need(t, name, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (B, H, n))
+    if o_lo is not None:
+        _need(o_lo, "o_lo", torch.bfloat16, (B, n, H, d))
+    dq, dk, dv = out
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _need(t, name, torch.bfloat16, tuple(ref.shape))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = _load().backlite_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
+                                      _ptr(lists["qcnt"]), _ptr(lists["qidx"]), _ptr(lists["kcnt"]),
+                                      _ptr(lists["kidx"]), B, n, H, Hk, d, scale, int(causal), int(window),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), _stream(q.device))
+    _check(rc, "backlite_bwd_noalloc")
+    return dq, dk, dv
 
 
 PROFILE_KERNELS = ("fwd", "mask_select", "mask_transpose", "delta", "kmean", "dk_plan", "dkdv", "dk_reduce", "dq",

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/backlite.h"
@@ -26,7 +27,7 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       int H, int Hk, int d, float scale, int causal, int window, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
                       uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
-                      float* dkpart, int dk_chmin, hipStream_t st);
+                      float* dkpart, int dk_chmin, int dk_pcap, hipStream_t st);
 size_t similarity_elems();
 hipError_t launch_similarity(const uint16_t* a, const uint16_t* b, long m, double* out, hipStream_t st);
 }  // namespace backlite
@@ -284,11 +285,14 @@ int backlite_mask_compact(const double* tile_w, int B, int H, int n, int causal,
                    kidx, stats, stream);
 }
 
-int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
-                 const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt, const uint16_t* qidx,
-                 const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k, int d,
-                 float scale, int causal, int window, uint16_t* dQ, uint16_t* dK, uint16_t* dV,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int check_bwd_args(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
+                   const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt,
+                   const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k,
+                   int d, float scale, int causal, int window, uint16_t* dQ, uint16_t* dK, uint16_t* dV) {
   TRY(check_shape(B, n, H, H_k, d));
   TRY(check_scale(scale));
   TRY(check_window(causal, window));
@@ -306,6 +310,90 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
   TRY(check_ptr(dQ, "dQ"));
   TRY(check_ptr(dK, "dK"));
   TRY(check_ptr(dV, "dV"));
+  return BACKLITE_OK;
+}
+
+int min_chunk() {
+  int chmin = 16;  // smallest chunk of a split G_K/G_V list (BACKLITE_DKDV_MIN_CHUNK overrides)
+  if (const char* env = std::getenv("BACKLITE_DKDV_MIN_CHUNK")) {
+    const int v = std::atoi(env);
+    if (v >= 1) chmin = v;
+  }
+  return chmin;
+}
+
+// Launch the backward with its base workspace at ws (D, LSE*log2 e, key means,
+// chunk plan, then pcap fp32 partial slots) and the stored-G_S part (NULL
+// gsinfo: none).
+int run_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O, const uint16_t* O_lo,
+            const uint16_t* dO, const float* lse_row, const int32_t* qcnt, const uint16_t* qidx,
+            const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k, int d, float scale, int causal,
+            int window, uint16_t* dQ, uint16_t* dK, uint16_t* dV, char* ws, int pcap, int32_t* gsinfo,
+            uint32_t* qbase, uint32_t* kslot, uint16_t* gs, float* gsl, long long cap, void* stream,
+            const char* what) {
+  const size_t kbar_off = 2 * delta_bytes(B, H, n);
+  const size_t plan_off = kbar_off + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
+  const size_t part_off = plan_off + dkplan_bytes(B, H_k, n);
+  return hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d,
+                                         scale, causal ? 1 : 0, window, dQ, dK, dV, (float*)ws,
+                                         (float*)(ws + delta_bytes(B, H, n)), (float*)(ws + kbar_off), gsinfo, qbase,
+                                         kslot, gs, gsl, cap, (int32_t*)(ws + plan_off), (float*)(ws + part_off),
+                                         min_chunk(), pcap, (hipStream_t)stream),
+                    what);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free backward: one copy per GPU the library runs
+// on, held until the process ends.  Host code never uses the array's name as
+// an address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_for_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BACKLITE_ERR_UNSUPPORTED, "device index %d beyond the %d the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(BACKLITE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch[dev] = p;
+  }
+  *out = (char*)g_scratch[dev];
+  return BACKLITE_OK;
+}
+
+// partial slots a scratch of kScratchBytes leaves after the fixed parts; <= 0: too small
+long long noalloc_partial_slots(int B, int H, int H_k, int n, int d) {
+  const size_t fixed = 2 * delta_bytes(B, H, n) + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float)) +
+                       dkplan_bytes(B, H_k, n);
+  if (fixed >= kScratchBytes) return 0;
+  const long long NK = (long long)B * H_k * ntiles(n);
+  const long long slots = (long long)((kScratchBytes - fixed) / ((size_t)2 * 128 * d * sizeof(float)));
+  return slots < NK ? slots : NK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
+                 const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt, const uint16_t* qidx,
+                 const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k, int d,
+                 float scale, int causal, int window, uint16_t* dQ, uint16_t* dK, uint16_t* dV,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_bwd_args(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window,
+                     dQ, dK, dV));
   if (env_on("BACKLITE_CHECK")) {
     // validate copies of the lists on the host before anything is launched
     const size_t T = (size_t)ntiles(n), nc = (size_t)B * H * T;
@@ -345,20 +433,10 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
     gs = (uint16_t*)(ws + need + idx);
     gsl = (float*)(ws + need + idx + (size_t)cap * 128 * 128 * 2);
   }
-  const size_t kbar_off = 2 * delta_bytes(B, H, n);
-  const size_t plan_off = kbar_off + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
-  const size_t part_off = plan_off + dkplan_bytes(B, H_k, n);
-  int chmin = 16;  // smallest chunk of a split G_K/G_V list (BACKLITE_DKDV_MIN_CHUNK overrides)
-  if (const char* env = std::getenv("BACKLITE_DKDV_MIN_CHUNK")) {
-    const int v = std::atoi(env);
-    if (v >= 1) chmin = v;
-  }
-  const int r = hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k,
-                                               d, scale, causal ? 1 : 0, window, dQ, dK, dV, (float*)ws,
-                                               (float*)(ws + delta_bytes(B, H, n)), (float*)(ws + kbar_off), gsinfo,
-                                               qbase, kslot, gs, gsl, cap, (int32_t*)(ws + plan_off),
-                                               (float*)(ws + part_off), chmin, (hipStream_t)stream),
-                           "backlite_bwd launch");
+  const int NK = B * H_k * ntiles(n);
+  const int r = run_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal,
+                        window, dQ, dK, dV, ws, NK, gsinfo, qbase, kslot, gs, gsl, cap, stream,
+                        "backlite_bwd launch");
   if (r == BACKLITE_OK && verbose()) {
     // which G_Q path served the kept tiles (a synchronous readback, debugging only)
     int32_t st[3] = {0, 0, 0};
@@ -376,6 +454,28 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
     }
   }
   return r;
+}
+
+size_t backlite_bwd_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int backlite_bwd_noalloc(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
+                         const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt,
+                         const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H,
+                         int H_k, int d, float scale, int causal, int window, uint16_t* dQ, uint16_t* dK,
+                         uint16_t* dV, void* stream) {
+  TRY(check_bwd_args(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window,
+                     dQ, dK, dV));
+  const long long pcap = noalloc_partial_slots(B, H, H_k, n, d);
+  if (pcap < 1)
+    return fail(BACKLITE_ERR_WORKSPACE,
+                "B=%d H=%d H_k=%d n=%d d=%d needs more than the %zu bytes of the allocation-free scratch "
+                "(use backlite_bwd with a workspace)",
+                B, H, H_k, n, d, kScratchBytes);
+  char* ws = nullptr;
+  TRY(scratch_for_current_device(&ws));
+  return run_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window, dQ,
+                 dK, dV, ws, (int)pcap, nullptr, nullptr, nullptr, nullptr, nullptr, 0, stream,
+                 "backlite_bwd_noalloc launch");
 }
 
 size_t backlite_similarity_elems(void) { return backlite::similarity_elems(); }

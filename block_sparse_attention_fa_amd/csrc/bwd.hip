@@ -122,10 +122,11 @@ __global__ __launch_bounds__(256) void kmean_kernel(BwdArgs a) {
 // of T (x group size) tiles.  Lists longer than the chunk length CH are split
 // into chunks of CH items, each its own workgroup; split chunks leave fp32
 // partial sums that dk_reduce_kernel adds up in chunk order (deterministic).
-// CH = max(minimum, ceil(2 * items / NK)): a split list of m > CH items makes
-// ceil(m / CH) < 2m / CH chunks, so all split chunks together are fewer than
-// 2 * items / CH <= NK.  That bounds the partial slots by NK and the chunks
-// by 2 NK without reading anything back.
+// CH = max(minimum, ceil(2 * items / P)) with P <= NK the partial slots the
+// workspace holds (NK normally; fewer in a fixed-size scratch): a split list of
+// m > CH items makes ceil(m / CH) < 2m / CH chunks, so all split chunks
+// together are fewer than 2 * items / CH <= P.  That bounds the partial slots
+// by P and the chunks by NK + P <= 2 NK without reading anything back.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void dk_plan_kernel(BwdArgs a) {
   __shared__ long long part[1024];
@@ -156,7 +157,8 @@ __global__ __launch_bounds__(1024) void dk_plan_kernel(BwdArgs a) {
   }
   if (tid == 0) {
     const long long total = part[0];
-    chs = (int)max((long long)a.dk_chmin, (2 * total + NK - 1) / NK);
+    const long long P = max(1, min(a.dk_pcap, NK));
+    chs = (int)max((long long)a.dk_chmin, (2 * total + P - 1) / P);
   }
   __syncthreads();
   const int CH = chs;
@@ -313,10 +315,10 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       int H, int Hk, int d, float scale, int causal, int window, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
                       uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
-                      float* dkpart, int dk_chmin, hipStream_t st) {
+                      float* dkpart, int dk_chmin, int dk_pcap, hipStream_t st) {
   BwdArgs a{q,    k,      v,     o,     olo,    dout,   lse,      qcnt, qidx, kcnt, kidx, dq,
             dk,   dv,     dbuf,  lse2,  kbar,   gsinfo, qbase,    kslot, gs, gsl, gs_cap, dkplan,
-            dkpart, dk_chmin, B, n, H, Hk, (n + TILE - 1) / TILE, window < n ? window : 0, scale,
+            dkpart, dk_chmin, dk_pcap, B, n, H, Hk, (n + TILE - 1) / TILE, window < n ? window : 0, scale,
             scale * LOG2E};
   if (d == 64) return causal ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
   return causal ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);

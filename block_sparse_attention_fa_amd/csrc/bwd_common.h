@@ -38,6 +38,7 @@ struct BwdArgs {
   int32_t* dkplan;
   float* dkpart;       // partial G_K, G_V of split key tiles: [slot][2][128][d] fp32, NK slots
   int dk_chmin;        // smallest chunk length
+  int dk_pcap;         // partial slots available (<= NK); bounds the number of split chunks
   int B, n, H, Hk, T;
   int window;          // sliding window (causal only): key j visible to row i iff i - window < j; 0 = none
   float scale;

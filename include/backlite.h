@@ -211,6 +211,33 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  uint16_t* dQ, uint16_t* dK, uint16_t* dV,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation as backlite_bwd with a workspace of the base
+ * size (G_Q recomputed, no stored-G_S slots), but its workspace is a device
+ * array inside the library, backlite_bwd_noalloc_scratch_bytes() = 256 MiB per
+ * GPU, reserved when the library's code is loaded on that GPU and held until
+ * the process ends.  The caller passes inputs and outputs only; the call makes
+ * no hipMalloc / hipFree and no other device allocation.  The scratch belongs
+ * to the calling thread's current device, which must be the stream's device.
+ * Every call on a GPU shares that GPU's scratch and leaves its contents behind
+ * (nothing in it needs to start at zero): calls that overlap on one GPU, on
+ * different streams or from different threads, race and must be serialised by
+ * the caller.  To fit the fixed scratch, split G_K/G_V lists are cut into
+ * longer chunks when their fp32 partial sums would not fit (the results then
+ * differ from backlite_bwd's by fp32 summation order; with no list split, or
+ * where the partial slots fit, they are identical bit for bit).  Shapes whose
+ * D, key-mean and plan arrays alone exceed the scratch return
+ * BACKLITE_ERR_WORKSPACE before anything is launched.  BACKLITE_CHECK and
+ * BACKLITE_VERBOSE are not consulted (their readbacks allocate host memory). */
+size_t backlite_bwd_noalloc_scratch_bytes(void);
+int backlite_bwd_noalloc(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                         const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
+                         const int32_t* qcnt, const uint16_t* qidx,
+                         const int32_t* kcnt, const uint16_t* kidx,
+                         int B, int n, int H, int H_k, int d, float scale, int causal, int window,
+                         uint16_t* dQ, uint16_t* dK, uint16_t* dV, void* stream);
+
 /* Mask from compact statistics: the tile_w output of backlite_fwd in place of
  * (tile_lse, lse_row); everything else as backlite_mask, and the same keep
  * bitmap and lists for the same forward.  tile_w may be NULL only with

@@ -118,3 +118,16 @@ def test_bwd_validation(L):
 def test_status_strings(L):
     for c in (0, -1, -2, -3, -4):
         assert L.backlite_status_string(c)
+
+
+def test_bwd_noalloc_rejects_shapes_beyond_the_scratch(L):
+    """The allocation-free backward's fixed scratch is 256 MiB: the 32k-token
+    shape with 1024 heads needs more for its D and key-mean arrays alone, so the
+    call returns the workspace status before touching the device."""
+    assert L.backlite_bwd_noalloc_scratch_bytes() == 256 << 20
+    args = [FAKE] * 11 + [1, 32760, 1024, 1024, 128, 0.088, 0, 0, FAKE, FAKE, FAKE, None]
+    assert L.backlite_bwd_noalloc(*args) == -3
+    assert b"scratch" in L.backlite_last_error()
+    bad = list(args)
+    bad[15] = 96                                  # head_dim: validated first
+    assert L.backlite_bwd_noalloc(*bad) == -2
