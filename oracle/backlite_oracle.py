@@ -65,7 +65,7 @@ def kv_head(h: int, H: int, Hk: int) -> int:
     return h // (H // Hk)
 
 
-def candidates(n: int, causal: bool, tile: int = TILE, window: int = 0) -> np.ndarray:
+def candidates(n: int, causal: bool, tile: int = TILE, window: int = 0, q_tile: int | None = None) -> np.ndarray:
     """cand[qt, kt]: the key tile holds at least one (i, j) with i, j < n that the
     causal rule (j <= i) allows.  Causally empty tiles are never candidates.
 
@@ -73,18 +73,24 @@ def candidates(n: int, causal: bool, tile: int = TILE, window: int = 0) -> np.nd
     query i iff i - window < j <= i (our reading of the blog's Nanochat windows of
     1024 / 2048 tokens, "Training Nanochat").  A tile pair is then a candidate iff
     its first key is <= its last row and its last key is > its first row - window.
+
+    q_tile: rows per query tile (default: tile).  The BackLite README forms the
+    mask "for each backward tile pair" ("How It Works / Sparse Backward
+    Masking"), and a backward's query tiles may be smaller than the forward's key
+    tiles; the result is then [ceil(n / q_tile), ceil(n / tile)].
     """
-    T = ntiles(n, tile)
-    qt = np.arange(T)[:, None]
-    kt = np.arange(T)[None, :]
+    q_tile = tile if q_tile is None else q_tile
+    Tq, Tk = ntiles(n, q_tile), ntiles(n, tile)
+    qt = np.arange(Tq)[:, None]
+    kt = np.arange(Tk)[None, :]
+    i_lo, i_hi = qt * q_tile, np.minimum(n, (qt + 1) * q_tile) - 1
+    k_lo, k_hi = kt * tile, np.minimum(n, (kt + 1) * tile) - 1
     if window:
         assert causal, "a sliding window is causal"
-        i_lo, i_hi = qt * tile, np.minimum(n, (qt + 1) * tile) - 1
-        k_lo, k_hi = kt * tile, np.minimum(n, (kt + 1) * tile) - 1
         return (k_lo <= i_hi) & (k_hi > i_lo - window)
     if causal:
-        return kt <= qt   # tile kt's first key 128*kt is <= the last row of tile qt
-    return np.ones((T, T), bool)
+        return np.broadcast_to(k_lo <= i_hi, (Tq, Tk)).copy()   # first key <= last row
+    return np.ones((Tq, Tk), bool)
 
 
 def _score_block(qh, kh, rows, scale, causal, window=0):
@@ -157,22 +163,25 @@ def forward(q, k, v, scale=None, causal=False, tile=TILE, heads=None, rows=None,
 # ----------------------------------------------------------------------------
 # mask from statistics
 # ----------------------------------------------------------------------------
-def tile_log_weights(tile_lse, lse, n, causal, tile=TILE, window=0):
+def tile_log_weights(tile_lse, lse, n, causal, tile=TILE, window=0, q_tile=None):
     """a[b, h, qt, kt] = max over valid rows i of the query tile of
     (LSE_tile[i, kt] - LSE_row[i]), in fp64; the tile weight is w = exp(a)
     (README phase 2: p_tile = exp(LSE_tile - LSE_row)).  -inf off-candidate.
 
-    tile_lse: [B, H, n, T] (fp32 or fp64 values); lse: [B, H, n].
+    tile_lse: [B, H, n, T] (fp32 or fp64 values); lse: [B, H, n].  The query
+    tiles have q_tile rows (default: tile), so a is [B, H, ceil(n/q_tile), T].
     """
+    q_tile = tile if q_tile is None else q_tile
     tl = np.asarray(tile_lse, dtype=np.float64)
     ls = np.asarray(lse, dtype=np.float64)
     B, H, nn, T = tl.shape
     assert nn == n
+    Tq = ntiles(n, q_tile)
     diff = tl - ls[..., None]
-    pad = np.full((B, H, T * tile, T), -np.inf)
+    pad = np.full((B, H, Tq * q_tile, T), -np.inf)
     pad[:, :, :n] = diff
-    a = pad.reshape(B, H, T, tile, T).max(axis=3)
-    cand = candidates(n, causal, tile, window)
+    a = pad.reshape(B, H, Tq, q_tile, T).max(axis=3)
+    cand = candidates(n, causal, tile, window, q_tile)
     return np.where(cand[None, None], a, -np.inf)
 
 
@@ -185,11 +194,11 @@ def select_keep(a, cand, negl_prob):
     prefix of the order.  Everything else among the candidates is kept.
     """
     a = np.asarray(a, dtype=np.float64)
-    B, H, T, _ = a.shape
-    keep = np.zeros((B, H, T, T), bool)
+    B, H, Tq, Tk = a.shape
+    keep = np.zeros((B, H, Tq, Tk), bool)
     for b in range(B):
         for h in range(H):
-            for qt in range(T):
+            for qt in range(Tq):
                 idx = np.nonzero(cand[qt])[0]
                 if idx.size == 0:
                     continue
@@ -203,27 +212,29 @@ def select_keep(a, cand, negl_prob):
     return keep
 
 
-def mask_from_stats(tile_lse, lse, n, causal, negl_prob, tile=TILE, window=0):
-    a = tile_log_weights(tile_lse, lse, n, causal, tile, window)
-    cand = candidates(n, causal, tile, window)
+def mask_from_stats(tile_lse, lse, n, causal, negl_prob, tile=TILE, window=0, q_tile=None):
+    a = tile_log_weights(tile_lse, lse, n, causal, tile, window, q_tile)
+    cand = candidates(n, causal, tile, window, q_tile)
     return select_keep(a, cand, negl_prob)
 
 
 def lists_from_keep(keep):
     """Compacted work lists.  q-list(qt) = kept kt ascending; k-list(kt) = kept
-    qt ascending.  Returns (qcnt, qidx, kcnt, kidx); rows of qidx/kidx hold the
-    list in their first cnt entries and zeros after."""
+    qt ascending.  Returns (qcnt [B,H,Tq], qidx [B,H,Tq,Tk], kcnt [B,H,Tk],
+    kidx [B,H,Tk,Tq]); rows of qidx/kidx hold the list in their first cnt
+    entries and zeros after."""
     keep = np.asarray(keep, bool)
-    B, H, T, _ = keep.shape
+    B, H, Tq, Tk = keep.shape
     qcnt = keep.sum(axis=3).astype(np.int32)
     kcnt = keep.sum(axis=2).astype(np.int32)
-    qidx = np.zeros((B, H, T, T), np.uint16)
-    kidx = np.zeros((B, H, T, T), np.uint16)
+    qidx = np.zeros((B, H, Tq, Tk), np.uint16)
+    kidx = np.zeros((B, H, Tk, Tq), np.uint16)
     for b in range(B):
         for h in range(H):
-            for t in range(T):
+            for t in range(Tq):
                 r = np.nonzero(keep[b, h, t])[0]
                 qidx[b, h, t, :r.size] = r
+            for t in range(Tk):
                 c = np.nonzero(keep[b, h, :, t])[0]
                 kidx[b, h, t, :c.size] = c
     return qcnt, qidx, kcnt, kidx
@@ -239,10 +250,11 @@ def delta(do, o):
 
 
 def backward(q, k, v, do, keep=None, scale=None, causal=False, tile=TILE,
-             heads=None, q_rows=None, window=0):
+             heads=None, q_rows=None, window=0, q_tile=None):
     """Masked attention backward in fp64.
 
-    keep: [B, H, T, T] bool tile mask over *all* heads (None = every candidate).
+    keep: [B, H, Tq, T] bool tile mask over *all* heads (None = every candidate);
+    its query tiles have q_tile rows (default: tile), its key tiles tile keys.
     heads: restrict to these query heads (G_K/G_V then sum over those heads only).
     q_rows: restrict the query rows that contribute (G_Q is returned for those
     rows only; G_K/G_V then hold only those rows' contributions).
@@ -254,8 +266,8 @@ def backward(q, k, v, do, keep=None, scale=None, causal=False, tile=TILE,
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     heads = list(range(H)) if heads is None else list(heads)
     rows = np.arange(n) if q_rows is None else np.asarray(q_rows)
-    T = ntiles(n, tile)
-    cand = candidates(n, causal, tile, window)
+    q_tile = tile if q_tile is None else q_tile
+    cand = candidates(n, causal, tile, window, q_tile)
     dQ = np.zeros((B, len(rows), len(heads), d))
     dK = np.zeros((B, n, Hk, d))
     dV = np.zeros((B, n, Hk, d))
@@ -275,7 +287,7 @@ def backward(q, k, v, do, keep=None, scale=None, causal=False, tile=TILE,
                 P = np.exp(S - L[:, None])
                 O = P @ vh
                 D = (doh[r] * O).sum(axis=1)           # full-row D
-                M = km[(r // tile)[:, None], kt_of_col[None, :]]
+                M = km[(r // q_tile)[:, None], kt_of_col[None, :]]
                 Ph = np.where(M, P, 0.0)
                 dP = doh[r] @ vh.T
                 dS = Ph * (dP - D[:, None])
@@ -309,7 +321,8 @@ def cosine(a, ref):
 # sampled evaluation for long sequences
 # ----------------------------------------------------------------------------
 def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), k_tiles=(),
-                       scale=None, tile=TILE, block=TILE, all_rows=True, stats=None, window=0, threads=1):
+                       scale=None, tile=TILE, block=TILE, all_rows=True, stats=None, window=0, threads=1,
+                       q_tile=None):
     """The same definitions as forward / mask_from_stats / backward, evaluated
     for one group of query heads sharing a kv head, but only for selected
     outputs, so that long sequences stay tractable on the CPU.
@@ -327,6 +340,9 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
     window of `candidates` / `forward` (causal only).  `threads` > 1 runs the
     query tiles of pass 1 on that many threads (each tile's arithmetic is the
     same; numpy releases the interpreter lock inside its array operations).
+    `q_tile`: rows per query tile of the mask (default: tile); q_tiles and
+    k_tiles stay in units of `tile` rows / keys, and out["keep"] is
+    [ceil(n / q_tile), T].
     """
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     B, n, H, d = q.shape
@@ -337,7 +353,9 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
     g = kv_head(heads[0], H, Hk)
     assert all(kv_head(h, H, Hk) == g for h in heads)
     T = ntiles(n, tile)
-    cand = candidates(n, causal, tile, window)
+    q_tile = tile if q_tile is None else q_tile
+    assert tile % q_tile == 0, "query tiles subdivide the statistics' row blocks"
+    cand = candidates(n, causal, tile, window, q_tile)
     kh, vh = k[0, :, g], v[0, :, g]
     q_tiles, k_tiles = list(q_tiles), list(k_tiles)
     out = {"keep": [], "lse": [], "tile_lse": [], "D": [], "O": [], "dQ": [], "stats": []}
@@ -379,11 +397,11 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
         out["stats"].append(st)
         # mask of the visited query tiles
         a = tile_log_weights(np.where(np.isfinite(TL), TL, -np.inf)[None, None],
-                             np.where(np.isfinite(L), L, 0.0)[None, None], n, causal, tile, window)
+                             np.where(np.isfinite(L), L, 0.0)[None, None], n, causal, tile, window, q_tile)
         cv = cand.copy()
         visited = np.zeros(T, bool)
         visited[list(p1_tiles)] = True
-        cv[~visited] = False
+        cv[~np.repeat(visited, tile // q_tile)[:cv.shape[0]]] = False
         kp = select_keep(a, cv, negl_prob)[0, 0]
         out["keep"].append(kp)
         out["lse"].append(L)
@@ -395,13 +413,13 @@ def sampled_head_group(q, k, v, do, heads, negl_prob, causal=False, q_tiles=(), 
             r = np.arange(qt * tile, min(n, (qt + 1) * tile))
             S = _score_block(qh, kh, r, scale, causal, window)
             P = np.exp(S - L[r][:, None])
-            M = kp[qt][np.arange(n) // tile][None, :]
+            M = kp[(r // q_tile)[:, None], (np.arange(n) // tile)[None, :]]
             dS = np.where(M, P, 0.0) * (doh[r] @ vh.T - Dr[r][:, None])
             out["dQ"].append((h, qt, scale * (dS @ kh)))
         for kt in k_tiles:
             c = np.arange(kt * tile, min(n, (kt + 1) * tile))
             for qt in np.nonzero(kp[:, kt])[0]:
-                r = np.arange(qt * tile, min(n, (qt + 1) * tile))
+                r = np.arange(qt * q_tile, min(n, (qt + 1) * q_tile))
                 Sc = scale * (qh[r] @ kh[c].T)
                 if causal:
                     ok = c[None, :] <= r[:, None]

@@ -636,3 +636,126 @@ def test_window_matches_torch_library(n, window):
     tl = f["tile_lse"][0]
     m = tl.max(-1, keepdims=True)
     np.testing.assert_allclose(m[..., 0] + np.log(np.exp(tl - m).sum(-1)), f["lse"][0], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# backward query tiles smaller than the key tiles ("for each backward tile
+# pair", BackLite README, "How It Works / Sparse Backward Masking")
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n,tile,q_tile,causal,window", [(50, 8, 4, False, 0), (50, 8, 4, True, 0),
+                                                         (45, 8, 2, True, 0), (50, 8, 4, True, 7),
+                                                         (37, 4, 2, True, 5), (64, 8, 8, True, 0)])
+def test_candidates_query_tiles_brute_force(n, tile, q_tile, causal, window):
+    """cand[qt, kt] with q_tile-row query tiles: some (i, j) with i in the query
+    tile, j in the key tile, both < n, that the causal rule (and window) allow."""
+    cand = orc.candidates(n, causal, tile, window, q_tile)
+    Tq, Tk = -(-n // q_tile), -(-n // tile)
+    assert cand.shape == (Tq, Tk)
+    for qt in range(Tq):
+        for kt in range(Tk):
+            want = any((not causal or j <= i) and (not window or j > i - window)
+                       for i in range(qt * q_tile, min(n, (qt + 1) * q_tile))
+                       for j in range(kt * tile, min(n, (kt + 1) * tile)))
+            assert cand[qt, kt] == want, (qt, kt)
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 11)])
+def test_tile_log_weights_query_tiles_brute_force(causal, window):
+    """a[qt, kt] over q_tile-row query tiles, by loops over the rows; and the
+    tile-row weight is exactly the larger of its two half-tile weights."""
+    n, tile, q = 45, 8, 4
+    g = np.random.default_rng(5)
+    qq, kk, vv = (g.standard_normal((1, n, 2, 4)) * 2 for _ in range(3))
+    f = orc.forward(qq, kk, vv, causal=causal, tile=tile, window=window)
+    a = orc.tile_log_weights(f["tile_lse"], f["lse"], n, causal, tile, window, q_tile=q)
+    cand = orc.candidates(n, causal, tile, window, q)
+    for h in range(2):
+        for qt in range(a.shape[2]):
+            for kt in range(a.shape[3]):
+                rows = range(qt * q, min(n, (qt + 1) * q))
+                want = max(f["tile_lse"][0, h, i, kt] - f["lse"][0, h, i] for i in rows) if cand[qt, kt] else -np.inf
+                assert a[0, h, qt, kt] == want
+    a8 = orc.tile_log_weights(f["tile_lse"], f["lse"], n, causal, tile, window)
+    a4 = np.concatenate([a, np.full(a.shape[:2] + (a8.shape[2] * 2 - a.shape[2], a.shape[3]), -np.inf)], axis=2)
+    halves = np.maximum(a4[:, :, 0::2], a4[:, :, 1::2])
+    np.testing.assert_array_equal(np.where(np.isfinite(a8), a8, -np.inf), np.where(np.isfinite(a8), halves, -np.inf))
+
+
+def test_lists_from_rectangular_keep():
+    keep = np.zeros((1, 1, 4, 2), bool)
+    keep[0, 0] = [[1, 0], [1, 1], [0, 1], [0, 0]]
+    qcnt, qidx, kcnt, kidx = orc.lists_from_keep(keep)
+    assert qidx.shape == (1, 1, 4, 2) and kidx.shape == (1, 1, 2, 4)
+    assert qcnt.tolist() == [[[1, 2, 1, 0]]] and kcnt.tolist() == [[[2, 2]]]
+    assert qidx[0, 0, 1, :2].tolist() == [0, 1] and kidx[0, 0, 0, :2].tolist() == [0, 1]
+    assert kidx[0, 0, 1, :2].tolist() == [1, 2]
+
+
+def test_masked_grads_query_tiles_torch_autograd():
+    """As test_masked_grads_torch_autograd with 32-row query tiles against
+    64-key tiles: the element mask is keep[i // 32, j // 64]."""
+    n, d, t, q = 192, 8, 64, 32
+    qq, kk, vv, do = _rand((1, n, 1, d), 44, 1.5), _rand((1, n, 1, d), 45, 1.5), _rand((1, n, 1, d), 46), _rand((1, n, 1, d), 47)
+    sc = 0.5
+    for causal in (False, True):
+        keep = orc.candidates(n, causal, t, q_tile=q).copy()
+        keep[5, 0] = False
+        keep[2, 1] = False
+        keep[3, 1] = True
+        g = orc.backward(qq, kk, vv, do, keep=keep[None, None], scale=sc, causal=causal, tile=t, q_tile=q)
+        tq, tk, tv = (torch.from_numpy(x[0, :, 0]).requires_grad_() for x in (qq, kk, vv))
+        tdo = torch.from_numpy(do[0, :, 0])
+        S = sc * tq @ tk.T
+        if causal:
+            S = S.masked_fill(~torch.ones(n, n, dtype=torch.bool).tril(), float("-inf"))
+        P = torch.softmax(S, -1)
+        O = P @ tv
+        dS_dense, = torch.autograd.grad(O, S, tdo, retain_graph=True)
+        M = torch.from_numpy(np.kron(keep, np.ones((q, t), bool))[:n, :n])
+        dQ, dK = torch.autograd.grad(S, (tq, tk), torch.where(M, dS_dense, 0.0))
+        dV, = torch.autograd.grad(torch.where(M, P, 0.0).detach() @ tv, tv, tdo)
+        np.testing.assert_allclose(g["dQ"][0, :, 0], dQ.numpy(), atol=1e-11)
+        np.testing.assert_allclose(g["dK"][0, :, 0], dK.numpy(), atol=1e-11)
+        np.testing.assert_allclose(g["dV"][0, :, 0], dV.numpy(), atol=1e-11)
+
+
+def test_query_tile_selection_invariants():
+    """With half-height query tiles each half keeps its own rows' skipped mass
+    below negl_prob (I3 per tile), keeps at least one key tile (I5), and is
+    never less sparse than the full-height mask: a full tile's weight is the
+    larger of its halves', so every weight-sorted prefix the full tile skips,
+    each half can skip too."""
+    x = make_inputs(small(1000, H=2, d=64, causal=True, kind="blocks", seed=3))
+    f = orc.forward(x["q"], x["k"], x["v"], causal=True)
+    p = np.exp(f["tile_lse"] - f["lse"][..., None])
+    for pi in (0.01, 0.05, 0.2):
+        k128 = orc.mask_from_stats(f["tile_lse"], f["lse"], 1000, True, pi)
+        k64 = orc.mask_from_stats(f["tile_lse"], f["lse"], 1000, True, pi, q_tile=64)
+        assert k64.shape == (1, 2, 16, 8) and k64.sum(axis=3).min() >= 1
+        for qt in range(16):
+            rows = p[0, :, qt * 64:min(1000, (qt + 1) * 64), :]
+            assert ((rows * ~k64[0, :, qt, None, :]).sum(-1) < pi).all()
+        assert k64.sum() <= 2 * k128.sum()
+
+
+def test_sampled_head_group_query_tiles_match_full_oracle():
+    """The sampled evaluation with 32-row query tiles against 64-key tiles
+    reproduces the full oracle's mask, G_Q rows and G_K/G_V key tiles."""
+    n, d, t, q = 300, 16, 64, 32
+    for causal, win in ((False, 0), (True, 0), (True, 90)):
+        qq, kk, vv, do = (_rand((1, n, 2, d), 70, 1.5), _rand((1, n, 1, d), 71, 1.5), _rand((1, n, 1, d), 72),
+                          _rand((1, n, 2, d), 73))
+        f = orc.forward(qq, kk, vv, causal=causal, tile=t, window=win)
+        keep = orc.mask_from_stats(f["tile_lse"], f["lse"], n, causal, 0.2, tile=t, window=win, q_tile=q)
+        g = orc.backward(qq, kk, vv, do, keep=keep, causal=causal, tile=t, window=win, q_tile=q)
+        sp = orc.sampled_head_group(qq, kk, vv, do, [0, 1], 0.2, causal, q_tiles=[0, 2, 4], k_tiles=[0, 3, 4],
+                                    tile=t, block=t, window=win, q_tile=q)
+        for h in range(2):
+            assert (sp["keep"][h] == keep[0, h]).all()
+        for (h, qt, dq) in sp["dQ"]:
+            r = slice(qt * t, min(n, qt * t + t))
+            np.testing.assert_allclose(dq, g["dQ"][0, r, h], atol=1e-11)
+        for kt in (0, 3, 4):
+            r = slice(kt * t, min(n, kt * t + t))
+            np.testing.assert_allclose(sp["dK"][kt], g["dK"][0, r, 0], atol=1e-11)
+            np.testing.assert_allclose(sp["dV"][kt], g["dV"][0, r, 0], atol=1e-11)
