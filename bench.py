@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--gs-budget-gb", type=float, default=None,
                     help="device memory for G_S slots (default: a slot for every kept tile when they fit); "
                          "query tiles past the budget recompute G_Q")
+    ap.add_argument("--q-tile", type=int, choices=[64, 128], default=128,
+                    help="rows of the backward's query tiles (the headline uses the workload's 128x128 tiles)")
+    ap.add_argument("--no-q64", action="store_true",
+                    help="skip the extra measurement of the sparse backward with 64-row query tiles")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for memory counters)")
     return ap.parse_args()
@@ -198,11 +202,12 @@ def main():
                                       gs_budget_bytes=int(args.gs_budget_gb * 1e9))
         tiles = int(lists["qcnt"].sum().item())
         free, _ = torch.cuda.mem_get_info(dev)
-        tiles = min(tiles, max(0, (free - (4 << 30)) // _lib.SLOT_BYTES))
+        tiles = min(tiles, max(0, (free - (4 << 30)) // _lib.slot_bytes(lists.get("q_tile", TILE))))
         return _lib.bwd_workspace(q, k, lists, stored_tiles=tiles)
 
+    QT = args.q_tile
     o0, lse0, _, _ = bl.fwd(q, k, v, causal=causal, window=win, tile_lse=tl, with_residual=True)
-    ws = workspace(bl.mask(tl, lse0, n, causal, negl, window=win))
+    ws = workspace(bl.mask(tl, lse0, n, causal, negl, window=win, q_tile=QT))
     del o0, lse0
 
     def step(rec=None):
@@ -210,9 +215,9 @@ def main():
         if rec is not None:
             rec[0].record()
         if compact:
-            m = _lib.mask_compact(tw, B, H, n, causal, negl, stats=stats, window=win)
+            m = _lib.mask_compact(tw, B, H, n, causal, negl, stats=stats, window=win, q_tile=QT)
         else:
-            m = bl.mask(tl, lse, n, causal, negl, window=win, stats=stats)
+            m = bl.mask(tl, lse, n, causal, negl, window=win, stats=stats, q_tile=QT)
         if rec is not None:
             rec[1].record()
         bl.bwd(q, k, v, o, do, lse, m, causal=causal, window=win, workspace=ws, out=(dq, dk, dv), o_lo=olo)
@@ -259,7 +264,7 @@ def main():
     sparse_grads = (dq.clone(), dk.clone(), dv.clone()) if (args.grad_check and not args.no_dense) else None
     if not args.no_dense:
         o, lse, olo = step()
-        md = bl.mask(None, lse, n, causal, 0.0, window=win)
+        md = bl.mask(None, lse, n, causal, 0.0, window=win)  # dense: the query-tile height does not matter
         del ws
         ws = workspace(md)
         for _ in range(max(1, args.warmup)):
@@ -288,7 +293,7 @@ def main():
     pairs_dense = visible_pairs(n, win) if causal else float(n) * n
     f_dense_bwd = 10.0 * d * B * H * pairs_dense
     f_fwd = 4.0 * d * B * H * pairs_dense
-    tile_bwd_flop = 10.0 * TILE * TILE * d
+    tile_bwd_flop = 10.0 * QT * TILE * d  # per executed (query tile, key tile) pair
     dense_equiv_tflops = f_dense_bwd / (bwd_ms * 1e-3) / 1e12
     mfma_frac = kept * tile_bwd_flop / (bwd_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
 
@@ -299,7 +304,7 @@ def main():
     # dominant kernel: dK/dV pass; algorithmic work = 4 of the 5 backward GEMMs
     # (S, G_P, G_V, G_K) per executed tile = 8*128*128*d FLOP
     dkdv_ms = kms.get("dkdv")
-    dkdv_flop = kept * 8.0 * TILE * TILE * d
+    dkdv_flop = kept * 8.0 * QT * TILE * d
     achieved = dkdv_flop / (dkdv_ms * 1e-3) / 1e12 if dkdv_ms else None
     roofline = {"kernel": "dkdv", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS if achieved else None,
@@ -309,14 +314,49 @@ def main():
     # row sums (2 KB) from HBM and writes G_Q once: an HBM-bound pass
     roofline_gq = None
     if gq_stored and kms.get("dq"):
-        gq_bytes = kept * (TILE * TILE * 2 + 4 * TILE * 4) + B * n * H * d * 2
+        gq_bytes = kept * _lib.slot_bytes(QT) + B * n * H * d * 2
         gbs = gq_bytes / (kms["dq"] * 1e-3) / 1e9
         roofline_gq = {"kernel": "dqs", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                        "frac": gbs / PEAK_HBM_GBS}
 
+    # The same sparse backward with 64-row query tiles (the finer mask the
+    # per-row statistics allow): mask + backward timed over the same steps, on
+    # the forward's outputs of the last step.
+    q64 = None
+    if QT == TILE and not args.no_q64 and dense_ms is not None:
+        o, lse, olo = step()
+        st64 = torch.zeros(2, dtype=torch.int64, device=dev)
+        m64 = bl.mask(tl, lse, n, causal, negl, window=win, q_tile=64)
+        ws64 = workspace(m64)
+        for _ in range(max(1, args.warmup)):
+            m64 = bl.mask(tl, lse, n, causal, negl, window=win, q_tile=64)
+            bl.bwd(q, k, v, o, do, lse, m64, causal=causal, window=win, workspace=ws64, out=(dq, dk, dv), o_lo=olo)
+        torch.cuda.synchronize()
+        ev64 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev64[i][0].record()
+            m64 = bl.mask(tl, lse, n, causal, negl, window=win, q_tile=64, stats=st64)
+            ev64[i][1].record()
+            bl.bwd(q, k, v, o, do, lse, m64, causal=causal, window=win, workspace=ws64, out=(dq, dk, dv), o_lo=olo)
+            ev64[i][2].record()
+        torch.cuda.synchronize()
+        m64_ms = sum(e[0].elapsed_time(e[1]) for e in ev64) / args.steps
+        b64_ms = sum(e[1].elapsed_time(e[2]) for e in ev64) / args.steps
+        s64 = st64.cpu().tolist()
+        kept64 = s64[1] / args.steps
+        q64 = {"q_tile": 64, "bwd_ms": b64_ms, "mask_ms": m64_ms, "sparsity": 1.0 - s64[1] / s64[0],
+               "executed_64x128_tiles_per_step": kept64,
+               "dense_equiv_tflops": f_dense_bwd / (b64_ms * 1e-3) / 1e12,
+               "bwd_speedup_vs_dense": dense_ms / b64_ms,
+               "executed_tile_mfma_frac": kept64 * 10.0 * 64 * TILE * d / (b64_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+               "gq_path": "stored" if _lib.bwd_state(ws64, B, H, Hk, n, d)[0] else "partly stored or recompute",
+               "bwd_workspace_gb": ws64.numel() / 1e9}
+        del ws64, m64
+
     # mask algorithmic bytes: tile-LSE of every candidate pair (512 B), the row LSE
     # and D-like row data of each query tile, bitmap + list entries written
-    mask_bytes = cand * 512 + B * H * n * 4 + B * H * T * T * 1 + kept * 2 * 2 + 2 * B * H * T * 4
+    Tq = (n + QT - 1) // QT
+    mask_bytes = cand * 512 + B * H * n * 4 + B * H * Tq * T * 1 + kept * 2 * 2 + 2 * B * H * (Tq + T) * 4
     delta_bytes = B * H * n * (4 * d + 4 + 2 * d)  # O, G_O, O_lo read; D written
 
     out = {
@@ -333,7 +373,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "H_k": Hk, "n": n, "d": d, "causal": causal,
-                   "window": win, "negl_prob": negl, "tile": TILE, "stats": args.stats},
+                   "window": win, "negl_prob": negl, "tile": TILE, "q_tile": QT, "stats": args.stats},
         "bwd_ms": bwd_ms,
         "fwd_ms": fwd_ms,
         "mask_ms": mask_ms,
@@ -358,11 +398,15 @@ def main():
         "wall_s_timed": wall,
         "roofline": roofline,
         "roofline_gq": roofline_gq,
+        "q_tile_64": q64,
         "cpu_baseline": None,
     }
     log(f"[bench] fwd {fwd_ms:.3f} ms  mask {mask_ms:.3f} ms  bwd {bwd_ms:.3f} ms  dense bwd "
         f"{dense_ms if dense_ms is None else round(dense_ms, 3)} ms  sparsity {sparsity:.3f}  "
         f"dense-equiv {dense_equiv_tflops:.1f} TFLOP/s  exec-tile MFMA {100 * mfma_frac:.1f}%")
+    if q64:
+        log(f"[bench] 64-row query tiles: mask {q64['mask_ms']:.3f} ms  bwd {q64['bwd_ms']:.3f} ms  sparsity "
+            f"{q64['sparsity']:.3f}  speedup vs dense {q64['bwd_speedup_vs_dense']:.2f}x")
     if args.cpu_baseline == "on":
         del q, k, v, do, tl, ws, dq, dk, dv
         log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows of head 0 ...")

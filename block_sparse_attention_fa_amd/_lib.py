@@ -36,25 +36,25 @@ def _load():
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.backlite_tile_lse_elems.argtypes = [I, I, I, I]
     lib.backlite_tile_lse_elems.restype = Z
-    lib.backlite_mask_elems.argtypes = [I, I, I]
+    lib.backlite_mask_elems.argtypes = [I, I, I, I]
     lib.backlite_mask_elems.restype = Z
-    lib.backlite_count_elems.argtypes = [I, I, I]
+    lib.backlite_count_elems.argtypes = [I, I, I, I]
     lib.backlite_count_elems.restype = Z
     lib.backlite_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.backlite_bwd_workspace_bytes.restype = Z
-    lib.backlite_bwd_workspace_bytes_stored.argtypes = [I, I, I, I, I, ctypes.c_int64]
+    lib.backlite_bwd_workspace_bytes_stored.argtypes = [I, I, I, I, I, I, ctypes.c_int64]
     lib.backlite_bwd_workspace_bytes_stored.restype = Z
     lib.backlite_bwd_state_offset.argtypes = [I, I, I, I, I]
     lib.backlite_bwd_state_offset.restype = Z
     lib.backlite_fwd.argtypes = [P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P, P]
     lib.backlite_fwd.restype = I
-    lib.backlite_mask.argtypes = [P, P, I, I, I, I, I, F, P, P, P, P, P, P, P]
+    lib.backlite_mask.argtypes = [P, P, I, I, I, I, I, I, F, P, P, P, P, P, P, P]
     lib.backlite_mask.restype = I
-    lib.backlite_mask_compact.argtypes = [P, I, I, I, I, I, F, P, P, P, P, P, P, P]
+    lib.backlite_mask_compact.argtypes = [P, I, I, I, I, I, I, F, P, P, P, P, P, P, P]
     lib.backlite_mask_compact.restype = I
-    lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, Z, P]
+    lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, P, P, P, Z, P]
     lib.backlite_bwd.restype = I
-    lib.backlite_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, P, P, P]
+    lib.backlite_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, P, P, P]
     lib.backlite_bwd_noalloc.restype = I
     lib.backlite_bwd_noalloc_scratch_bytes.argtypes = []
     lib.backlite_bwd_noalloc_scratch_bytes.restype = Z
@@ -109,8 +109,8 @@ def _need(t, name, dtype, shape=None):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def ntiles(n: int) -> int:
-    return (n + TILE - 1) // TILE
+def ntiles(n: int, tile: int = TILE) -> int:
+    return (n + tile - 1) // tile
 
 
 def tile_lse_elems(B, H, n, causal) -> int:
@@ -118,8 +118,9 @@ def tile_lse_elems(B, H, n, causal) -> int:
 
 
 def tile_w_elems(B, H, n, causal) -> int:
-    """fp64 entries of the compact statistics: one per (b, h, tile pair)."""
-    return tile_lse_elems(B, H, n, causal) // TILE
+    """fp64 entries of the compact statistics: two per (b, h, tile pair), one per
+    64-row half of the query tile."""
+    return tile_lse_elems(B, H, n, causal) // 64
 
 
 def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_residual=False, window=0,
@@ -153,48 +154,48 @@ def fwd(q, k, v, scale=None, causal=False, with_stats=True, tile_lse=None, with_
     return o, lse, tile_lse
 
 
-def mask(tile_lse, lse, n, causal, negl_prob, stats=None, window=0):
-    """keep [B,H,T,T] u8, qcnt [B,H,T] i32, qidx [B,H,T,T] i16 (uint16 bits), kcnt, kidx."""
+def _mask_outputs(B, H, n, q_tile, dev):
+    T, Tq = ntiles(n), ntiles(n, q_tile)
+    return {
+        "keep": torch.empty((B, H, Tq, T), dtype=torch.uint8, device=dev),
+        "qcnt": torch.empty((B, H, Tq), dtype=torch.int32, device=dev),
+        "qidx": torch.empty((B, H, Tq, T), dtype=torch.int16, device=dev),
+        "kcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
+        "kidx": torch.empty((B, H, T, Tq), dtype=torch.int16, device=dev),
+        "q_tile": int(q_tile),
+    }
+
+
+def mask(tile_lse, lse, n, causal, negl_prob, stats=None, window=0, q_tile=TILE):
+    """keep [B,H,Tq,T] u8, qcnt [B,H,Tq] i32, qidx [B,H,Tq,T] i16 (uint16 bits),
+    kcnt [B,H,T], kidx [B,H,T,Tq], for query tiles of q_tile rows (128 or 64),
+    and "q_tile" itself (bwd() reads it)."""
     B, H, nn = lse.shape
     assert nn == n
     _need(lse, "lse", torch.float32)
     if tile_lse is not None:
         _need(tile_lse, "tile_lse", torch.float32, (tile_lse_elems(B, H, n, causal),))
-    T = ntiles(n)
     dev = lse.device
-    out = {
-        "keep": torch.empty((B, H, T, T), dtype=torch.uint8, device=dev),
-        "qcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
-        "qidx": torch.empty((B, H, T, T), dtype=torch.int16, device=dev),
-        "kcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
-        "kidx": torch.empty((B, H, T, T), dtype=torch.int16, device=dev),
-    }
+    out = _mask_outputs(B, H, n, q_tile, dev)
     if stats is not None:
         _need(stats, "stats", torch.int64, (2,))
-    rc = _load().backlite_mask(_ptr(tile_lse), _ptr(lse), B, H, n, int(causal), int(window), float(negl_prob),
-                               _ptr(out["keep"]), _ptr(out["qcnt"]), _ptr(out["qidx"]),
+    rc = _load().backlite_mask(_ptr(tile_lse), _ptr(lse), B, H, n, int(causal), int(window), int(q_tile),
+                               float(negl_prob), _ptr(out["keep"]), _ptr(out["qcnt"]), _ptr(out["qidx"]),
                                _ptr(out["kcnt"]), _ptr(out["kidx"]), _ptr(stats), _stream(dev))
     _check(rc, "backlite_mask")
     return out
 
 
-def mask_compact(tile_w, B, H, n, causal, negl_prob, stats=None, window=0, device=None):
+def mask_compact(tile_w, B, H, n, causal, negl_prob, stats=None, window=0, device=None, q_tile=TILE):
     """As mask(), from the compact statistics fwd(..., tile_w=) wrote."""
     dev = tile_w.device if tile_w is not None else device
     if tile_w is not None:
         _need(tile_w, "tile_w", torch.float64, (tile_w_elems(B, H, n, causal),))
-    T = ntiles(n)
-    out = {
-        "keep": torch.empty((B, H, T, T), dtype=torch.uint8, device=dev),
-        "qcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
-        "qidx": torch.empty((B, H, T, T), dtype=torch.int16, device=dev),
-        "kcnt": torch.empty((B, H, T), dtype=torch.int32, device=dev),
-        "kidx": torch.empty((B, H, T, T), dtype=torch.int16, device=dev),
-    }
+    out = _mask_outputs(B, H, n, q_tile, dev)
     if stats is not None:
         _need(stats, "stats", torch.int64, (2,))
-    rc = _load().backlite_mask_compact(_ptr(tile_w), B, H, n, int(causal), int(window), float(negl_prob),
-                                       _ptr(out["keep"]), _ptr(out["qcnt"]), _ptr(out["qidx"]),
+    rc = _load().backlite_mask_compact(_ptr(tile_w), B, H, n, int(causal), int(window), int(q_tile),
+                                       float(negl_prob), _ptr(out["keep"]), _ptr(out["qcnt"]), _ptr(out["qidx"]),
                                        _ptr(out["kcnt"]), _ptr(out["kidx"]), _ptr(stats), _stream(dev))
     _check(rc, "backlite_mask_compact")
     return out
@@ -204,8 +205,8 @@ def bwd_workspace_bytes(B, H, Hk, n, d) -> int:
     return int(_load().backlite_bwd_workspace_bytes(B, H, Hk, n, d))
 
 
-def bwd_workspace_bytes_stored(B, H, Hk, n, d, max_tiles) -> int:
-    return int(_load().backlite_bwd_workspace_bytes_stored(B, H, Hk, n, d, int(max_tiles)))
+def bwd_workspace_bytes_stored(B, H, Hk, n, d, max_tiles, q_tile=TILE) -> int:
+    return int(_load().backlite_bwd_workspace_bytes_stored(B, H, Hk, n, d, int(q_tile), int(max_tiles)))
 
 
 def bwd_state_offset(B, H, Hk, n, d) -> int:
@@ -240,52 +241,74 @@ def check_lists(qcnt, qidx, kcnt, kidx, B, H, n, causal, window=0, q_tile=TILE):
         raise BackliteError(f"backlite_check_lists: {msg.value.decode()}")
 
 
-def candidate_pairs(n: int, causal: bool, window: int = 0) -> int:
-    """Candidate (query tile, key tile) pairs of one (batch, head): all T*T, or
+def candidate_pairs(n: int, causal: bool, window: int = 0, q_tile: int = TILE) -> int:
+    """Candidate (query tile, key tile) pairs of one (batch, head): all Tq*T, or
     the causal triangle, or its band under a sliding window (integer bookkeeping
     for workspace sizes)."""
-    T = ntiles(n)
+    T, Tq = ntiles(n), ntiles(n, q_tile)
     if not causal:
-        return T * T
+        return Tq * T
     w = window if 0 < window < n else 0
     tot = 0
-    for qt in range(T):
-        first = qt * TILE - w + 1
-        lo = first // TILE if (w and first > 0) else 0
-        tot += qt - lo + 1
+    for qt in range(Tq):
+        first = qt * q_tile
+        last = min(n, first + q_tile) - 1
+        lo = (first - w + 1) // TILE if (w and first - w + 1 > 0) else 0
+        tot += last // TILE - lo + 1
     return tot
 
 
 # Default share of device memory given to stored-G_S slots when the caller
 # sets no budget.
 GS_BUDGET_FRACTION = 1 / 8
-SLOT_BYTES = TILE * TILE * 2 + 4 * TILE * 4
+def slot_bytes(q_tile: int = TILE) -> int:
+    """Bytes of one stored tile: bf16 G_S of q_tile x 128 and 4 x q_tile fp32 sums."""
+    return q_tile * TILE * 2 + 4 * q_tile * 4
 
 
-def gs_slots_for_budget(B, H, n, causal, window, budget_bytes, device) -> int:
+SLOT_BYTES = slot_bytes(TILE)
+
+
+def gs_slots_for_budget(B, H, n, causal, window, budget_bytes, device, q_tile=TILE) -> int:
     """Slots for a G_S budget in bytes (None: GS_BUDGET_FRACTION of the device's
     memory), never more than the candidate pairs: no device readback."""
     if budget_bytes is None:
         budget_bytes = int(torch.cuda.get_device_properties(device).total_memory * GS_BUDGET_FRACTION)
-    return max(0, min(B * H * candidate_pairs(n, causal, window), int(budget_bytes) // SLOT_BYTES))
+    return max(0, min(B * H * candidate_pairs(n, causal, window, q_tile), int(budget_bytes) // slot_bytes(q_tile)))
 
 
-def bwd_workspace(q, k, lists=None, stored_tiles="auto", causal=False, window=0, gs_budget_bytes=None) -> torch.Tensor:
+def bwd_workspace(q, k, lists=None, stored_tiles="auto", causal=False, window=0, gs_budget_bytes=None,
+                  q_tile=None) -> torch.Tensor:
     """A backward workspace.  stored_tiles: "auto" gives G_S slots for every
     candidate tile pair, capped by gs_budget_bytes (default: an eighth of the
     device's memory), without reading anything back from the device; an int
     gives that many slots; 0 gives the base workspace (G_Q recomputes P and
     G_S).  When the kept tiles outnumber the slots, the query tiles past the
-    slots recompute their G_Q (decided on the device)."""
+    slots recompute their G_Q (decided on the device).  q_tile: the lists'
+    query-tile rows (default: lists["q_tile"], else 128)."""
     B, n, H, d = q.shape
     Hk = k.shape[2]
+    if q_tile is None:
+        q_tile = lists.get("q_tile", TILE) if lists is not None else TILE
     base = bwd_workspace_bytes(B, H, Hk, n, d)
     if stored_tiles == "auto":
-        tiles = gs_slots_for_budget(B, H, n, causal, window, gs_budget_bytes, q.device)
+        tiles = gs_slots_for_budget(B, H, n, causal, window, gs_budget_bytes, q.device, q_tile)
     else:
         tiles = int(stored_tiles or 0)
-    size = bwd_workspace_bytes_stored(B, H, Hk, n, d, tiles) if tiles > 0 else base
+    size = bwd_workspace_bytes_stored(B, H, Hk, n, d, tiles, q_tile) if tiles > 0 else base
     return torch.empty(size, dtype=torch.uint8, device=q.device)
+
+
+def _check_lists_shapes(lists, B, H, n) -> int:
+    """The lists' query-tile rows (lists["q_tile"], default 128), after checking
+    the four arrays' dtypes and shapes."""
+    q_tile = int(lists.get("q_tile", TILE))
+    T, Tq = ntiles(n), ntiles(n, q_tile)
+    _need(lists["qcnt"], "qcnt", torch.int32, (B, H, Tq))
+    _need(lists["kcnt"], "kcnt", torch.int32, (B, H, T))
+    _need(lists["qidx"], "qidx", torch.int16, (B, H, Tq, T))
+    _need(lists["kidx"], "kidx", torch.int16, (B, H, T, Tq))
+    return q_tile
 
 
 def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, out=None, o_lo=None,
@@ -303,11 +326,7 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
     _need(lse, "lse", torch.float32, (B, H, n))
     if o_lo is not None:
         _need(o_lo, "o_lo", torch.bfloat16, (B, n, H, d))
-    T = ntiles(n)
-    _need(lists["qcnt"], "qcnt", torch.int32, (B, H, T))
-    _need(lists["kcnt"], "kcnt", torch.int32, (B, H, T))
-    _need(lists["qidx"], "qidx", torch.int16, (B, H, T, T))
-    _need(lists["kidx"], "kidx", torch.int16, (B, H, T, T))
+    q_tile = _check_lists_shapes(lists, B, H, n)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -318,7 +337,7 @@ def bwd(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, ou
     rc = _load().backlite_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
                               _ptr(lists["qcnt"]), _ptr(lists["qidx"]), _ptr(lists["kcnt"]),
                               _ptr(lists["kidx"]), B, n, H, Hk, d, scale, int(causal),
-                              int(window), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                              int(window), q_tile, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                               _stream(q.device))
     _check(rc, "backlite_bwd")
     return dq, dk, dv
@@ -352,11 +371,12 @@ def bwd_noalloc(q, k, v, o, do, lse, lists, out, scale=None, causal=False, o_lo=
     dq, dk, dv = out
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         _need(t, name, torch.bfloat16, tuple(ref.shape))
+    q_tile = _check_lists_shapes(lists, B, H, n)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     rc = _load().backlite_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
                                       _ptr(lists["qcnt"]), _ptr(lists["qidx"]), _ptr(lists["kcnt"]),
                                       _ptr(lists["kidx"]), B, n, H, Hk, d, scale, int(causal), int(window),
-                                      _ptr(dq), _ptr(dk), _ptr(dv), _stream(q.device))
+                                      q_tile, _ptr(dq), _ptr(dk), _ptr(dv), _stream(q.device))
     _check(rc, "backlite_bwd_noalloc")
     return dq, dk, dv
 

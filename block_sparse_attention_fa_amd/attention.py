@@ -28,7 +28,7 @@ from . import _lib
 
 class _BackLiteFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, scale, causal, negl_prob, tile_stats, stats_out, window, ws_cache):
+    def forward(ctx, q, k, v, scale, causal, negl_prob, tile_stats, stats_out, window, ws_cache, q_tile):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         tw = None
         if negl_prob > 0:
@@ -40,7 +40,7 @@ class _BackLiteFn(torch.autograd.Function):
         # the compact statistics live as long as the graph (autograd frees them
         # with it), so a second backward through the same graph finds them too
         ctx.save_for_backward(q, k, v, o, olo, lse, tw)
-        ctx.scale, ctx.causal, ctx.negl, ctx.window = scale, causal, negl_prob, window
+        ctx.scale, ctx.causal, ctx.negl, ctx.window, ctx.q_tile = scale, causal, negl_prob, window, q_tile
         ctx.stats_out = stats_out
         ctx.ws_cache = ws_cache
         ctx.mark_non_differentiable(lse)
@@ -52,11 +52,11 @@ class _BackLiteFn(torch.autograd.Function):
         n = q.shape[1]
         B, _, H, _ = q.shape
         lists = _lib.mask_compact(tw, B, H, n, ctx.causal, ctx.negl, stats=ctx.stats_out,
-                                  window=ctx.window, device=q.device)
-        ws = ctx.ws_cache.get(q, k, ctx.causal, ctx.window) if ctx.ws_cache is not None else None
+                                  window=ctx.window, device=q.device, q_tile=ctx.q_tile)
+        ws = ctx.ws_cache.get(q, k, ctx.causal, ctx.window, ctx.q_tile) if ctx.ws_cache is not None else None
         dq, dk, dv = _lib.bwd(q, k, v, o, do.contiguous(), lse, lists, scale=ctx.scale,
                               causal=ctx.causal, o_lo=olo, window=ctx.window, workspace=ws)
-        return dq, dk, dv, None, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None, None
 
 
 class _WorkspaceCache:
@@ -70,12 +70,12 @@ class _WorkspaceCache:
         self.gs_budget_bytes = gs_budget_bytes
         self._ws = {}
 
-    def get(self, q, k, causal, window):
-        key = (q.device, tuple(q.shape), k.shape[2], bool(causal), int(window))
+    def get(self, q, k, causal, window, q_tile):
+        key = (q.device, tuple(q.shape), k.shape[2], bool(causal), int(window), int(q_tile))
         ws = self._ws.get(key)
         if ws is None:
             ws = _lib.bwd_workspace(q, k, None, "auto", causal=causal, window=window,
-                                    gs_budget_bytes=self.gs_budget_bytes)
+                                    gs_budget_bytes=self.gs_budget_bytes, q_tile=q_tile)
             self._ws[key] = ws
         return ws
 
@@ -92,11 +92,16 @@ class BackLite(torch.nn.Module):
     workspace (None: an eighth of the device's memory, at most one slot per
     candidate tile pair).  The workspace is allocated on the first backward of
     a shape and reused.
+    q_tile: rows of the backward's query tiles, 128 or 64 (half-height tiles
+    give a finer mask: the README forms it "for each backward tile pair").
     """
 
     def __init__(self, negl_prob: float = 0.05, causal: bool = False, window: int = 0,
-                 gs_budget_bytes: int | None = None):
+                 gs_budget_bytes: int | None = None, q_tile: int = 128):
         super().__init__()
+        if q_tile not in (64, 128):
+            raise ValueError("q_tile must be 64 or 128")
+        self.q_tile = int(q_tile)
         if not (0.0 <= negl_prob < 1.0) or math.isnan(negl_prob):
             raise ValueError("negl_prob must be in [0, 1)")
         if window < 0 or (window > 0 and not causal):
@@ -119,13 +124,13 @@ class BackLite(torch.nn.Module):
             stats = torch.zeros(2, dtype=torch.int64, device=query.device)
             self.last_stats = stats
         o, lse = _BackLiteFn.apply(query, key, value, scale, causal, self.negl_prob, tile_stats, stats,
-                                   self.window if causal else 0, self.workspaces)
+                                   self.window if causal else 0, self.workspaces, self.q_tile)
         if return_softmax_lse:
             return o, lse
         return o
 
     def extra_repr(self) -> str:
-        return f"negl_prob={self.negl_prob}, causal={self.causal}, window={self.window}"
+        return f"negl_prob={self.negl_prob}, causal={self.causal}, window={self.window}, q_tile={self.q_tile}"
 
 
 def sparsity(stats: torch.Tensor) -> float:

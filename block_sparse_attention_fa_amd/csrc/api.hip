@@ -19,12 +19,12 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
                       int Hk, int d, float scale, int causal, int window, uint16_t* o, uint16_t* olo,
                       float* lse, float* tlse, double* tw, hipStream_t st);
 hipError_t launch_mask(const float* tlse, const double* tw, const float* lse, int B, int H, int n, int causal,
-                       int window, double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
-                       uint16_t* kidx, int64_t* stats, hipStream_t st);
+                       int window, int q_tile, double negl, uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
+                       int32_t* kcnt, uint16_t* kidx, int64_t* stats, hipStream_t st);
 hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                       const uint16_t* olo, const uint16_t* dout, const float* lse, const int32_t* qcnt,
                       const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
-                      int H, int Hk, int d, float scale, int causal, int window, uint16_t* dq,
+                      int H, int Hk, int d, float scale, int causal, int window, int q_tile, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
                       uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
                       float* dkpart, int dk_chmin, int dk_pcap, hipStream_t st);
@@ -55,6 +55,16 @@ int ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int ntiles(int n) { return (n + kTile - 1) / kTile; }
+int ntiles(int n, int tile) { return (n + tile - 1) / tile; }
+
+// Rows per backward query tile: 128 (the forward's tiles) or 64 (half-height
+// backward tiles, a finer mask; the README forms the mask "for each backward
+// tile pair", and a backward's tiles need not match the forward's).
+int check_q_tile(int q_tile) {
+  if (q_tile != 64 && q_tile != 128)
+    return fail(BACKLITE_ERR_UNSUPPORTED, "q_tile must be 64 or 128 (got %d)", q_tile);
+  return BACKLITE_OK;
+}
 
 // Shape checks shared by fwd and bwd.  Sizes must keep every element index of
 // the largest tensor below 2^62 and the grid below 2^31 workgroups.
@@ -121,15 +131,14 @@ size_t backlite_tile_lse_elems(int B, int H, int n, int causal) {
   return (size_t)B * H * pairs * kTile;
 }
 
-size_t backlite_mask_elems(int B, int H, int n) {
-  if (B < 1 || H < 1 || n < 1) return 0;
-  const size_t T = (size_t)ntiles(n);
-  return (size_t)B * H * T * T;
+size_t backlite_mask_elems(int B, int H, int n, int q_tile) {
+  if (B < 1 || H < 1 || n < 1 || (q_tile != 64 && q_tile != 128)) return 0;
+  return (size_t)B * H * ntiles(n, q_tile) * ntiles(n);
 }
 
-size_t backlite_count_elems(int B, int H, int n) {
-  if (B < 1 || H < 1 || n < 1) return 0;
-  return (size_t)B * H * ntiles(n);
+size_t backlite_count_elems(int B, int H, int n, int tile) {
+  if (B < 1 || H < 1 || n < 1 || (tile != 64 && tile != 128)) return 0;
+  return (size_t)B * H * ntiles(n, tile);
 }
 
 namespace {
@@ -157,19 +166,21 @@ size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d) {
 }
 
 namespace {
-constexpr size_t kSlotBytes = 128 * 128 * 2 + 4 * 128 * 4;  // bf16 G_S tile + residual sums
+// one stored tile: bf16 G_S of q_tile x 128 + fp32 residual sums [4][q_tile]
+size_t slot_bytes(int q_tile) { return (size_t)q_tile * 128 * 2 + 4 * (size_t)q_tile * 4; }
 constexpr size_t kStateBytes = 256;                          // gsinfo words
-// stored-path index arrays after the base workspace: state, qbase, kslot
-size_t gs_index_bytes(int B, int H, int n) {
-  const size_t T = (size_t)ntiles(n);
-  return kStateBytes + round256((size_t)B * H * T * 4) + round256((size_t)B * H * T * T * 4);
+// stored-path index arrays after the base workspace: state, qbase [B,H,Tq], kslot [B,H,T,Tq]
+size_t gs_index_bytes(int B, int H, int n, int q_tile) {
+  const size_t T = (size_t)ntiles(n), Tq = (size_t)ntiles(n, q_tile);
+  return kStateBytes + round256((size_t)B * H * Tq * 4) + round256((size_t)B * H * T * Tq * 4);
 }
 }  // namespace
 
-size_t backlite_bwd_workspace_bytes_stored(int B, int H, int H_k, int n, int d, int64_t max_tiles) {
+size_t backlite_bwd_workspace_bytes_stored(int B, int H, int H_k, int n, int d, int q_tile, int64_t max_tiles) {
   const size_t base = backlite_bwd_workspace_bytes(B, H, H_k, n, d);
   if (base == 0 || max_tiles < 1) return base;
-  return base + gs_index_bytes(B, H, n) + (size_t)max_tiles * kSlotBytes;
+  if (q_tile != 64 && q_tile != 128) return 0;
+  return base + gs_index_bytes(B, H, n, q_tile) + (size_t)max_tiles * slot_bytes(q_tile);
 }
 
 size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d) {
@@ -203,14 +214,15 @@ namespace {
 // Shared by backlite_mask (per-row statistics) and backlite_mask_compact
 // (tile_w); exactly one of tile_lse / tile_w is used, or neither with negl 0.
 int mask_impl(bool compact, const float* tile_lse, const double* tile_w, const float* lse_row, int B, int H,
-              int n, int causal, int window, float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
-              int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream) {
+              int n, int causal, int window, int q_tile, float negl_prob, uint8_t* keep, int32_t* qcnt,
+              uint16_t* qidx, int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream) {
   if (B < 1 || n < 1 || H < 1)
     return fail(BACKLITE_ERR_INVALID_ARG, "B, n, H must be >= 1 (got B=%d n=%d H=%d)", B, n, H);
   if (n > kMaxN) return fail(BACKLITE_ERR_UNSUPPORTED, "n = %d exceeds the supported maximum %d", n, kMaxN);
   if ((long long)B * H * ntiles(n) > 0x7fffffffLL)
     return fail(BACKLITE_ERR_INVALID_ARG, "B*H*ceil(n/128) exceeds 2^31");
   TRY(check_window(causal, window));
+  TRY(check_q_tile(q_tile));
   if (!std::isfinite(negl_prob) || negl_prob < 0.f || negl_prob >= 1.f)
     return fail(BACKLITE_ERR_INVALID_ARG, "negl_prob must be finite and in [0, 1) (got %g)",
                 (double)negl_prob);
@@ -225,16 +237,17 @@ int mask_impl(bool compact, const float* tile_lse, const double* tile_w, const f
   TRY(check_ptr(kcnt, "kcnt"));
   TRY(check_ptr(kidx, "kidx"));
   TRY(check_ptr(stats, "stats", true));
-  hipError_t e = backlite::launch_mask(tile_w ? nullptr : tile_lse, tile_w, lse_row, B, H, n, causal ? 1 : 0, window, (double)negl_prob,
-                                       keep, qcnt, qidx, kcnt, kidx, stats, (hipStream_t)stream);
+  hipError_t e = backlite::launch_mask(tile_w ? nullptr : tile_lse, tile_w, lse_row, B, H, n, causal ? 1 : 0, window,
+                                       q_tile, (double)negl_prob, keep, qcnt, qidx, kcnt, kidx, stats,
+                                       (hipStream_t)stream);
   int r = hip_status(e, "backlite_mask launch");
   if (r == BACKLITE_OK && verbose()) {
     // synchronous readback of the counts: a debugging aid, off by default
-    const size_t nq = (size_t)B * H * ntiles(n);
-    std::vector<int32_t> qc(nq), kc(nq);
+    const size_t nq = (size_t)B * H * ntiles(n, q_tile), nk = (size_t)B * H * ntiles(n);
+    std::vector<int32_t> qc(nq), kc(nk);
     long long hs[2] = {0, 0};
     e = hipMemcpyAsync(qc.data(), qcnt, nq * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(kc.data(), kcnt, nq * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(kc.data(), kcnt, nk * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
     if (e == hipSuccess && stats) e = hipMemcpyAsync(hs, stats, sizeof(hs), hipMemcpyDeviceToHost, (hipStream_t)stream);
     if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "BACKLITE_VERBOSE readback");
@@ -244,23 +257,26 @@ int mask_impl(bool compact, const float* tile_lse, const double* tile_w, const f
       kept += qc[i];
       qmin = std::min(qmin, (int)qc[i]);
       qmax = std::max(qmax, (int)qc[i]);
+    }
+    for (size_t i = 0; i < nk; ++i) {
       kmin = std::min(kmin, (int)kc[i]);
       kmax = std::max(kmax, (int)kc[i]);
     }
-    const int T = ntiles(n), w = (window > 0 && window < n) ? window : 0;
-    for (int qt = 0; qt < T; ++qt) {  // candidate key tiles per query tile
+    const int T = ntiles(n), Tq = ntiles(n, q_tile), w = (window > 0 && window < n) ? window : 0;
+    for (int qt = 0; qt < Tq; ++qt) {  // candidate key tiles per query tile
+      const int first = qt * q_tile, last = std::min(n, first + q_tile) - 1;
       int lo = 0, hi = T - 1;
-      if (causal) hi = qt;
-      if (w && qt * kTile - w + 1 > 0) lo = (qt * kTile - w + 1) / kTile;
+      if (causal) hi = last / kTile;
+      if (w && first - w + 1 > 0) lo = (first - w + 1) / kTile;
       cand += hi - lo + 1;
     }
     cand *= (long long)B * H;
     std::fprintf(stderr,
-                 "[backlite] mask B=%d H=%d n=%d causal=%d window=%d negl_prob=%g: kept %lld of %lld candidate "
-                 "tiles (density %.4f, sparsity %.4f); q-list length min %d mean %.1f max %d; k-list length min %d "
-                 "mean %.1f max %d",
-                 B, H, n, causal ? 1 : 0, w, (double)negl_prob, kept, cand, cand ? (double)kept / cand : 0.0,
-                 cand ? 1.0 - (double)kept / cand : 0.0, qmin, (double)kept / nq, qmax, kmin, (double)kept / nq,
+                 "[backlite] mask B=%d H=%d n=%d causal=%d window=%d q_tile=%d negl_prob=%g: kept %lld of %lld "
+                 "candidate tiles (density %.4f, sparsity %.4f); q-list length min %d mean %.1f max %d; k-list "
+                 "length min %d mean %.1f max %d",
+                 B, H, n, causal ? 1 : 0, w, q_tile, (double)negl_prob, kept, cand, cand ? (double)kept / cand : 0.0,
+                 cand ? 1.0 - (double)kept / cand : 0.0, qmin, (double)kept / nq, qmax, kmin, (double)kept / nk,
                  kmax);
     if (stats) std::fprintf(stderr, "; stats buffer (accumulated) %lld / %lld", hs[1], hs[0]);
     std::fprintf(stderr, "\n");
@@ -272,17 +288,17 @@ int mask_impl(bool compact, const float* tile_lse, const double* tile_w, const f
 extern "C" {
 
 int backlite_mask(const float* tile_lse, const float* lse_row, int B, int H, int n, int causal,
-                  int window, float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
-                  uint16_t* kidx, int64_t* stats, void* stream) {
-  return mask_impl(false, tile_lse, nullptr, lse_row, B, H, n, causal, window, negl_prob, keep, qcnt, qidx, kcnt,
-                   kidx, stats, stream);
+                  int window, int q_tile, float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
+                  int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream) {
+  return mask_impl(false, tile_lse, nullptr, lse_row, B, H, n, causal, window, q_tile, negl_prob, keep, qcnt, qidx,
+                   kcnt, kidx, stats, stream);
 }
 
-int backlite_mask_compact(const double* tile_w, int B, int H, int n, int causal, int window,
+int backlite_mask_compact(const double* tile_w, int B, int H, int n, int causal, int window, int q_tile,
                           float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx, int32_t* kcnt,
                           uint16_t* kidx, int64_t* stats, void* stream) {
-  return mask_impl(true, nullptr, tile_w, nullptr, B, H, n, causal, window, negl_prob, keep, qcnt, qidx, kcnt,
-                   kidx, stats, stream);
+  return mask_impl(true, nullptr, tile_w, nullptr, B, H, n, causal, window, q_tile, negl_prob, keep, qcnt, qidx,
+                   kcnt, kidx, stats, stream);
 }
 
 }  // extern "C"
@@ -292,10 +308,11 @@ namespace {
 int check_bwd_args(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
                    const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt,
                    const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k,
-                   int d, float scale, int causal, int window, uint16_t* dQ, uint16_t* dK, uint16_t* dV) {
+                   int d, float scale, int causal, int window, int q_tile, uint16_t* dQ, uint16_t* dK, uint16_t* dV) {
   TRY(check_shape(B, n, H, H_k, d));
   TRY(check_scale(scale));
   TRY(check_window(causal, window));
+  TRY(check_q_tile(q_tile));
   TRY(check_ptr(Q, "Q"));
   TRY(check_ptr(K, "K"));
   TRY(check_ptr(V, "V"));
@@ -328,14 +345,14 @@ int min_chunk() {
 int run_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O, const uint16_t* O_lo,
             const uint16_t* dO, const float* lse_row, const int32_t* qcnt, const uint16_t* qidx,
             const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k, int d, float scale, int causal,
-            int window, uint16_t* dQ, uint16_t* dK, uint16_t* dV, char* ws, int pcap, int32_t* gsinfo,
+            int window, int q_tile, uint16_t* dQ, uint16_t* dK, uint16_t* dV, char* ws, int pcap, int32_t* gsinfo,
             uint32_t* qbase, uint32_t* kslot, uint16_t* gs, float* gsl, long long cap, void* stream,
             const char* what) {
   const size_t kbar_off = 2 * delta_bytes(B, H, n);
   const size_t plan_off = kbar_off + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
   const size_t part_off = plan_off + dkplan_bytes(B, H_k, n);
   return hip_status(backlite::launch_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d,
-                                         scale, causal ? 1 : 0, window, dQ, dK, dV, (float*)ws,
+                                         scale, causal ? 1 : 0, window, q_tile, dQ, dK, dV, (float*)ws,
                                          (float*)(ws + delta_bytes(B, H, n)), (float*)(ws + kbar_off), gsinfo, qbase,
                                          kslot, gs, gsl, cap, (int32_t*)(ws + plan_off), (float*)(ws + part_off),
                                          min_chunk(), pcap, (hipStream_t)stream),
@@ -390,23 +407,24 @@ extern "C" {
 int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
                  const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt, const uint16_t* qidx,
                  const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k, int d,
-                 float scale, int causal, int window, uint16_t* dQ, uint16_t* dK, uint16_t* dV,
+                 float scale, int causal, int window, int q_tile, uint16_t* dQ, uint16_t* dK, uint16_t* dV,
                  void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_bwd_args(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window,
-                     dQ, dK, dV));
+                     q_tile, dQ, dK, dV));
   if (env_on("BACKLITE_CHECK")) {
     // validate copies of the lists on the host before anything is launched
-    const size_t T = (size_t)ntiles(n), nc = (size_t)B * H * T;
-    std::vector<int32_t> qc(nc), kc(nc);
-    std::vector<uint16_t> qi(nc * T), ki(nc * T);
-    hipError_t e = hipMemcpyAsync(qc.data(), qcnt, nc * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(kc.data(), kcnt, nc * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(qi.data(), qidx, nc * T * 2, hipMemcpyDeviceToHost, (hipStream_t)stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(ki.data(), kidx, nc * T * 2, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    const size_t T = (size_t)ntiles(n), Tq = (size_t)ntiles(n, q_tile);
+    const size_t nq = (size_t)B * H * Tq, nk = (size_t)B * H * T;
+    std::vector<int32_t> qc(nq), kc(nk);
+    std::vector<uint16_t> qi(nq * T), ki(nk * Tq);
+    hipError_t e = hipMemcpyAsync(qc.data(), qcnt, nq * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(kc.data(), kcnt, nk * 4, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(qi.data(), qidx, nq * T * 2, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(ki.data(), kidx, nk * Tq * 2, hipMemcpyDeviceToHost, (hipStream_t)stream);
     if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "BACKLITE_CHECK list readback");
     char msg[400];
-    if (backlite_check_lists(qc.data(), qi.data(), kc.data(), ki.data(), B, H, n, causal, window, kTile, msg,
+    if (backlite_check_lists(qc.data(), qi.data(), kc.data(), ki.data(), B, H, n, causal, window, q_tile, msg,
                              sizeof(msg)) != BACKLITE_OK)
       return fail(BACKLITE_ERR_INVALID_ARG, "BACKLITE_CHECK: %s", msg);
   }
@@ -422,20 +440,20 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
   uint16_t* gs = nullptr;
   float* gsl = nullptr;
   long long cap = 0;
-  const size_t idx = gs_index_bytes(B, H, n);
-  if (workspace_bytes >= need + idx + kSlotBytes) {
-    const size_t T = (size_t)ntiles(n);
-    cap = (long long)((workspace_bytes - need - idx) / kSlotBytes);
+  const size_t idx = gs_index_bytes(B, H, n, q_tile), sb = slot_bytes(q_tile);
+  if (workspace_bytes >= need + idx + sb) {
+    const size_t Tq = (size_t)ntiles(n, q_tile);
+    cap = (long long)((workspace_bytes - need - idx) / sb);
     if (cap > 0xffffffffLL) cap = 0xffffffffLL;  // slot indices are 32-bit
     gsinfo = (int32_t*)(ws + need);
     qbase = (uint32_t*)(ws + need + kStateBytes);
-    kslot = (uint32_t*)(ws + need + kStateBytes + round256((size_t)B * H * T * 4));
+    kslot = (uint32_t*)(ws + need + kStateBytes + round256((size_t)B * H * Tq * 4));
     gs = (uint16_t*)(ws + need + idx);
-    gsl = (float*)(ws + need + idx + (size_t)cap * 128 * 128 * 2);
+    gsl = (float*)(ws + need + idx + (size_t)cap * q_tile * 128 * 2);
   }
   const int NK = B * H_k * ntiles(n);
   const int r = run_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal,
-                        window, dQ, dK, dV, ws, NK, gsinfo, qbase, kslot, gs, gsl, cap, stream,
+                        window, q_tile, dQ, dK, dV, ws, NK, gsinfo, qbase, kslot, gs, gsl, cap, stream,
                         "backlite_bwd launch");
   if (r == BACKLITE_OK && verbose()) {
     // which G_Q path served the kept tiles (a synchronous readback, debugging only)
@@ -461,10 +479,10 @@ size_t backlite_bwd_noalloc_scratch_bytes(void) { return kScratchBytes; }
 int backlite_bwd_noalloc(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
                          const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt,
                          const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H,
-                         int H_k, int d, float scale, int causal, int window, uint16_t* dQ, uint16_t* dK,
-                         uint16_t* dV, void* stream) {
+                         int H_k, int d, float scale, int causal, int window, int q_tile, uint16_t* dQ,
+                         uint16_t* dK, uint16_t* dV, void* stream) {
   TRY(check_bwd_args(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window,
-                     dQ, dK, dV));
+                     q_tile, dQ, dK, dV));
   const long long pcap = noalloc_partial_slots(B, H, H_k, n, d);
   if (pcap < 1)
     return fail(BACKLITE_ERR_WORKSPACE,
@@ -473,8 +491,8 @@ int backlite_bwd_noalloc(const uint16_t* Q, const uint16_t* K, const uint16_t* V
                 B, H, H_k, n, d, kScratchBytes);
   char* ws = nullptr;
   TRY(scratch_for_current_device(&ws));
-  return run_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window, dQ,
-                 dK, dV, ws, (int)pcap, nullptr, nullptr, nullptr, nullptr, nullptr, 0, stream,
+  return run_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window,
+                 q_tile, dQ, dK, dV, ws, (int)pcap, nullptr, nullptr, nullptr, nullptr, nullptr, 0, stream,
                  "backlite_bwd_noalloc launch");
 }
 

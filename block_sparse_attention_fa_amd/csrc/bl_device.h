@@ -61,11 +61,14 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
 //                8 consecutive elements along the head dimension)
 //   tr pattern:  16-lane group g reads rows 32kb + 16st + 4*h32 + 8*half + i/4,
 //                columns 32db + 16(g%2) + 4(i%4) (ds_read_b64_tr_b16)
+//   db_shift: the tr offsets of column block db are those of block db + db_shift
+//   (a wave that works on a slice of the head dimension); blocks past D / 32
+//   are left unset.
 template <int D>
 struct LdsOffsets {
   int row[D / 16];
   int tr[2][D / 32];
-  __device__ __forceinline__ void init(int lane) {
+  __device__ __forceinline__ void init(int lane, int db_shift = 0) {
     const int l32 = lane & 31, h32 = lane >> 5, i = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) row[ks] = 2 * tile_off<D>(l32, 2 * ks + h32);
@@ -74,8 +77,8 @@ struct LdsOffsets {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int r = 4 * h32 + 8 * half + (i >> 2);
-        const int col = 32 * db + 16 * (g & 1) + 4 * (i & 3);
-        tr[half][db] = 2 * (tile_off<D>(r, col >> 3) + (col & 7));
+        const int col = 32 * (db + db_shift) + 16 * (g & 1) + 4 * (i & 3);
+        tr[half][db] = col < D ? 2 * (tile_off<D>(r, col >> 3) + (col & 7)) : 0;
       }
   }
 };

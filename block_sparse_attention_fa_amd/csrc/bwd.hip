@@ -145,7 +145,7 @@ __global__ __launch_bounds__(1024) void dk_plan_kernel(BwdArgs a) {
     const int kt = k % T, bg = k / T;
     const int g = bg % a.Hk, b = bg / a.Hk;
     int m = 0;
-    for (int hh = 0; hh < G; ++hh) m += max(0, min(a.kcnt[((long)b * a.H + g * G + hh) * T + kt], T));
+    for (int hh = 0; hh < G; ++hh) m += max(0, min(a.kcnt[((long)b * a.H + g * G + hh) * T + kt], a.Tq));
     items[k] = m;
     sum += m;
   }
@@ -312,14 +312,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                       const uint16_t* olo, const uint16_t* dout, const float* lse, const int32_t* qcnt,
                       const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n,
-                      int H, int Hk, int d, float scale, int causal, int window, uint16_t* dq,
+                      int H, int Hk, int d, float scale, int causal, int window, int q_tile, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
                       uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
                       float* dkpart, int dk_chmin, int dk_pcap, hipStream_t st) {
   BwdArgs a{q,    k,      v,     o,     olo,    dout,   lse,      qcnt, qidx, kcnt, kidx, dq,
             dk,   dv,     dbuf,  lse2,  kbar,   gsinfo, qbase,    kslot, gs, gsl, gs_cap, dkplan,
-            dkpart, dk_chmin, dk_pcap, B, n, H, Hk, (n + TILE - 1) / TILE, window < n ? window : 0, scale,
-            scale * LOG2E};
+            dkpart, dk_chmin, dk_pcap, B, n, H, Hk, (n + TILE - 1) / TILE, (n + q_tile - 1) / q_tile, q_tile,
+            window < n ? window : 0, scale, scale * LOG2E};
   if (d == 64) return causal ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
   return causal ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
 }

@@ -25,10 +25,10 @@ struct BwdArgs {
   float* kbar;  // per key tile mean of K over its valid keys, [B, Hk, T, d]
   // Stored-G_S state (all NULL when the workspace holds no slots).
   int32_t* gsinfo;     // [0] 1 = every kept tile had a slot, [1] kept tiles, [2] kept tiles with a slot
-  uint32_t* qbase;     // [B, H, T]: first slot of each query tile's kept tiles
-  uint32_t* kslot;     // [B, H, T, T]: slot of each k-list entry, laid out like kidx
-  uint16_t* gs;        // slots of 128 x 128 bf16 G_S
-  float* gsl;          // per slot, [4 key quarters][128 rows] sums of the G_S rounding residual
+  uint32_t* qbase;     // [B, H, Tq]: first slot of each query tile's kept tiles
+  uint32_t* kslot;     // [B, H, T, Tq]: slot of each k-list entry, laid out like kidx
+  uint16_t* gs;        // slots of qrows x 128 bf16 G_S
+  float* gsl;          // per slot, [4 key quarters][qrows rows] sums of the G_S rounding residual
   long long gs_cap;    // slots available
   // Chunked G_K/G_V work (always present): header [4] = {chunks, partial slots,
   // chunk length, -}, then the chunk table int4 [2 * NK] = {key tile (b, g, kt)
@@ -39,7 +39,8 @@ struct BwdArgs {
   float* dkpart;       // partial G_K, G_V of split key tiles: [slot][2][128][d] fp32, NK slots
   int dk_chmin;        // smallest chunk length
   int dk_pcap;         // partial slots available (<= NK); bounds the number of split chunks
-  int B, n, H, Hk, T;
+  int B, n, H, Hk, T;  // T: key tiles of 128 keys
+  int Tq, qrows;       // query tiles of the lists and their rows (128, or 64: half-height backward tiles)
   int window;          // sliding window (causal only): key j visible to row i iff i - window < j; 0 = none
   float scale;
   float scale_log2;

@@ -16,41 +16,51 @@
 
 namespace backlite {
 
-// Sources of query tile qt of head h (Q, G_O rows; LSE, D words) as buffer
-// resources whose range ends after the last valid row: the rows of the ragged
-// last tile, and every row when `valid` is false, read as zero.  Zero rows
-// contribute nothing to G_K and G_V (their G_O and D are zero), so no other
-// padding is needed.
+// Sources of query tile qt (of a.qrows rows) of head h (Q, G_O rows; LSE, D
+// words) as buffer resources whose range ends after the last valid row: the
+// rows of the ragged last tile, and every row when `valid` is false, read as
+// zero.  Zero rows contribute nothing to G_K and G_V (their G_O and D are
+// zero), so no other padding is needed.  With shift = 64 the resources start 64
+// rows before the tile, so that the copy offsets of stage rows 64..127 land on
+// the tile's rows 0..63 (the second 64-row item of a visit); offsets below the
+// shift are never issued for it.
 struct QgSrc {
   __amdgpu_buffer_rsrc_t q, g, l, d;
 };
 template <int D>
-__device__ __forceinline__ QgSrc qg_src(const BwdArgs& a, long bh, int b, int h, int qt, bool valid) {
+__device__ __forceinline__ QgSrc qg_src(const BwdArgs& a, long bh, int b, int h, int qt, bool valid, int shift) {
   const int n = a.n;
   const long qstride = (long)a.H * D;
-  const int q0 = qt * TILE;
+  const int q0 = qt * a.qrows;
   // list entries past the last tile (a malformed list) read as empty tiles
-  const uint32_t rows = (valid && q0 < n) ? (uint32_t)min(TILE, n - q0) : 0u;
-  const long off = ((long)b * n + q0) * qstride + (long)h * D;
-  const uint32_t bytes = rows * (uint32_t)qstride * 2u;
+  const uint32_t rows = (valid && q0 < n) ? (uint32_t)min(a.qrows, n - q0) : 0u;
+  const long r0 = (long)q0 - shift;
+  const long off = ((long)b * n + r0) * qstride + (long)h * D;
+  const uint32_t bytes = (rows + (uint32_t)shift) * (uint32_t)qstride * 2u;
+  const uint32_t words = (rows + (uint32_t)shift) * 4u;
   return QgSrc{buffer_rsrc(a.q + off, bytes), buffer_rsrc(a.dout + off, bytes),
-               buffer_rsrc(a.lse2 + bh * n + q0, rows * 4u), buffer_rsrc(a.dbuf + bh * n + q0, rows * 4u)};
+               buffer_rsrc(a.lse2 + bh * n + r0, words), buffer_rsrc(a.dbuf + bh * n + r0, words)};
 }
 
-// LSE and D words of a staged query tile: one instruction each, waves 0 and 1
-__device__ __forceinline__ void stage_ld(float* Ld, float* Dd, const QgSrc& s, int wave, int lane) {
+// LSE and D words of a staged unit: one instruction each for stage rows 0..63
+// (from sa) and 64..127 (from sb, the same source for a 128-row item), waves 0
+// and 1
+__device__ __forceinline__ void stage_ld(float* Ld, float* Dd, const QgSrc& sa, const QgSrc& sb, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < TILE / 64; ++i) {
+    const QgSrc& s = i ? sb : sa;
     if (wave == 0) load_lds4<true>(s.l, nullptr, lds_ptr(Ld + 64 * i), (uint32_t)(64 * i + lane) * 4u);
     if (wave == 1) load_lds4<true>(s.d, nullptr, lds_ptr(Dd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
   }
 }
 
-// Copy instruction i (of 2 NI) of a staged query tile: Q rows, then G_O rows.
+// Copy instruction i (of 2 NI) of a staged unit: Q rows, then G_O rows; the
+// instructions of stage rows 64..127 read from sb.
 template <int D, int NT, int I>
-__device__ __forceinline__ void stage_qg_part(bf16* Qd, bf16* Gd, const QgSrc& s, const DmaOffsets<D, NT>& dmo,
-                                              int wave) {
+__device__ __forceinline__ void stage_qg_part(bf16* Qd, bf16* Gd, const QgSrc& sa, const QgSrc& sb,
+                                              const DmaOffsets<D, NT>& dmo, int wave) {
   constexpr int NI = DmaOffsets<D, NT>::NI, II = I % NI;
+  const QgSrc& s = II < NI / 2 ? sa : sb;  // instruction II covers stage rows 64 II / (NI / 2) ..
   lds_byte* dst = lds_ptr((I < NI ? Qd : Gd) + ((II * (NT / 64) + wave) * 64) * 8);
   load_lds16<true>(I < NI ? s.q : s.g, nullptr, dst, dmo.off[II]);
 }
@@ -78,8 +88,10 @@ constexpr int DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141, DPP_XOR2 = 0x
 // One workgroup of 4 waves (one per SIMD, so each wave may hold up to 512
 // registers) per (b, kv head g, key tile kt).  Wave w owns keys 32w .. +31 of
 // the tile; their K, V fragments and G_K, G_V accumulators stay in registers.
-// The next listed query tile is copied into the other LDS stage while the
-// current one is consumed.
+// A visit consumes one unit of 128 query rows in four 32-row chunks: one
+// 128-row query tile, or, with 64-row backward query tiles, two consecutive
+// list items (chunks 0-1 from the first, 2-3 from the second).  The next unit
+// is copied into the other LDS stage while the current one is consumed.
 //
 // The GS variant runs whenever the workspace carries G_S slots (a.gsinfo !=
 // NULL); tiles whose slot index is past the capacity are computed without
@@ -171,11 +183,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     int p0 = 0;
     for (int hh = 0; hh < G && p0 < f1; ++hh) {
       const long row = ((bh0 + hh) * T + kt);
-      const int c = max(0, min(a.kcnt[row], T));  // as dk_plan_kernel counts it
+      const int c = max(0, min(a.kcnt[row], a.Tq));  // as dk_plan_kernel counts it
       const int lo_p = max(f0, p0), hi_p = min(f1, p0 + c);
       for (int p = lo_p + tid; p < hi_p; p += NT) {
-        itab[p - f0] = ((uint32_t)hh << 16) | a.kidx[row * T + (p - p0)];
-        if constexpr (GS) stab[p - f0] = a.kslot[row * T + (p - p0)];
+        itab[p - f0] = ((uint32_t)hh << 16) | a.kidx[row * a.Tq + (p - p0)];
+        if constexpr (GS) stab[p - f0] = a.kslot[row * a.Tq + (p - p0)];
       }
       p0 += c;
     }
@@ -193,19 +205,35 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     if constexpr (GS) s = __builtin_amdgcn_readfirstlane(stab[p - ibase]);
     return Item{(int)(e >> 16), (int)(e & 0xFFFFu), s};
   };
-  Item it_cur = item_at(0);
-  // Stored-G_S constants.  Slot layout (32 KB of bf16): 1 KB blocks
-  // ((kw * 4 + chunk) * 2 + s), each the 64 lanes' 16-byte operands sk[s] of
-  // that wave and chunk, lane (h32, l32) at position 2 * l32 + h32.  Row sums
-  // (2 KB of fp32 per slot): [kw][query row of the tile], the fp32 G_S summed
-  // over the wave's 32 keys; the G_Q pass subtracts the sums of the bf16 values
-  // it reads to get the rounding residual's row sums.  After the butterfly in
-  // the tile's B phases, lane (bits b0..b5) holds the sum for query row
-  // 16 b3 + 8 b2 + 4 b5 + 2 b1 + b4 of the chunk; odd lanes hold a copy and
-  // store out of range (dropped).  The stores of chunk 3 are issued after the
-  // next tile's barrier (or after the last tile): issued at the end of a tile
-  // they would still be in flight at the next tile's wait for its staged
-  // operands, which counts stores too.
+  // units of 128 stage rows: one item of 128 rows, or two of 64 (see above)
+  const bool half = a.qrows == 64;
+  const int QR = a.qrows, CPI = QR / 32;  // rows and 32-row chunks per item
+  const int nunits = half ? (nitems + 1) / 2 : nitems;
+  constexpr uint32_t NO_SLOT = 0xFFFFFFFFu;  // never below the capacity: stores dropped
+  Item A_cur = item_at(0);
+  bool vB_cur = half && nitems > 1;
+  Item B_cur = vB_cur ? item_at(1) : A_cur;
+  // Stored-G_S constants.  Slot layout (QR x 128 bf16): 1 KB blocks
+  // ((kw * CPI + chunk of the item) * 2 + s), each the 64 lanes' 16-byte
+  // operands sk[s] of that wave and chunk, lane (h32, l32) at position
+  // 2 * l32 + h32.  Row sums (4 QR fp32 per slot): [kw][query row of the item],
+  // the fp32 G_S summed over the wave's 32 keys; the G_Q pass subtracts the
+  // sums of the bf16 values it reads to get the rounding residual's row sums.
+  // After the butterfly in the unit's B phases, lane (bits b0..b5) holds the
+  // sum for query row 16 b3 + 8 b2 + 4 b5 + 2 b1 + b4 of the chunk; odd lanes
+  // hold a copy and store out of range (dropped).  The stores of chunk 3 (the
+  // last chunk of its item) are issued after the next unit's barrier (or after
+  // the last unit): issued at the end of a unit they would still be in flight
+  // at the next unit's wait for its staged operands, which counts stores too.
+  const uint32_t slot_elems = (uint32_t)QR * TILE, slot_sums = 4u * QR;
+  auto gs_rsrc = [&](uint32_t slot) {
+    const bool ok = GS && (long long)slot < a.gs_cap;
+    return buffer_rsrc(GS && ok ? a.gs + (size_t)slot * slot_elems : nullptr, ok ? slot_elems * 2u : 0u);
+  };
+  auto gsl_rsrc = [&](uint32_t slot) {
+    const bool ok = GS && (long long)slot < a.gs_cap;
+    return buffer_rsrc(GS && ok ? a.gsl + (size_t)slot * slot_sums : nullptr, ok ? slot_sums * 4u : 0u);
+  };
 
   const uint32_t gs_voff = (uint32_t)(2 * l32 + h32) * 16u;
   const uint32_t ls_q = 16 * ((lane >> 3) & 1) + 8 * ((lane >> 2) & 1) + 4 * (lane >> 5) + 2 * ((lane >> 1) & 1) +
@@ -213,22 +241,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   const bool sel3 = (lane >> 3) & 1, sel2 = (lane >> 2) & 1, sel1 = (lane >> 1) & 1;
   bf16x8 pk[2][2], sk[2][2];  // packed bf16 P and G_S operands [chunk parity][sub-step]
   float bw_def = 0.f;             // row sums of chunk 3 awaiting their store
-  bool def_pending = false;       // chunk 3 of the previous tile not stored yet
+  bool def_pending = false;       // chunk 3 of the previous unit not stored yet
   uint32_t def_slot = 0;
-  // stores of chunk 3 of the tile in slot `slot` (its operands are still in sk[1])
+  // stores of chunk 3 (the last chunk of its item) in slot `slot` (its
+  // operands are still in sk[1])
   auto store_late = [&](uint32_t slot) {
-    const bool ok = (long long)slot < a.gs_cap;
-    const __amdgpu_buffer_rsrc_t r1 = buffer_rsrc(a.gs + (size_t)slot * (TILE * TILE), ok ? TILE * TILE * 2u : 0u);
-    const __amdgpu_buffer_rsrc_t r2 = buffer_rsrc(a.gsl + (size_t)slot * (4 * TILE), ok ? 4u * TILE * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t r1 = gs_rsrc(slot), r2 = gsl_rsrc(slot);
+    const int ci = CPI - 1;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sk[1][s2]), r1, gs_voff,
-                                             (kw * 8 + 3 * 2 + s2) * 1024, CPOL_NT);
-    const uint32_t off = (lane & 1) ? 0x40000000u : (uint32_t)(kw * TILE + 32 * 3 + ls_q) * 4u;
+                                             ((kw * CPI + ci) * 2 + s2) * 1024, CPOL_NT);
+    const uint32_t off = (lane & 1) ? 0x40000000u : (uint32_t)(kw * QR + 32 * ci + ls_q) * 4u;
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, bw_def), r2, off, 0, CPOL_NT);
   };
-  // stage S (a compile-time 0 or 1) holds item j; the other stage receives j + 1
-  auto visit = [&](int j, auto stage) {
+  // stage S (a compile-time 0 or 1) holds unit u; the other stage receives u + 1
+  auto visit = [&](int u, auto stage) {
     constexpr int S = decltype(stage)::value;
     const bf16* Qc = S ? Qs1 : Qs0;
     const bf16* Gc = S ? Gs1 : Gs0;
@@ -238,40 +266,39 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     bf16* Gn = S ? Gs0 : Gs1;
     float* Ln = S ? Ls0 : Ls1;
     float* Dn = S ? Ds0 : Ds1;
-    const int qt = it_cur.qt;
     wait_vmem();
-    __syncthreads();  // item j staged in (Qc, Gc, Lc, Dc); stage n is free
-    if (j + 1 >= ibase + ITAB && j + 1 < nitems) {  // slide the item window
+    __syncthreads();  // unit u staged in (Qc, Gc, Lc, Dc); stage n is free
+    const int jn = half ? 2 * (u + 1) : u + 1;  // first item of the next unit
+    if (jn >= ibase + ITAB && jn < nitems) {     // slide the item window (ITAB is even)
       ibase += ITAB;
       fill_items(ibase);
       __syncthreads();
     }
-    const Item it_nxt = (j + 1 < nitems) ? item_at(j + 1) : it_cur;
+    const bool vA_nxt = jn < nitems, vB_nxt = half && jn + 1 < nitems;
+    const Item A_nxt = vA_nxt ? item_at(jn) : A_cur;
+    const Item B_nxt = vB_nxt ? item_at(jn + 1) : A_nxt;
+    // slots of the current unit's items (a missing second item stores nothing)
+    const uint32_t slotA = A_cur.slot, slotB = half ? (vB_cur ? B_cur.slot : NO_SLOT) : A_cur.slot;
     if constexpr (GS) {
       if (def_pending) store_late(def_slot);
       def_pending = true;
-      def_slot = it_cur.slot;
+      def_slot = slotB;
     }
-    // Stage item j + 1 into the free stage: its LSE and D words now, its Q and
+    // Stage unit u + 1 into the free stage: its LSE and D words now, its Q and
     // G_O rows one copy instruction every few MFMAs in the first part of this
-    // tile's stream (issued back to back they would stall the wave: the copy
+    // unit's stream (issued back to back they would stall the wave: the copy
     // pipeline holds few requests while rows stream in from HBM).  Without a
     // next item the copies read nothing and land zeros in the free stage.
-    const QgSrc nsrc = qg_src<D>(a, bh0 + it_nxt.hh, b, (int)(g * G + it_nxt.hh), it_nxt.qt, j + 1 < nitems);
-    stage_ld(Ln, Dn, nsrc, wave, lane);
-    const int q0 = qt * TILE;
-    // on the diagonal tile a query row drops keys after it
-    const bool diag = CAUSAL && qt == kt;
-    // with a sliding window, a tile holding keys <= some row - window drops them
-    const bool wedge = CAUSAL && a.window != 0 && kt * TILE <= q0 + TILE - 1 - a.window;
-    const int lim0 = key - (q0 + 4 * h32);
-    // the tile's slot; a slot index past the capacity (lists that disagree)
+    const QgSrc nsrcA = qg_src<D>(a, bh0 + A_nxt.hh, b, (int)(g * G + A_nxt.hh), A_nxt.qt, vA_nxt, 0);
+    const QgSrc nsrcB =
+        half ? qg_src<D>(a, bh0 + B_nxt.hh, b, (int)(g * G + B_nxt.hh), B_nxt.qt, vB_nxt, 64) : nsrcA;
+    stage_ld(Ln, Dn, nsrcA, nsrcB, wave, lane);
+    // first rows of the unit's items; chunk cs covers rows row0(cs) .. +31
+    const int q0A = A_cur.qt * QR, q0B = B_cur.qt * QR;
+    // the items' slots; a slot index past the capacity (lists that disagree)
     // gets empty ranges, so its stores are dropped
-    const bool slot_ok = GS && (long long)it_cur.slot < a.gs_cap;
-    const __amdgpu_buffer_rsrc_t gsr =
-        buffer_rsrc(GS ? a.gs + (size_t)it_cur.slot * (TILE * TILE) : nullptr, slot_ok ? TILE * TILE * 2u : 0u);
-    const __amdgpu_buffer_rsrc_t lsr =
-        buffer_rsrc(GS ? a.gsl + (size_t)it_cur.slot * (4 * TILE) : nullptr, slot_ok ? 4u * TILE * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t gsrA = gs_rsrc(slotA), lsrA = gsl_rsrc(slotA);
+    const __amdgpu_buffer_rsrc_t gsrB = gs_rsrc(slotB), lsrB = gsl_rsrc(slotB);
     // One tile: A(c) forms S and G_P of query chunk c (32 rows), B(c)
     // accumulates G_V and G_K from chunk c's P and G_S, in the order of
     // TileSched; chunk c's softmax (exp, mask, G_S) is spread over the MFMAs
@@ -303,17 +330,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       constexpr int k = decltype(kc)::value, ph = SC::phase_of(k), st = k - SC::start(ph), c4 = SC::chunk(ph);
       if constexpr (k + AHEAD < NSTEP)
         ring[(k + AHEAD) % RING] = fetch(std::integral_constant<int, k + AHEAD>{});
-      if constexpr (k % DSTEP == 0 && k / DSTEP < 2 * NI) stage_qg_part<D, NT, k / DSTEP>(Qn, Gn, nsrc, dmo, wave);
+      if constexpr (k % DSTEP == 0 && k / DSTEP < 2 * NI)
+        stage_qg_part<D, NT, k / DSTEP>(Qn, Gn, nsrcA, nsrcB, dmo, wave);
       if constexpr (st == 0 && !SC::is_b(ph)) {
         sacc[c4 & 1] = f32x16{};
         gacc[c4 & 1] = f32x16{};
       }
       if constexpr (GS && SC::is_b(ph) && st == 0 && c4 < 3) {
-        // chunk c4's bf16 G_S operands to the tile's slot
+        // chunk c4's bf16 G_S operands to its item's slot
+        const int ci = half ? (c4 & 1) : c4;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sk[c4 & 1][s2]), gsr, gs_voff,
-                                                 (kw * 8 + c4 * 2 + s2) * 1024, CPOL_NT);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sk[c4 & 1][s2]), c4 >= 2 ? gsrB : gsrA,
+                                                 gs_voff, ((kw * CPI + ci) * 2 + s2) * 1024, CPOL_NT);
       }
       static_for<0, 4>([&](auto cc) {
         constexpr int cs = decltype(cc)::value;
@@ -368,8 +397,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
             } else {
               bw += dpp<DPP_XOR1>(bw);
               if constexpr (c4 < 3) {
-                const uint32_t off = (lane & 1) ? 0x40000000u : (uint32_t)(kw * TILE + 32 * c4 + ls_q) * 4u;
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, bw), lsr, off, 0, CPOL_NT);
+                const int ci = half ? (c4 & 1) : c4;
+                const uint32_t off = (lane & 1) ? 0x40000000u : (uint32_t)(kw * QR + 32 * ci + ls_q) * 4u;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, bw), c4 >= 2 ? lsrB : lsrA, off, 0,
+                                                      CPOL_NT);
               } else {
                 bw_def = bw;
               }
@@ -383,16 +414,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
         f32x16& gv = gacc[cs & 1];
         if constexpr (SC::soft_begin(cs) == k) {
           if constexpr (CAUSAL) {
-            // on the diagonal tile a query drops the keys after it: score -inf,
-            // so P = 0 there; only that tile takes this branch
+            // rows row0 .. row0+31 of this chunk drop the keys after them (score
+            // -inf, so P = 0), and with a sliding window the keys <= row -
+            // window; only chunks that reach such keys take this branch
+            const int row0 = half ? (cs < 2 ? q0A : q0B) + 32 * (cs & 1) : q0A + 32 * cs;
+            const bool diag = kt * TILE + TILE - 1 > row0;
+            const bool wedge = a.window != 0 && kt * TILE <= row0 + 31 - a.window;
             if (diag || wedge) {
-              // keep query offsets in [lim0, limw) - 32cs: at or after the key, and
-              // before key + window
-              const int limw = wedge ? lim0 + a.window : (1 << 30);
+              // keep query offsets in [lim, limw): at or after the key, and before
+              // key + window
+              const int lim = key - (row0 + 4 * h32);
+              const int limw = wedge ? lim + a.window : (1 << 30);
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int off = 8 * (r >> 2) + (r & 3);
-                sv[r] = (off >= lim0 - cs * 32 && off < limw - cs * 32) ? sv[r] : -INFINITY;
+                sv[r] = (off >= lim && off < limw) ? sv[r] : -INFINITY;
               }
             }
           } else if constexpr (RAGGED) {
@@ -421,23 +457,27 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    it_cur = it_nxt;
+    A_cur = A_nxt;
+    B_cur = B_nxt;
+    vB_cur = vB_nxt;
   };
 
   {
-    const QgSrc s0 = qg_src<D>(a, bh0 + it_cur.hh, b, (int)(g * G + it_cur.hh), it_cur.qt, nitems > 0);
-    stage_ld(Ls0, Ds0, s0, wave, lane);
-    static_for<0, 2 * DmaOffsets<D, NT>::NI>([&](auto ic) { stage_qg_part<D, NT, decltype(ic)::value>(Qs0, Gs0, s0, dmo, wave); });
+    const QgSrc s0 = qg_src<D>(a, bh0 + A_cur.hh, b, (int)(g * G + A_cur.hh), A_cur.qt, nitems > 0, 0);
+    const QgSrc s1 = half ? qg_src<D>(a, bh0 + B_cur.hh, b, (int)(g * G + B_cur.hh), B_cur.qt, vB_cur, 64) : s0;
+    stage_ld(Ls0, Ds0, s0, s1, wave, lane);
+    static_for<0, 2 * DmaOffsets<D, NT>::NI>(
+        [&](auto ic) { stage_qg_part<D, NT, decltype(ic)::value>(Qs0, Gs0, s0, s1, dmo, wave); });
   }
-  // pairs of items (stage 0, then stage 1), then the odd one out: no branch
+  // pairs of units (stage 0, then stage 1), then the odd one out: no branch
   // between the two visits of an iteration, so the accumulators keep one
   // register assignment around the loop
   int j = 0;
-  for (; j + 1 < nitems; j += 2) {
+  for (; j + 1 < nunits; j += 2) {
     visit(j, std::integral_constant<int, 0>{});
     visit(j + 1, std::integral_constant<int, 1>{});
   }
-  if (j < nitems) visit(j, std::integral_constant<int, 0>{});
+  if (j < nunits) visit(j, std::integral_constant<int, 0>{});
   if constexpr (GS) {
     if (def_pending) store_late(def_slot);
   }

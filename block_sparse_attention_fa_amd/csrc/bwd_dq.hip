@@ -51,6 +51,13 @@ __device__ __forceinline__ void stage_kbar(float* Bd, const KvSrc& s, int wave, 
 // owns query rows 32w .. +31: their Q, G_O fragments and the G_Q^T accumulator
 // stay in registers.  The next listed key tile is copied into the other LDS
 // stage while the current one is consumed.
+//
+// With 64-row backward query tiles the workgroup still covers 128 rows (the
+// tiles 2p and 2p+1: waves 0-1 and 2-3) and walks the union of the two
+// q-lists, each entry flagged with the halves that keep it; a wave pair whose
+// half does not keep the tile only issues its share of the staging copies.
+// A half whose G_Q comes from stored G_S (dqs_kernel) is skipped entirely and
+// its rows are not written here.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   constexpr int NT = 256;
@@ -62,7 +69,9 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE * D];
   __shared__ __attribute__((aligned(16))) float Kb0[D];
   __shared__ __attribute__((aligned(16))) float Kb1[D];
-  __shared__ uint16_t itab[MAX_TILES];  // this query tile's q-list
+  __shared__ uint32_t itab[MAX_TILES];  // q-list (union of both halves): kt | halves keeping it << 16
+  __shared__ uint8_t fl[2][MAX_TILES];  // 64-row tiles: which half keeps each key tile
+  __shared__ int red[NT / 64];
 
   const int T = a.T, n = a.n;
   const int L = work_index(blockIdx.x);
@@ -105,20 +114,80 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   // with G_S slots, the query tiles whose kept tiles all have a slot take G_Q
   // from the stored tiles (dqs_kernel); only the others are recomputed here
   if (a.gsinfo != nullptr && a.gsinfo[0] != 0) return;  // every tile had a slot
-  const int cnt = max(0, min(a.qcnt[(long)bh * T + qt], T));
-  if (a.gsinfo != nullptr && (long long)a.qbase[(long)bh * T + qt] + cnt <= a.gs_cap) return;
-  {
+  const bool split = a.qrows != TILE;                     // two 64-row query tiles
+  const int Tq = a.Tq;
+  int cnt_h[2] = {0, 0};
+  bool mine_h[2] = {false, false};                        // half recomputed here
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int t = split ? 2 * qt + hf : qt;
+    if ((split || hf == 0) && t < Tq) {
+      const long bq = (long)bh * Tq + t;
+      cnt_h[hf] = max(0, min(a.qcnt[bq], T));
+      mine_h[hf] = a.gsinfo == nullptr || (long long)a.qbase[bq] + cnt_h[hf] > a.gs_cap;
+    }
+  }
+  if (!split) mine_h[1] = mine_h[0];
+  if (!mine_h[0] && !mine_h[1]) return;
+  int cnt;
+  if (!split) {
     // the q-list in LDS: reading the next key tile is then an LDS read, not a
     // global load whose latency would stall the wave before the next copy
-    const uint16_t* list = a.qidx + ((long)bh * T + qt) * T;
-    for (int i = tid; i < cnt; i += NT) itab[i] = list[i];
+    cnt = cnt_h[0];
+    const uint16_t* list = a.qidx + ((long)bh * Tq + qt) * T;
+    for (int i = tid; i < cnt; i += NT) itab[i] = list[i] | (3u << 16);
+  } else {
+    // union of the two halves' lists (only halves recomputed here), in kt order
+    for (int i = tid; i < T; i += NT) fl[0][i] = fl[1][i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      if (!mine_h[hf]) continue;
+      const uint16_t* list = a.qidx + ((long)bh * Tq + 2 * qt + hf) * T;
+      for (int i = tid; i < cnt_h[hf]; i += NT) {
+        const int kt = list[i];
+        if (kt < T) fl[hf][kt] = 1;
+      }
+    }
+    __syncthreads();
+    constexpr int PER = MAX_TILES / NT;
+    int f[PER], m = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int kt = tid * PER + u;
+      f[u] = kt < T ? (fl[0][kt] | (fl[1][kt] << 1)) : 0;
+      m += f[u] != 0;
+    }
+    // block-wide exclusive scan of m
+    int x = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) red[wave] = x;
+    __syncthreads();
+    int base = 0;
+    cnt = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      const int r = red[w];
+      if (w < wave) base += r;
+      cnt += r;
+    }
+    int pos = base + x - m;
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (f[u]) itab[pos++] = (uint32_t)(tid * PER + u) | ((uint32_t)f[u] << 16);
   }
   LdsOffsets<D> lo;
   lo.init(lane);
   DmaOffsets<D, NT> dmo;
   dmo.init(kvstride, tid);
   __syncthreads();
-  int kt_cur = (cnt > 0) ? (int)__builtin_amdgcn_readfirstlane(itab[0]) : 0;
+  const int my_bit = split ? 1 << (wave >> 1) : 3;
+  int kt_cur = (cnt > 0) ? (int)(__builtin_amdgcn_readfirstlane(itab[0]) & 0xFFFFu) : 0;
+  int fl_cur = (cnt > 0) ? (int)(__builtin_amdgcn_readfirstlane(itab[0]) >> 16) : 0;
 
   using SC = TileSched<2 * NKS, 2 * NDB>;  // A: S^T, G_P^T of 32 keys; B: G_Q^T
   constexpr int NSTEP = SC::total;
@@ -143,9 +212,18 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
     // back they would stall the wave).  Without a next item the copies read
     // nothing and land zeros in the free stage.
     const bool more = j + 1 < cnt;
-    const int kt_nxt = more ? (int)__builtin_amdgcn_readfirstlane(itab[j + 1]) : kt;
+    const uint32_t e_nxt = more ? __builtin_amdgcn_readfirstlane(itab[j + 1]) : 0u;
+    const int kt_nxt = more ? (int)(e_nxt & 0xFFFFu) : kt;
+    const int fl_nxt = (int)(e_nxt >> 16);
     const KvSrc nsrc = kv_src<D>(kbase, vbase, kbar, kvstride, n, kt_nxt, more);
     stage_kbar<D>(Bn, nsrc, wave, lane);
+    if (!(fl_cur & my_bit)) {
+      // this wave's half does not keep tile kt: only its share of the copies
+      static_for<0, 2 * NI>([&](auto ic) { stage_kv_part<D, NT, decltype(ic)::value>(Kn, Vn, nsrc, dmo, wave); });
+      kt_cur = kt_nxt;
+      fl_cur = fl_nxt;
+      return;
+    }
 
     const int key0 = kt * TILE;
     // register r of chunk kb holds key key0 + 32kb + 4*h32 + 8(r/4) + r%4; a key
@@ -244,6 +322,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
       }
     }
     kt_cur = kt_nxt;
+    fl_cur = fl_nxt;
   };
 
   {
@@ -280,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
     for (int it = 0; it < TILE * CH / NT; ++it) {
       const int cc = tid + it * NT;
       const int row = cc / CH, ch = cc % CH;
-      if (qt * TILE + row < n)
+      if (qt * TILE + row < n && mine_h[split ? row / 64 : 0])  // rows of a stored half are dqs_kernel's
         *reinterpret_cast<u32x4*>(op + (long)row * qstride + ch * 8) =
             *reinterpret_cast<const u32x4*>(Vs0 + tile_off<D>(row, ch));
     }

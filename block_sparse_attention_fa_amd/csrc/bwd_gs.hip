@@ -31,7 +31,7 @@ namespace backlite {
 // LDS, then each thread writes its run's prefix values.
 __global__ __launch_bounds__(1024) void gs_scan_kernel(BwdArgs a) {
   __shared__ long long part[1024];
-  const long N = (long)a.B * a.H * a.T;
+  const long N = (long)a.B * a.H * a.Tq;
   const int tid = threadIdx.x;
   const long per = (N + 1023) / 1024;
   const long s0 = min(N, (long)tid * per), s1 = min(N, s0 + per);
@@ -62,36 +62,42 @@ __global__ __launch_bounds__(1024) void gs_scan_kernel(BwdArgs a) {
 // kt's k-list.  One workgroup per (b, h, qt): each kept kt of the q-list finds
 // qt in kt's ascending k-list by binary search.
 __global__ __launch_bounds__(256) void gs_slot_kernel(BwdArgs a) {
-  const int T = a.T;
-  const long bq = blockIdx.x;  // (b * H + h) * T + qt
-  const int qt = (int)(bq % T);
-  const long bh = bq / T;
+  const int T = a.T, Tq = a.Tq;
+  const long bq = blockIdx.x;  // (b * H + h) * Tq + qt
+  const int qt = (int)(bq % Tq);
+  const long bh = bq / Tq;
   const int cnt = max(0, min(a.qcnt[bq], T));
   const uint32_t base = a.qbase[bq];
   for (int i = threadIdx.x; i < cnt; i += 256) {
     const int kt = a.qidx[bq * T + i];
     if (kt >= T) continue;
     const long row = bh * T + kt;
-    const int kc = max(0, min(a.kcnt[row], T));
-    const uint16_t* list = a.kidx + row * T;
+    const int kc = max(0, min(a.kcnt[row], Tq));
+    const uint16_t* list = a.kidx + row * Tq;
     int lo = 0, hi = kc;  // first position whose entry is >= qt
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if ((int)list[mid] < qt) lo = mid + 1;
       else hi = mid;
     }
-    if (lo < kc && (int)list[lo] == qt) a.kslot[row * T + lo] = base + (uint32_t)i;
+    if (lo < kc && (int)list[lo] == qt) a.kslot[row * Tq + lo] = base + (uint32_t)i;
   }
 }
 
 // ---------------------------------------------------------------------------
-// G_Q from stored G_S.  One workgroup of 4 waves per (b, h, query tile qt);
-// wave w owns query rows 32w .. +31 and accumulates G_Q^T (C layout
-// [dim][query]) over the q-list:  G_Q^T += K^T G_S^T, both operands read from
-// LDS with the transpose read.  K rows are shared by the waves (three LDS
-// stages, copied two tiles ahead).  Each wave's own G_S rows (8 KB per tile,
-// the HBM stream of this pass) are loaded into registers three tiles ahead and
-// written to a private LDS buffer at the start of their tile.
+// G_Q from stored G_S.  One workgroup of 4 waves per (b, h, query tile qt of
+// QR rows).  QR = 128: wave w owns query rows 32w .. +31 and the whole head
+// dimension.  QR = 64 (half-height backward tiles): wave w owns rows
+// 32 (w % 2) .. +31 and half of the head dimension (columns 64 (w / 2) ..).
+// Each wave accumulates G_Q^T (C layout [dim][query]) over the q-list:
+// G_Q^T += K^T G_S^T, both operands read from LDS with the transpose read.  K
+// rows are shared by the waves (three LDS stages, copied two tiles ahead).
+// The G_S rows of each 32-row group (8 KB per tile, the HBM stream of this
+// pass) are loaded into registers three tiles ahead and written to LDS at the
+// start of their tile: with QR = 128 by the wave that owns them, into a buffer
+// of its own; with QR = 64 half by each of the two waves that share the rows,
+// into a buffer of the row group, double-buffered by tile parity (a wave may
+// still read one tile's rows while its partner writes the next tile's).
 //
 // G_S operand, per 16-key step ks (keys 16ks + 4*h32 + {0..3, 8..11}, the same
 // order as the K operand): the slot's fragment-order block of wave kw =
@@ -109,17 +115,18 @@ __device__ __forceinline__ void stage_k_part(bf16* Kd, const __amdgpu_buffer_rsr
   load_lds16<true>(rs, nullptr, dst, dmo.off[I]);
 }
 
-template <int D>
+template <int D, int QR>
 __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   constexpr int NT = 256;
-  constexpr int NDB = D / 32;
+  constexpr int NDB = QR == TILE ? D / 32 : D / 64;  // 32-wide head-dimension blocks per wave
   constexpr int NKS = TILE / 16;  // 16-key contraction steps per key tile
-  constexpr int GW = 8 * 1024;    // one wave's G_S bytes per tile
+  constexpr int GW = 8 * 1024;    // G_S bytes of one 32-row group per tile
   constexpr int NI = DmaOffsets<D, NT>::NI;
   constexpr int NST = 3;          // K stages (two tiles ahead) and G_S register sets (three ahead)
   // vector-memory operations one visit issues per wave: NI K copies, 2 row-sum
-  // words, 1 key-mean word, 8 G_S loads
-  constexpr int NSMALL = 3, NGS = 8, PER_VISIT = NI + NSMALL + NGS;
+  // words, 1 key-mean word, NGS G_S loads (8 blocks of 1 KB per 32-row group,
+  // shared by two waves when QR = 64)
+  constexpr int NSMALL = 3, NGS = QR == TILE ? 8 : 4, PER_VISIT = NI + NSMALL + NGS;
   // one variable per stage: the compiler then knows a copy into one stage
   // does not alias reads of another and waits for it only where it is read
   __shared__ __attribute__((aligned(16))) bf16 Ks0[TILE * D];
@@ -134,20 +141,22 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float Kb2[D];
   __shared__ uint16_t itab[MAX_TILES];
 
-  const int T = a.T, n = a.n;
+  const int T = a.T, n = a.n, Tq = a.Tq;
   const int L = work_index(blockIdx.x);
-  const int qt = L % T;
-  const int bh = L / T;
+  const int qt = L % Tq;
+  const int bh = L / Tq;
   const int h = bh % a.H, b = bh / a.H;
   const int g = h / (a.H / a.Hk);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5;
-  const int lrow = wave * 32 + l32;
+  const int rw = QR == TILE ? wave : (wave & 1);       // 32-row group of the wave
+  const int dh = QR == TILE ? 0 : (wave >> 1);         // head-dimension half (QR = 64)
+  const int lrow = rw * 32 + l32;
   const long qstride = (long)a.H * D;
   const long kvstride = (long)a.Hk * D;
   const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
   const float* kbar = a.kbar + (long)(b * a.Hk + g) * T * D;
-  const long bq = (long)bh * T + qt;
+  const long bq = (long)bh * Tq + qt;
   const int cnt = max(0, min(a.qcnt[bq], T));
   const uint32_t sbase = a.qbase[bq];
   // only query tiles whose kept tiles all have a slot; dq_kernel recomputes the rest
@@ -157,13 +166,14 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     for (int i = tid; i < cnt; i += NT) itab[i] = list[i];
   }
   LdsOffsets<D> lo;
-  lo.init(lane);
+  lo.init(lane, dh * NDB);
   DmaOffsets<D, NT> dmo;
   dmo.init(kvstride, tid);
   const int i16 = lane & 15, sh = (lane >> 4) & 1;
   const uint32_t goff = (uint32_t)(sh * 1024 + 128 * (h32 ^ sh) + 32 * (i16 >> 2) + 16 * (i16 & 1) +
                                    8 * ((i16 >> 1) & 1));
-  char* gw = Gw + wave * GW;
+  // this wave's G_S buffer (QR = 128), or its row group's pair (QR = 64, by parity)
+  char* gw = QR == TILE ? Gw + wave * GW : Gw + rw * GW;
   f32x16 dq[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     const uint32_t rows = valid ? (uint32_t)min(TILE, n - key0) : 0u;
     const size_t slot = (size_t)sbase + (size_t)i;
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + (long)key0 * kvstride, rows * (uint32_t)kvstride * 2u);
-    const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a.gsl + slot * (4 * TILE), valid ? 4u * TILE * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(a.gsl + slot * (4 * QR), valid ? 4u * QR * 4u : 0u);
     // key mean: D/64 copy instructions; wave w issues number w % (D/64), so
     // waves beyond the first D/64 repeat a copy (same words to the same place)
     // and every wave issues one
@@ -201,23 +211,24 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     for (int it = 0; it < 2; ++it) {
       const int e = lane + 64 * it;
       load_lds4<true>(rl, nullptr, lds_ptr(l_of(st) + wave * TILE + 64 * it),
-                      (uint32_t)((e >> 5) * TILE + 32 * wave + (e & 31)) * 4u);
+                      (uint32_t)((e >> 5) * QR + 32 * rw + (e & 31)) * 4u);
     }
     load_lds4<true>(rb, nullptr, lds_ptr(b_of(st) + 64 * kb_part), (uint32_t)(64 * kb_part + lane) * 4u);
     static_for<0, NI>([&](auto ic) { stage_k_part<D, NT, decltype(ic)::value>(k_of(st), rk, dmo, wave); });
   };
-  // this wave's 8 blocks of item i's G_S into registers: block ib = (kw, s),
-  // lane l takes the 16 bytes at position l ^ 8s
-  u32x4 gr[NST][8];
-  auto load_gs = [&](u32x4 (&r)[8], int i) {
+  // the wave's NGS blocks of item i's G_S into registers: block ib = (kw, s) of
+  // its row group (kw = 2 dh + ib / 2 when QR = 64), lane l takes the 16 bytes
+  // at position l ^ 8s
+  u32x4 gr[NST][NGS];
+  auto load_gs = [&](u32x4 (&r)[NGS], int i) {
     const size_t slot = (size_t)sbase + (size_t)i;
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.gs + slot * (TILE * TILE), i < cnt ? TILE * TILE * 2u : 0u);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.gs + slot * (QR * TILE), i < cnt ? QR * TILE * 2u : 0u);
 #pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      const int kw = ib >> 1, s2 = ib & 1;
+    for (int ib = 0; ib < NGS; ++ib) {
+      const int kw = (QR == TILE ? 0 : 2 * dh) + (ib >> 1), s2 = ib & 1;
       r[ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, (uint32_t)((lane ^ (8 * s2)) * 16), ((kw * 4 + wave) * 2 + s2) * 1024,
-                                            CPOL_NT));
+                                            rs, (uint32_t)((lane ^ (8 * s2)) * 16),
+                                            ((kw * (QR / 32) + rw) * 2 + s2) * 1024, CPOL_NT));
     }
   };
 
@@ -243,8 +254,10 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     constexpr int VM = NGS + PER_VISIT;
     static_assert(VM < 64, "vmcnt field");
     __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    char* gb0 = QR == TILE ? gw : gw + (j & 1) * (2 * GW);  // this tile's G_S buffer
 #pragma unroll
-    for (int ib = 0; ib < 8; ++ib) *reinterpret_cast<u32x4*>(gw + ib * 1024 + lane * 16) = gr[S][ib];
+    for (int ib = 0; ib < NGS; ++ib)
+      *reinterpret_cast<u32x4*>(gb0 + ((QR == TILE ? 0 : 4 * dh) + ib) * 1024 + lane * 16) = gr[S][ib];
     // Barrier without the workgroup fence of __syncthreads: the fence would
     // make every wave finish all its pending LDS copies here (item j + 1's K
     // too), which would leave K only one tile of lead.  What the barrier must
@@ -260,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     float hsum = 0.f;  // this row's sum of the bf16 G_S operands over the lane's 64 keys
     static_for<0, NKS>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
-      const char* gb = gw + (ks >> 1) * 2048 + (ks & 1) * 512 + goff;
+      const char* gb = gb0 + (ks >> 1) * 2048 + (ks & 1) * 512 + goff;
       const bf16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(gb));
       const bf16x4 g1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(gb + 256));
@@ -289,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         bf16x8 al = {};
-        if (h32 == 0) al[0] = (bf16)Bc[db * 32 + l32];
+        if (h32 == 0) al[0] = (bf16)Bc[(dh * NDB + db) * 32 + l32];
         dq[db] = mfma32(al, bl, dq[db]);
       }
     }
@@ -304,13 +317,14 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   if (j + 1 < cnt) visit(j + 1, std::integral_constant<int, 1>{});
 
   // epilogue: dq C layout is [dim = 32db + 8(r/4) + 4*h32 + r%4][query l32]
+  // (db counted from the wave's head-dimension slice)
   wait_vmem();
   __syncthreads();
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int dim = db * 32 + 8 * jj + 4 * h32;
+      const int dim = (dh * NDB + db) * 32 + 8 * jj + 4 * h32;
       bf16x4 w4 = {(bf16)(dq[db][4 * jj] * a.scale), (bf16)(dq[db][4 * jj + 1] * a.scale),
                    (bf16)(dq[db][4 * jj + 2] * a.scale), (bf16)(dq[db][4 * jj + 3] * a.scale)};
       *reinterpret_cast<bf16x4*>(Ks0 + tile_off<D>(lrow, dim >> 3) + (dim & 7)) = w4;
@@ -318,12 +332,12 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   __syncthreads();
   {
     constexpr int CH = D / 8;
-    uint16_t* op = a.dq + ((long)b * n + (long)qt * TILE) * qstride + (long)h * D;
+    uint16_t* op = a.dq + ((long)b * n + (long)qt * QR) * qstride + (long)h * D;
 #pragma unroll
-    for (int it = 0; it < TILE * CH / NT; ++it) {
+    for (int it = 0; it < QR * CH / NT; ++it) {
       const int cc = tid + it * NT;
       const int row = cc / CH, ch = cc % CH;
-      if (qt * TILE + row < n)
+      if (qt * QR + row < n)
         *reinterpret_cast<u32x4*>(op + (long)row * qstride + ch * 8) =
             *reinterpret_cast<const u32x4*>(Ks0 + tile_off<D>(row, ch));
     }
@@ -335,15 +349,20 @@ hipError_t launch_gs_slots(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(gs_scan_kernel, dim3(1), dim3(1024), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gs_slot_kernel, dim3(a.B * a.H * a.T), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(gs_slot_kernel, dim3(a.B * a.H * a.Tq), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dq_gs(const BwdArgs& a, int d, hipStream_t st) {
   ProfScope ps(PK_DQ, st);
-  const dim3 grid(a.B * a.H * a.T), block(256);
-  if (d == 64) hipLaunchKernelGGL((dqs_kernel<64>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((dqs_kernel<128>), grid, block, 0, st, a);
+  const dim3 grid(a.B * a.H * a.Tq), block(256);
+  if (a.qrows == TILE) {
+    if (d == 64) hipLaunchKernelGGL((dqs_kernel<64, TILE>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((dqs_kernel<128, TILE>), grid, block, 0, st, a);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((dqs_kernel<64, 64>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((dqs_kernel<128, 64>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

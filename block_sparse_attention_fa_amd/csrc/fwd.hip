@@ -34,7 +34,7 @@ struct FwdArgs {
   uint16_t* olo;  // optional: bf16 rounding residual of O
   float* lse;
   float* tlse;
-  double* tw;  // optional compact statistics: per tile pair, max over rows of (tile LSE - row LSE)
+  double* tw;  // optional compact statistics: per tile pair and 64-row half, max over its rows of (tile LSE - row LSE)
   int B, n, H, Hk, T;
   int window;        // sliding window (causal only): key j visible to row i iff i - window < j; 0 = none
   float scale_log2;  // scale * log2(e)
@@ -270,11 +270,13 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
     }
   }
 
-  // Compact statistics: for each (query tile, key tile) the workgroup visited,
-  // a = max over the tile's valid rows of (tile LSE - row LSE), in fp64 from the
-  // fp32 values just written (the mask's own arithmetic, so the selection from
-  // a is the same as from the per-row values).  One wave per tile pair: 64
-  // lanes read the pair's 128 row values (512 contiguous bytes, still in L2).
+  // Compact statistics: for each (query tile, key tile) the workgroup visited
+  // and each 64-row half of the query tile, a = max over the half's valid rows
+  // of (tile LSE - row LSE), in fp64 from the fp32 values just written (the
+  // mask's own arithmetic, so the selection from a is the same as from the
+  // per-row values, for 128-row query tiles as the larger of the two).  One
+  // wave per tile pair: 64 lanes read the pair's 128 row values (512
+  // contiguous bytes, still in L2).
   if (a.tw) {
     wait_vmem();      // this wave's tile-LSE stores have completed
     __syncthreads();  // ... and every other wave's, and lse_s is written
@@ -303,12 +305,19 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
           const int kt = kb + u * (NT / 64);
-          double m = -INFINITY;
-          if (v0) m = fmax(m, (double)x0[u] - l0);
-          if (v1) m = fmax(m, (double)x1[u] - l1);
+          // one value per 64-row half: rows 0-63 (lane) and 64-127 (lane + 64)
+          double m0 = v0 ? (double)x0[u] - l0 : -INFINITY;
+          double m1 = v1 ? (double)x1[u] - l1 : -INFINITY;
 #pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o));
-          if (lane == 0 && kt <= hi) a.tw[(long)bh * pairs + pair_index(qj, kt, T, CAUSAL)] = m;
+          for (int o = 32; o >= 1; o >>= 1) {
+            m0 = fmax(m0, __shfl_xor(m0, o));
+            m1 = fmax(m1, __shfl_xor(m1, o));
+          }
+          if (lane == 0 && kt <= hi) {
+            double* w2 = a.tw + 2 * ((long)bh * pairs + pair_index(qj, kt, T, CAUSAL));
+            w2[0] = m0;
+            w2[1] = m1;
+          }
         }
       }
     }

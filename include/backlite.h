@@ -22,7 +22,11 @@
  *    fastest (the README's (batch, seq_len, heads, head_dim) layout).
  *  - Query head h reads key/value head h / (H / H_k) (grouped-query attention,
  *    README "Usage": key/value carry heads_k <= heads).
- *  - Tiles are 128 query rows x 128 keys; T = ceil(n / 128).
+ *  - The forward's tiles are 128 query rows x 128 keys; T = ceil(n / 128).
+ *    The backward's query tiles have q_tile rows, 128 or 64 (the README forms
+ *    the mask "for each backward tile pair", "How It Works / Sparse Backward
+ *    Masking", and a backward's tiles need not match the forward's; half-height
+ *    query tiles give a finer mask); Tq = ceil(n / q_tile).  Key tiles stay 128.
  *  - All launches are asynchronous on `stream` (a hipStream_t; NULL = the
  *    default stream).  Argument validation is synchronous: a call that fails
  *    validation returns an error code and launches nothing.
@@ -57,11 +61,14 @@ typedef enum {
  * Returns 0 for invalid sizes. */
 size_t backlite_tile_lse_elems(int B, int H, int n, int causal);
 
-/* Number of elements of each [B, H, T, T] mask array (keep, qidx, kidx). */
-size_t backlite_mask_elems(int B, int H, int n);
+/* Number of elements of each mask array: keep and qidx are [B, H, Tq, T],
+ * kidx is [B, H, T, Tq] (Tq query tiles of q_tile rows).  0 for invalid sizes
+ * or a q_tile other than 64 or 128. */
+size_t backlite_mask_elems(int B, int H, int n, int q_tile);
 
-/* Number of int32 elements of each [B, H, T] count array (qcnt, kcnt). */
-size_t backlite_count_elems(int B, int H, int n);
+/* Number of int32 elements of a count array over tiles of `tile` rows (64 or
+ * 128): qcnt is [B, H, Tq] (tile = q_tile), kcnt is [B, H, T] (tile = 128). */
+size_t backlite_count_elems(int B, int H, int n, int tile);
 
 /* Bytes of device workspace backlite_bwd needs: the per-row D = rowsum(G_O*O)
  * values in fp32 [B, H, n], the row LSE times log2(e) in fp32 [B, H, n], the
@@ -77,9 +84,10 @@ size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d);
  * G_S K is then formed from the stored tiles instead of a second
  * recomputation of S, P and G_P; "Introducing BackLite", backward equations).
  * Layout after the base workspace: 256 bytes of state words, slot starts per
- * query tile uint32 [B, H, T], slots per k-list entry uint32 [B, H, T, T],
- * then the slots (each 32 KB of bf16 G_S plus 2 KB of fp32 sums of its
- * rounding residual).  Any workspace of at least the base size plus the state
+ * query tile uint32 [B, H, Tq], slots per k-list entry uint32 [B, H, T, Tq],
+ * then the slots (each q_tile x 128 bf16 G_S, 32 or 16 KB, plus 4 x q_tile
+ * fp32 sums of its rounding residual).  The workspace serves backward calls
+ * with that q_tile.  Any workspace of at least the base size plus the state
  * and index arrays plus one slot enables the path.  Slots are dealt to the
  * kept tiles in query-tile order (b, h, qt, then q-list order); every query
  * tile whose kept tiles all received a slot takes its G_Q from the stored
@@ -87,7 +95,7 @@ size_t backlite_bwd_workspace_bytes(int B, int H, int H_k, int n, int d);
  * smaller than the kept tiles still serves a prefix of the query tiles, and
  * the choice is made on the device: the host reads nothing back.
  * max_tiles < 1 returns the base size. */
-size_t backlite_bwd_workspace_bytes_stored(int B, int H, int H_k, int n, int d, int64_t max_tiles);
+size_t backlite_bwd_workspace_bytes_stored(int B, int H, int H_k, int n, int d, int q_tile, int64_t max_tiles);
 
 /* Byte offset, within a workspace enabling the stored path, of its state
  * words (int32): [0] = 1 if every kept tile of the last backlite_bwd on it had
@@ -125,14 +133,16 @@ size_t backlite_bwd_state_offset(int B, int H, int H_k, int n, int d);
  *     query tile are written as -inf.  May be NULL: then no statistics are
  *     written (the negl_prob = 0 dense mode).
  *   tile_w: fp64 out, optional (may be NULL; needs tile_lse): the compact
- *     statistics, backlite_tile_lse_elems() / 128 doubles in the pair layout
- *     of tile_lse without the row index.  Entry (qt, kt) is the mask's
- *     log-weight a(qt, kt) = max over the valid rows i of tile qt of
- *     (tile_lse[i, kt] - lse_row[i]), formed in fp64 from the fp32 values the
- *     call writes, exactly as backlite_mask forms it; so backlite_mask_compact
- *     on tile_w selects the same tiles as backlite_mask on (tile_lse, lse_row).
+ *     statistics, backlite_tile_lse_elems() / 64 doubles: two per tile pair,
+ *     in the pair layout of tile_lse, for the two 64-row halves of the query
+ *     tile.  Entry (qt, kt, j) is the mask's log-weight of half j:
+ *     max over its valid rows i of (tile_lse[i, kt] - lse_row[i]), formed in
+ *     fp64 from the fp32 values the call writes, exactly as backlite_mask forms
+ *     it (-inf for a half with no valid row); a 128-row query tile's weight is
+ *     the larger of its two.  So backlite_mask_compact on tile_w selects the
+ *     same tiles as backlite_mask on (tile_lse, lse_row), for either q_tile.
  *     tile_lse is then only staging: it may be reused once the call has run,
- *     and tile_w (128 rows reduced to one value, 64x fewer bytes) is what is
+ *     and tile_w (64 rows reduced to one value, 32x fewer bytes) is what is
  *     kept until the backward.  Written for candidate pairs only.
  * Requires B, n, H, H_k >= 1, H % H_k == 0, d in {64, 128}. */
 int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
@@ -142,9 +152,11 @@ int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
 
 /* Mask from statistics (README phase 2; "Using Sparsity").
  *
- * For every (b, h, query tile qt) and candidate key tile kt (all kt, or
- * kt <= qt when causal; with a sliding window w also kt >= the tile holding
- * key 128*qt - w + 1, i.e. the tiles with a key inside some row's window):
+ * For every (b, h, query tile qt of q_tile rows: 128, or 64 for half-height
+ * backward tiles) and candidate key tile kt (all kt; when causal, the key
+ * tiles whose first key is at or before the query tile's last row; with a
+ * sliding window w also kt >= the tile holding key (first row) - w + 1, i.e.
+ * the tiles with a key inside some row's window):
  *   a(qt,kt) = max over valid rows i of tile qt of (tile_lse[i,kt] - lse_row[i]),
  *              computed in fp64 from the fp32 inputs; the tile weight is
  *              w = exp(a) = the largest p_tile = exp(LSE_tile - LSE_row) of the
@@ -153,11 +165,13 @@ int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
  *   in that order, left to right; every tile whose running sum is still
  *   < negl_prob is skipped, every other candidate is kept.
  * Outputs (all written in full for every (b, h, tile)):
- *   keep [B,H,T,T] uint8: 1 = tile (qt, kt) is computed by the backward.
- *   qcnt [B,H,T] int32, qidx [B,H,T,T] uint16: for query tile qt, its kept key
- *     tiles in ascending order in qidx[..., qt, 0:qcnt]; the rest of the row is
- *     left unspecified.
- *   kcnt, kidx: the same per key tile kt (kept query tiles, ascending).
+ *   keep [B,H,Tq,T] uint8: 1 = tile (qt, kt) is computed by the backward.
+ *   qcnt [B,H,Tq] int32, qidx [B,H,Tq,T] uint16: for query tile qt, its kept
+ *     key tiles in ascending order in qidx[..., qt, 0:qcnt]; the rest of the
+ *     row is left unspecified.
+ *   kcnt [B,H,T], kidx [B,H,T,Tq]: the same per key tile kt (kept query tiles,
+ *     ascending).
+ *   backlite_bwd must be given the same q_tile.
  *   stats: optional (may be NULL) int64[2], ACCUMULATED into (not cleared):
  *     [0] += candidate tile pairs, [1] += kept tile pairs.
  *   With the environment variable BACKLITE_VERBOSE=1 the call synchronises and
@@ -167,7 +181,7 @@ int backlite_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
  * negl_prob must be finite and in [0, 1); with negl_prob <= 1 every query tile
  * keeps at least one key tile. */
 int backlite_mask(const float* tile_lse, const float* lse_row,
-                  int B, int H, int n, int causal, int window, float negl_prob,
+                  int B, int H, int n, int causal, int window, int q_tile, float negl_prob,
                   uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
                   int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream);
 
@@ -183,7 +197,10 @@ int backlite_mask(const float* tile_lse, const float* lse_row,
  * head sum over its query heads.  Every element of dQ, dK, dV is written (key
  * rows no list reaches get zeros).
  *   qcnt/qidx drive G_Q (per query tile); kcnt/kidx drive G_K, G_V (per key
- *   tile); both must describe the same tile set (as backlite_mask writes them).
+ *   tile); both must describe the same tile set (as backlite_mask writes them
+ *   with the same q_tile, 64 or 128: the query tiles' rows; with 64 the
+ *   G_K/G_V pass takes two list items per 128-row step and the G_Q passes work
+ *   on 64-row tiles).
  *   workspace: device buffer of at least backlite_bwd_workspace_bytes(); its
  *   contents on entry are ignored.  A larger one (see
  *   backlite_bwd_workspace_bytes_stored) enables the stored-G_S path, chosen
@@ -207,7 +224,7 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
                  const int32_t* qcnt, const uint16_t* qidx,
                  const int32_t* kcnt, const uint16_t* kidx,
-                 int B, int n, int H, int H_k, int d, float scale, int causal, int window,
+                 int B, int n, int H, int H_k, int d, float scale, int causal, int window, int q_tile,
                  uint16_t* dQ, uint16_t* dK, uint16_t* dV,
                  void* workspace, size_t workspace_bytes, void* stream);
 
@@ -235,17 +252,17 @@ int backlite_bwd_noalloc(const uint16_t* Q, const uint16_t* K, const uint16_t* V
                          const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
                          const int32_t* qcnt, const uint16_t* qidx,
                          const int32_t* kcnt, const uint16_t* kidx,
-                         int B, int n, int H, int H_k, int d, float scale, int causal, int window,
+                         int B, int n, int H, int H_k, int d, float scale, int causal, int window, int q_tile,
                          uint16_t* dQ, uint16_t* dK, uint16_t* dV, void* stream);
 
 /* Mask from compact statistics: the tile_w output of backlite_fwd in place of
- * (tile_lse, lse_row); everything else as backlite_mask, and the same keep
- * bitmap and lists for the same forward.  tile_w may be NULL only with
+ * (tile_lse, lse_row); everything else as backlite_mask (q_tile 64 or 128),
+ * and the same keep bitmap and lists for the same forward.  tile_w may be NULL only with
  * negl_prob == 0.  The pages speak of statistics per (query tile, key tile)
  * ("Using Sparsity") and report the method's small extra peak memory
  * ("Training Nanochat"); tile_w is that per-pair form, reduced inside the
  * forward from the per-row values. */
-int backlite_mask_compact(const double* tile_w, int B, int H, int n, int causal, int window,
+int backlite_mask_compact(const double* tile_w, int B, int H, int n, int causal, int window, int q_tile,
                           float negl_prob, uint8_t* keep, int32_t* qcnt, uint16_t* qidx,
                           int32_t* kcnt, uint16_t* kidx, int64_t* stats, void* stream);
 

@@ -52,13 +52,14 @@ def rows_to_packed(rows, B, H, n, causal):
     return out.reshape(-1)
 
 
-def lists_to_torch(keep, device):
+def lists_to_torch(keep, device, q_tile=TILE):
     qcnt, qidx, kcnt, kidx = orc.lists_from_keep(keep)
     return {
         "qcnt": torch.from_numpy(qcnt).to(device),
         "qidx": torch.from_numpy(qidx.view(np.int16)).to(device),
         "kcnt": torch.from_numpy(kcnt).to(device),
         "kidx": torch.from_numpy(kidx.view(np.int16)).to(device),
+        "q_tile": q_tile,
     }
 
 
@@ -72,11 +73,12 @@ def check_lists(m, keep_ref):
     assert (gq == qcnt).all() and (gk == kcnt).all()
     gqi = m["qidx"].cpu().numpy().view(np.uint16)
     gki = m["kidx"].cpu().numpy().view(np.uint16)
-    B, H, T, _ = keep_ref.shape
+    B, H, Tq, Tk = keep_ref.shape
     for b in range(B):
         for h in range(H):
-            for t in range(T):
+            for t in range(Tq):
                 assert (gqi[b, h, t, :qcnt[b, h, t]] == qidx[b, h, t, :qcnt[b, h, t]]).all()
+            for t in range(Tk):
                 assert (gki[b, h, t, :kcnt[b, h, t]] == kidx[b, h, t, :kcnt[b, h, t]]).all()
 
 

@@ -36,8 +36,11 @@ def test_sizes(L):
     assert L.backlite_tile_lse_elems(1, 2, 1024, 0) == 2 * 64 * 128
     assert L.backlite_tile_lse_elems(1, 1, 300, 1) == 6 * 128          # T = 3 -> 6 pairs
     assert L.backlite_tile_lse_elems(1, 40, 75600, 0) == 40 * 591 * 591 * 128
-    assert L.backlite_mask_elems(2, 3, 129) == 2 * 3 * 4
-    assert L.backlite_count_elems(2, 3, 129) == 2 * 3 * 2
+    assert L.backlite_mask_elems(2, 3, 129, 128) == 2 * 3 * 4
+    assert L.backlite_mask_elems(2, 3, 129, 64) == 2 * 3 * 3 * 2      # Tq = 3 query tiles x T = 2
+    assert L.backlite_mask_elems(2, 3, 129, 96) == 0
+    assert L.backlite_count_elems(2, 3, 129, 128) == 2 * 3 * 2
+    assert L.backlite_count_elems(2, 3, 129, 64) == 2 * 3 * 3
     # D and LSE*log2(e): 1*2*100 floats = 800 B -> 1024 each; kbar: 1*2*1*64 floats = 512 B;
     # G_K/G_V chunk plan: NK = 2 key tiles, 4 + 11*2 int32 = 104 B -> 256; partial sums:
     # 2 x 2 x 128 x 64 floats = 131072 B
@@ -46,12 +49,15 @@ def test_sizes(L):
     assert L.backlite_tile_lse_elems(0, 1, 1, 0) == 0
     # stored-G_S workspace: base, 256 B of state words, qbase (2 x 1 uint32 -> 256 B),
     # kslot (2 x 1 x 1 uint32 -> 256 B), then 34816 B (32 KB G_S + 2 KB row sums) per slot
-    assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 0) == base
-    assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 3) == base + 3 * 256 + 3 * 34816
+    assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 128, 0) == base
+    assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 128, 3) == base + 3 * 256 + 3 * 34816
+    # 64-row query tiles: Tq = 2; qbase 2 x 2 uint32, kslot 2 x 1 x 2 uint32 (each -> 256 B);
+    # 16 KB G_S + 1 KB sums per slot
+    assert L.backlite_bwd_workspace_bytes_stored(1, 2, 2, 100, 64, 64, 3) == base + 3 * 256 + 3 * 17408
     assert L.backlite_bwd_state_offset(1, 2, 2, 100, 64) == base
     # the 32k-token video shape: T = 256, 40 heads
     big = L.backlite_bwd_workspace_bytes(1, 40, 40, 32760, 128)
-    assert L.backlite_bwd_workspace_bytes_stored(1, 40, 40, 32760, 128, 1000) == \
+    assert L.backlite_bwd_workspace_bytes_stored(1, 40, 40, 32760, 128, 128, 1000) == \
         big + 256 + 40 * 256 * 4 + 40 * 256 * 256 * 4 + 1000 * 34816
 
 
@@ -75,14 +81,14 @@ def test_fwd_validation(L, kw, code):
     assert L.backlite_last_error()
 
 
-def _mask(L, negl=0.05, tl=FAKE, keep=FAKE, n=256, causal=0, window=0):
-    return L.backlite_mask(tl, FAKE, 1, 2, n, causal, window, negl, keep, FAKE, FAKE, FAKE, FAKE, None, None)
+def _mask(L, negl=0.05, tl=FAKE, keep=FAKE, n=256, causal=0, window=0, q_tile=128):
+    return L.backlite_mask(tl, FAKE, 1, 2, n, causal, window, q_tile, negl, keep, FAKE, FAKE, FAKE, FAKE, None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(negl=-0.1), -1), (dict(negl=1.0), -1), (dict(negl=float("nan")), -1),
     (dict(tl=None), -1), (dict(keep=None), -1), (dict(keep=MIS), -1), (dict(n=0), -1),
-    (dict(window=64), -1), (dict(causal=1, window=-5), -1),
+    (dict(window=64), -1), (dict(causal=1, window=-5), -1), (dict(q_tile=32), -2), (dict(q_tile=0), -2),
 ])
 def test_mask_validation(L, kw, code):
     assert _mask(L, **kw) == code
@@ -90,17 +96,17 @@ def test_mask_validation(L, kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(tw=None), -1), (dict(negl=1.0), -1), (dict(tw=MIS), -1), (dict(causal=0, window=8), -1),
-    (dict(n=131073), -2),
+    (dict(n=131073), -2), (dict(q_tile=256), -2),
 ])
 def test_mask_compact_validation(L, kw, code):
-    a = dict(tw=FAKE, n=256, causal=1, window=0, negl=0.05)
+    a = dict(tw=FAKE, n=256, causal=1, window=0, negl=0.05, q_tile=128)
     a.update(kw)
-    assert L.backlite_mask_compact(a["tw"], 1, 2, a["n"], a["causal"], a["window"], a["negl"], FAKE, FAKE, FAKE,
-                                   FAKE, FAKE, None, None) == code
+    assert L.backlite_mask_compact(a["tw"], 1, 2, a["n"], a["causal"], a["window"], a["q_tile"], a["negl"], FAKE,
+                                   FAKE, FAKE, FAKE, FAKE, None, None) == code
 
 
 def test_bwd_validation(L):
-    args = [FAKE] * 11 + [1, 256, 4, 2, 128, 0.1, 0, 0, FAKE, FAKE, FAKE]
+    args = [FAKE] * 11 + [1, 256, 4, 2, 128, 0.1, 0, 0, 128, FAKE, FAKE, FAKE]
     # workspace too small / missing
     assert L.backlite_bwd(*args, FAKE, 16, None) == -3
     assert L.backlite_bwd(*args, None, 1 << 20, None) == -3
@@ -113,6 +119,9 @@ def test_bwd_validation(L):
     bad = list(args)
     bad[18] = 64                                  # a window without causal
     assert L.backlite_bwd(*bad, FAKE, 1 << 20, None) == -1
+    bad = list(args)
+    bad[19] = 32                                  # q_tile
+    assert L.backlite_bwd(*bad, FAKE, 1 << 20, None) == -2
 
 
 def test_status_strings(L):
@@ -125,7 +134,7 @@ def test_bwd_noalloc_rejects_shapes_beyond_the_scratch(L):
     shape with 1024 heads needs more for its D and key-mean arrays alone, so the
     call returns the workspace status before touching the device."""
     assert L.backlite_bwd_noalloc_scratch_bytes() == 256 << 20
-    args = [FAKE] * 11 + [1, 32760, 1024, 1024, 128, 0.088, 0, 0, FAKE, FAKE, FAKE, None]
+    args = [FAKE] * 11 + [1, 32760, 1024, 1024, 128, 0.088, 0, 0, 128, FAKE, FAKE, FAKE, None]
     assert L.backlite_bwd_noalloc(*args) == -3
     assert b"scratch" in L.backlite_last_error()
     bad = list(args)

@@ -27,16 +27,17 @@ IDS = [f"{w.name}-w{win}" for w, win in CASES]
 
 
 def _unpack_w(tw, B, H, n, causal, cand):
-    """[B*H*pairs] fp64 -> [B, H, T, T], -inf off-candidate."""
+    """[B*H*pairs*2] fp64 -> [B, H, ceil(n/64), T]: the value of 64-row half j of
+    query tile qt at row 2 qt + j; -inf where the 128-row pair is no candidate."""
     T = (n + TILE - 1) // TILE
     pairs = T * (T + 1) // 2 if causal else T * T
-    a = np.asarray(tw, dtype=np.float64).reshape(B, H, pairs)
-    out = np.full((B, H, T, T), -np.inf)
+    a = np.asarray(tw, dtype=np.float64).reshape(B, H, pairs, 2)
+    out = np.full((B, H, 2 * T, T), -np.inf)
     for qt in range(T):
         for kt in range(T):
             if cand[qt, kt]:
-                out[:, :, qt, kt] = a[:, :, pair_index(qt, kt, T, causal)]
-    return out
+                out[:, :, 2 * qt:2 * qt + 2, kt] = a[:, :, pair_index(qt, kt, T, causal), :]
+    return out[:, :, :(n + 63) // 64]
 
 
 def _run(bl, w, win):
@@ -65,14 +66,17 @@ def test_compact_statistics_bit_exact(case):
     cand = orc.candidates(n, causal, window=win)
     rows = packed_to_rows(tl.cpu().numpy(), B, H, n, causal)
     rows = np.where(np.broadcast_to(cand[np.arange(n) // TILE], rows.shape), rows, -np.inf)
-    want = orc.tile_log_weights(rows, lse.cpu().numpy(), n, causal, window=win)
+    # one value per 64-row half: the oracle's log-weights over 64-row query tiles
+    want = orc.tile_log_weights(rows, lse.cpu().numpy(), n, causal, window=win, q_tile=64)
     got = _unpack_w(tw.cpu().numpy(), B, H, n, causal, cand)
     assert np.array_equal(got, want)
-    # the compact mask selects exactly what the per-row mask selects
-    for negl in (0.0, 0.01, 0.05, 0.3):
-        m1 = bl.mask(tl, lse, n, causal, negl, window=win)
-        m2 = bl._lib.mask_compact(tw, B, H, n, causal, negl, window=win)
-        check_lists(m2, m1["keep"].cpu().numpy().astype(bool))
+    # the compact mask selects exactly what the per-row mask selects, for both
+    # query-tile heights
+    for q_tile in (128, 64):
+        for negl in (0.0, 0.01, 0.05, 0.3):
+            m1 = bl.mask(tl, lse, n, causal, negl, window=win, q_tile=q_tile)
+            m2 = bl._lib.mask_compact(tw, B, H, n, causal, negl, window=win, q_tile=q_tile)
+            check_lists(m2, m1["keep"].cpu().numpy().astype(bool))
     # and dense without statistics
     m0 = bl._lib.mask_compact(None, B, H, n, causal, 0.0, window=win, device=tw.device)
     T = m0["keep"].shape[-1]
@@ -90,9 +94,10 @@ def test_compact_mask_full_size(w, win):
     B, H, n, causal = w.B, w.H, w.n, w.causal
     o, lse, tl, tw, o2, lse2 = _run(bl, w, win)
     assert torch.equal(o, o2)
-    for negl in w.negl_probs:
-        m1 = bl.mask(tl, lse, n, causal, negl, window=win)
-        m2 = bl._lib.mask_compact(tw, B, H, n, causal, negl, window=win)
+    sparse = next(p for p in w.negl_probs if p > 0)
+    for negl, q_tile in [(p, 128) for p in w.negl_probs] + [(sparse, 64)]:
+        m1 = bl.mask(tl, lse, n, causal, negl, window=win, q_tile=q_tile)
+        m2 = bl._lib.mask_compact(tw, B, H, n, causal, negl, window=win, q_tile=q_tile)
         for key in ("keep", "qcnt", "qidx", "kcnt", "kidx"):
             if key in ("qidx", "kidx"):
                 # compare only the listed prefix of each row
@@ -102,7 +107,7 @@ def test_compact_mask_full_size(w, win):
                 assert torch.equal(m1[key][sel], m2[key][sel]), key
             else:
                 assert torch.equal(m1[key], m2[key]), key
-        flush_print(f"  negl={negl}: kept {int(m1['qcnt'].sum())} tiles, identical")
+        flush_print(f"  negl={negl} q_tile={q_tile}: kept {int(m1['qcnt'].sum())} tiles, identical")
     flush_print(f"  tile_lse {tl.numel() * 4 / 1e9:.3f} GB, tile_w {tw.numel() * 8 / 1e9:.4f} GB")
 
 
