@@ -53,8 +53,9 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-backward comparison")
     ap.add_argument("--grad-check", action="store_true",
                     help="report cosine and rel-L2 of the sparse gradients against the dense (negl_prob = 0) ones")
-    ap.add_argument("--gq-path", choices=["stored", "recompute"], default="stored",
-                    help="G_Q from stored bf16 G_S tiles (workspace slots) or by recomputation")
+    ap.add_argument("--gq-path", choices=["stored", "recompute", "atomic"], default="stored",
+                    help="G_Q from stored bf16 G_S tiles (workspace slots), by recomputation, or by fp32 atomics "
+                         "inside the G_K/G_V pass (fused single pass)")
     ap.add_argument("--gs-budget-gb", type=float, default=None,
                     help="device memory for G_S slots (default: a slot for every kept tile when they fit); "
                          "query tiles past the budget recompute G_Q")
@@ -191,10 +192,22 @@ def main():
     stats = torch.zeros(2, dtype=torch.int64, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     stored = args.gq_path == "stored"
+    atomic = args.gq_path == "atomic"
+    if atomic and args.q_tile != TILE:
+        sys.exit("--gq-path atomic takes 128-row query tiles")
+
+    def backward(lists, ws, o, lse, olo):
+        if atomic:
+            return _lib.bwd_atomic(q, k, v, o, do, lse, lists, causal=causal, window=win, workspace=ws,
+                                   out=(dq, dk, dv), o_lo=olo)
+        return bl.bwd(q, k, v, o, do, lse, lists, causal=causal, window=win, workspace=ws, out=(dq, dk, dv),
+                      o_lo=olo)
 
     def workspace(lists):
         # G_S slots: a budget, or one slot per kept tile when they fit in free
         # device memory (counted once here, outside the timed region)
+        if atomic:
+            return _lib.bwd_atomic_workspace(q, k)
         if not stored:
             return _lib.bwd_workspace(q, k, lists, stored_tiles=0)
         if args.gs_budget_gb is not None:
@@ -220,7 +233,7 @@ def main():
             m = bl.mask(tl, lse, n, causal, negl, window=win, stats=stats, q_tile=QT)
         if rec is not None:
             rec[1].record()
-        bl.bwd(q, k, v, o, do, lse, m, causal=causal, window=win, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+        backward(m, ws, o, lse, olo)
         return o, lse, olo
 
     for _ in range(args.warmup):
@@ -252,7 +265,7 @@ def main():
     st = stats.cpu().tolist()
     cand, kept = st[0] / args.steps, st[1] / args.steps
     sparsity = 1.0 - kept / cand if cand else 0.0
-    has_slots = ws.numel() > _lib.bwd_workspace_bytes(B, H, Hk, n, d)
+    has_slots = not atomic and ws.numel() > _lib.bwd_workspace_bytes(B, H, Hk, n, d)
     gq_state = _lib.bwd_state(ws, B, H, Hk, n, d) if has_slots else (False, int(kept), 0)
     gq_stored = gq_state[0]
     ws_bytes = ws.numel()
@@ -268,17 +281,17 @@ def main():
         del ws
         ws = workspace(md)
         for _ in range(max(1, args.warmup)):
-            bl.bwd(q, k, v, o, do, lse, md, causal=causal, window=win, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+            backward(md, ws, o, lse, olo)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
-            bl.bwd(q, k, v, o, do, lse, md, causal=causal, window=win, workspace=ws, out=(dq, dk, dv), o_lo=olo)
+            backward(md, ws, o, lse, olo)
         e1.record()
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / args.steps
-        dense_stored = _lib.bwd_stored_taken(ws, B, H, Hk, n, d)[0] if ws.numel() > _lib.bwd_workspace_bytes(
-            B, H, Hk, n, d) else False
+        dense_stored = _lib.bwd_stored_taken(ws, B, H, Hk, n, d)[0] if (
+            not atomic and ws.numel() > _lib.bwd_workspace_bytes(B, H, Hk, n, d)) else False
 
     # dense-vs-sparse gradients (after the dense timing dq, dk, dv hold the dense ones)
     grad_cmp = None
@@ -323,7 +336,7 @@ def main():
     # per-row statistics allow): mask + backward timed over the same steps, on
     # the forward's outputs of the last step.
     q64 = None
-    if QT == TILE and not args.no_q64 and dense_ms is not None:
+    if QT == TILE and not args.no_q64 and not atomic and dense_ms is not None:
         o, lse, olo = step()
         st64 = torch.zeros(2, dtype=torch.int64, device=dev)
         m64 = bl.mask(tl, lse, n, causal, negl, window=win, q_tile=64)
@@ -380,7 +393,8 @@ def main():
         "dense_bwd_ms": dense_ms,
         "bwd_speedup_vs_dense": (dense_ms / bwd_ms) if dense_ms else None,
         "dense_vs_sparse_grads": grad_cmp,
-        "gq_path": "stored" if gq_stored else ("partly stored" if gq_state[2] else "recompute"),
+        "gq_path": "atomic" if atomic else (
+            "stored" if gq_stored else ("partly stored" if gq_state[2] else "recompute")),
         "gq_stored_tiles": gq_state[2],
         "peak_mem_gb": peak_mem / 1e9,
         "dense_gq_path": None if dense_stored is None else ("stored" if dense_stored else "recompute"),

@@ -54,6 +54,10 @@ def _load():
     lib.backlite_mask_compact.restype = I
     lib.backlite_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, P, P, P, Z, P]
     lib.backlite_bwd.restype = I
+    lib.backlite_bwd_atomic_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.backlite_bwd_atomic_workspace_bytes.restype = Z
+    lib.backlite_bwd_atomic.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, P, P, P, Z, P]
+    lib.backlite_bwd_atomic.restype = I
     lib.backlite_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, I, P, P, P, P]
     lib.backlite_bwd_noalloc.restype = I
     lib.backlite_bwd_noalloc_scratch_bytes.argtypes = []
@@ -354,6 +358,36 @@ def similarity_sums(a, b, out=None):
     _check(_load().backlite_similarity_sums(_ptr(a), _ptr(b), a.numel(), _ptr(out), _stream(a.device)),
            "backlite_similarity_sums")
     return out
+
+
+def bwd_atomic_workspace(q, k) -> torch.Tensor:
+    B, n, H, d = q.shape
+    nb = int(_load().backlite_bwd_atomic_workspace_bytes(B, H, k.shape[2], n, d))
+    return torch.empty(nb, dtype=torch.uint8, device=q.device)
+
+
+def bwd_atomic(q, k, v, o, do, lse, lists, scale=None, causal=False, workspace=None, out=None, o_lo=None, window=0):
+    """The fused single-pass backward with an fp32-atomic G_Q (backlite_bwd_atomic);
+    128-row query tiles only."""
+    B, n, H, d = q.shape
+    Hk = k.shape[2]
+    for name, t, shp in (("q", q, (B, n, H, d)), ("k", k, (B, n, Hk, d)), ("v", v, (B, n, Hk, d)),
+                         ("o", o, (B, n, H, d)), ("do", do, (B, n, H, d))):
+        _need(t, name, torch.bfloat16, shp)
+    _need(lse, "lse", torch.float32, (B, H, n))
+    if _check_lists_shapes(lists, B, H, n) != TILE:
+        raise ValueError("the atomic G_Q backward takes 128-row query tiles")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    if workspace is None:
+        workspace = bwd_atomic_workspace(q, k)
+    rc = _load().backlite_bwd_atomic(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_lo), _ptr(do), _ptr(lse),
+                                     _ptr(lists["qcnt"]), _ptr(lists["qidx"]), _ptr(lists["kcnt"]),
+                                     _ptr(lists["kidx"]), B, n, H, Hk, d, scale, int(causal), int(window),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                     _stream(q.device))
+    _check(rc, "backlite_bwd_atomic")
+    return dq, dk, dv
 
 
 def bwd_noalloc(q, k, v, o, do, lse, lists, out, scale=None, causal=False, o_lo=None, window=0):

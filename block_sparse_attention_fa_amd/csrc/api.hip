@@ -27,7 +27,7 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       int H, int Hk, int d, float scale, int causal, int window, int q_tile, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
                       uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
-                      float* dkpart, int dk_chmin, int dk_pcap, hipStream_t st);
+                      float* dkpart, int dk_chmin, int dk_pcap, float* dqacc, hipStream_t st);
 size_t similarity_elems();
 hipError_t launch_similarity(const uint16_t* a, const uint16_t* b, long m, double* out, hipStream_t st);
 }  // namespace backlite
@@ -347,7 +347,7 @@ int run_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint1
             const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H, int H_k, int d, float scale, int causal,
             int window, int q_tile, uint16_t* dQ, uint16_t* dK, uint16_t* dV, char* ws, int pcap, int32_t* gsinfo,
             uint32_t* qbase, uint32_t* kslot, uint16_t* gs, float* gsl, long long cap, void* stream,
-            const char* what) {
+            const char* what, float* dqacc = nullptr) {
   const size_t kbar_off = 2 * delta_bytes(B, H, n);
   const size_t plan_off = kbar_off + round256((size_t)B * H_k * ntiles(n) * d * sizeof(float));
   const size_t part_off = plan_off + dkplan_bytes(B, H_k, n);
@@ -355,7 +355,7 @@ int run_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint1
                                          scale, causal ? 1 : 0, window, q_tile, dQ, dK, dV, (float*)ws,
                                          (float*)(ws + delta_bytes(B, H, n)), (float*)(ws + kbar_off), gsinfo, qbase,
                                          kslot, gs, gsl, cap, (int32_t*)(ws + plan_off), (float*)(ws + part_off),
-                                         min_chunk(), pcap, (hipStream_t)stream),
+                                         min_chunk(), pcap, dqacc, (hipStream_t)stream),
                     what);
 }
 
@@ -472,6 +472,31 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const 
     }
   }
   return r;
+}
+
+size_t backlite_bwd_atomic_workspace_bytes(int B, int H, int H_k, int n, int d) {
+  const size_t base = backlite_bwd_workspace_bytes(B, H, H_k, n, d);
+  if (base == 0) return 0;
+  return base + round256((size_t)B * H * ntiles(n) * kTile * d * sizeof(float));
+}
+
+int backlite_bwd_atomic(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const uint16_t* O,
+                        const uint16_t* O_lo, const uint16_t* dO, const float* lse_row, const int32_t* qcnt,
+                        const uint16_t* qidx, const int32_t* kcnt, const uint16_t* kidx, int B, int n, int H,
+                        int H_k, int d, float scale, int causal, int window, uint16_t* dQ, uint16_t* dK,
+                        uint16_t* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_bwd_args(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window,
+                     kTile, dQ, dK, dV));
+  const size_t need = backlite_bwd_atomic_workspace_bytes(B, H, H_k, n, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(BACKLITE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", need, workspace_bytes,
+                workspace ? "" : ", NULL");
+  TRY(check_ptr(workspace, "workspace"));
+  char* ws = (char*)workspace;
+  const size_t base = backlite_bwd_workspace_bytes(B, H, H_k, n, d);
+  return run_bwd(Q, K, V, O, O_lo, dO, lse_row, qcnt, qidx, kcnt, kidx, B, n, H, H_k, d, scale, causal, window,
+                 kTile, dQ, dK, dV, ws, B * H_k * ntiles(n), nullptr, nullptr, nullptr, nullptr, nullptr, 0, stream,
+                 "backlite_bwd_atomic launch", (float*)(ws + base));
 }
 
 size_t backlite_bwd_noalloc_scratch_bytes(void) { return kScratchBytes; }

@@ -31,6 +31,8 @@ hipError_t launch_dkdv_d64(const BwdArgs& a, bool causal, hipStream_t st);
 hipError_t launch_dkdv_d128(const BwdArgs& a, bool causal, hipStream_t st);
 hipError_t launch_dkdv_d64_gs(const BwdArgs& a, bool causal, hipStream_t st);
 hipError_t launch_dkdv_d128_gs(const BwdArgs& a, bool causal, hipStream_t st);
+hipError_t launch_dkdv_d64_atom(const BwdArgs& a, bool causal, hipStream_t st);
+hipError_t launch_dkdv_d128_atom(const BwdArgs& a, bool causal, hipStream_t st);
 // stored-G_S path (bwd_gs.hip): slot assignment, G_Q from stored G_S
 hipError_t launch_gs_slots(const BwdArgs& a, hipStream_t st);
 hipError_t launch_dq_gs(const BwdArgs& a, int d, hipStream_t st);
@@ -257,6 +259,37 @@ __global__ __launch_bounds__(256) void dk_reduce_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32-atomic G_Q variant: zero the accumulator before the pass, convert it
+// to bf16 G_Q = scale * acc afterwards (rows >= n are padding).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void zero_f32x4_kernel(float* p, long n4) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256)
+    reinterpret_cast<f32x4*>(p)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dq_convert_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 values each
+  const long rows = (long)a.B * a.n * a.H;
+  const long row = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  if (row >= rows) return;
+  // row = (b*n + i)*H + h of G_Q; the accumulator is [b*H + h][T*128][D]
+  const int h = (int)(row % a.H);
+  const long bi = row / a.H;
+  const int i = (int)(bi % a.n), b = (int)(bi / a.n);
+  const float* src = a.dqacc + (((long)b * a.H + h) * (long)(a.T * TILE) + i) * D + sub * 8;
+  const f32x4 x0 = reinterpret_cast<const f32x4*>(src)[0], x1 = reinterpret_cast<const f32x4*>(src)[1];
+  bf16x8 o;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    o[u] = (bf16)(x0[u] * a.scale);
+    o[4 + u] = (bf16)(x1[u] * a.scale);
+  }
+  *reinterpret_cast<bf16x8*>(a.dq + row * D + sub * 8) = o;
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   {
@@ -282,6 +315,32 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(dk_fill_kernel, dim3((NK + 255) / 256), dim3(256), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (a.dqacc) {
+    // fused single pass: G_K/G_V and the atomic G_Q product, then the conversion
+    const long n4 = (long)a.B * a.H * a.T * TILE * D / 4;
+    {
+      ProfScope ps(PK_DQ, st);
+      hipLaunchKernelGGL(zero_f32x4_kernel, dim3(2048), dim3(256), 0, st, a.dqacc, n4);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    {
+      ProfScope ps(PK_DKDV, st);
+      e = D == 64 ? launch_dkdv_d64_atom(a, CAUSAL, st) : launch_dkdv_d128_atom(a, CAUSAL, st);
+      if (e != hipSuccess) return e;
+    }
+    {
+      ProfScope ps(PK_DK_REDUCE, st);
+      hipLaunchKernelGGL((dk_reduce_kernel<D>), dim3(NK * DK_RS), dim3(256), 0, st, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    ProfScope ps(PK_DQ, st);
+    const long rows = (long)a.B * a.n * a.H;
+    const long rpb = 256 / (D / 8);
+    hipLaunchKernelGGL((dq_convert_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, a);
+    return hipGetLastError();
   }
   // With slots in the workspace the G_K/G_V pass stores G_S for every kept
   // tile that has a slot (slots are dealt in query-tile order); each query tile
@@ -315,10 +374,10 @@ hipError_t launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       int H, int Hk, int d, float scale, int causal, int window, int q_tile, uint16_t* dq,
                       uint16_t* dk, uint16_t* dv, float* dbuf, float* lse2, float* kbar, int32_t* gsinfo, uint32_t* qbase,
                       uint32_t* kslot, uint16_t* gs, float* gsl, long long gs_cap, int32_t* dkplan,
-                      float* dkpart, int dk_chmin, int dk_pcap, hipStream_t st) {
+                      float* dkpart, int dk_chmin, int dk_pcap, float* dqacc, hipStream_t st) {
   BwdArgs a{q,    k,      v,     o,     olo,    dout,   lse,      qcnt, qidx, kcnt, kidx, dq,
             dk,   dv,     dbuf,  lse2,  kbar,   gsinfo, qbase,    kslot, gs, gsl, gs_cap, dkplan,
-            dkpart, dk_chmin, dk_pcap, B, n, H, Hk, (n + TILE - 1) / TILE, (n + q_tile - 1) / q_tile, q_tile,
+            dkpart, dk_chmin, dk_pcap, dqacc, B, n, H, Hk, (n + TILE - 1) / TILE, (n + q_tile - 1) / q_tile, q_tile,
             window < n ? window : 0, scale, scale * LOG2E};
   if (d == 64) return causal ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
   return causal ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);

@@ -39,6 +39,7 @@ struct BwdArgs {
   float* dkpart;       // partial G_K, G_V of split key tiles: [slot][2][128][d] fp32, NK slots
   int dk_chmin;        // smallest chunk length
   int dk_pcap;         // partial slots available (<= NK); bounds the number of split chunks
+  float* dqacc;        // fp32-atomic G_Q variant: [B, H, T * 128, d] accumulator of G_S K (else NULL)
   int B, n, H, Hk, T;  // T: key tiles of 128 keys
   int Tq, qrows;       // query tiles of the lists and their rows (128, or 64: half-height backward tiles)
   int window;          // sliding window (causal only): key j visible to row i iff i - window < j; 0 = none

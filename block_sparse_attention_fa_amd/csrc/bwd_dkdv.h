@@ -102,9 +102,18 @@ constexpr int DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141, DPP_XOR2 = 0x
 // skips that tile, so its loop carries no per-element mask at all.  (Causal
 // attention masks them through the diagonal, and without G_S stores their
 // rows are simply never written.)
-template <int D, bool CAUSAL, bool GS, bool RAGGED>
+//
+// ATOM (the fused single-pass variant, 128-row query tiles, no G_S stores):
+// after each chunk's softmax the wave also forms its share of G_Q, the chunk's
+// G_S (32 rows x the wave's 32 keys, transposed through a 2 KB LDS scratch)
+// times the wave's 32 K rows, and adds it to the fp32 accumulator a.dqacc
+// with global atomics.  G_S enters as bf16 hi + lo (two products), so no
+// rounding compensation is needed.  The order of the atomic adds varies from
+// run to run, so G_Q is not bit-reproducible in this variant.
+template <int D, bool CAUSAL, bool GS, bool RAGGED, bool ATOM = false>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   static_assert(!RAGGED || (GS && !CAUSAL), "the ragged instance is the stored non-causal one");
+  static_assert(!ATOM || (!GS && !RAGGED), "the atomic G_Q variant stores no G_S");
   constexpr int NT = 256;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -119,6 +128,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   constexpr int ITAB = 2048;  // work-list window held in LDS
   __shared__ uint32_t itab[ITAB];
   __shared__ uint32_t stab[GS ? ITAB : 1];  // G_S slot of each windowed item
+  __shared__ __attribute__((aligned(16))) bf16 Gt[ATOM ? 4 * 2048 : 8];  // per wave: G_S hi, lo [32 keys][32 rows]
 
   const int T = a.T, n = a.n;
   // this workgroup's chunk of the work: items [i0, i1) of key tile bgk's list
@@ -164,6 +174,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   for (int i = 0; i < NDB; ++i) {
     dk[i] = f32x16{};
     dv[i] = f32x16{};
+  }
+  // ATOM: the wave's 32 K rows as B operands of G_Q = G_S K: block db, 16-key
+  // step s, lane (dim 32db + l32, h32) holds keys 16s + 8h32 + 0..7
+  bf16x8 kT[ATOM ? NDB : 1][2];
+  if constexpr (ATOM) {
+    const uint16_t* kb = a.k + ((long)b * n) * kvstride + (long)g * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kj = kt * TILE + kw * 32 + 16 * s2 + 8 * h32 + j;
+          const uint16_t u = kj < n ? kb[(long)kj * kvstride + 32 * db + l32] : (uint16_t)0;
+          kT[db][s2][j] = __builtin_bit_cast(bf16, u);
+        }
   }
   const float c = a.scale_log2;
   LdsOffsets<D> lo;
@@ -453,6 +479,55 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
           pk[cs & 1][1] = pack8(pv16[cs & 1], 1);
           sk[cs & 1][0] = pack8(gs16[cs & 1], 0);
           sk[cs & 1][1] = pack8(gs16[cs & 1], 1);
+          if constexpr (ATOM) {
+            // G_S of this chunk as hi + lo bf16, row key l32 of the wave's scratch
+            // (columns = the chunk's 32 query rows): register r is row 8(r/4) + 4h32 + r%4
+            bf16* gt = Gt + kw * 2048;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              bf16x4 hi4, lo4;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const float x = gs16[cs & 1][4 * g4 + t];
+                hi4[t] = (bf16)x;
+                lo4[t] = (bf16)(x - (float)hi4[t]);
+              }
+              *reinterpret_cast<bf16x4*>(gt + l32 * 32 + 8 * g4 + 4 * h32) = hi4;
+              *reinterpret_cast<bf16x4*>(gt + 1024 + l32 * 32 + 8 * g4 + 4 * h32) = lo4;
+            }
+            // A operands (lane = query row l32, keys 16s + 8h32 + 0..7) by transpose reads:
+            // 16-lane group gi covers rows 16(gi%2) .. +15 and keys 8(gi/2) + {0..3, 4..7}
+            const int gi = lane >> 4, i16 = lane & 15;
+            bf16x8 ah[2], al[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const int k0 = 16 * s2 + 8 * (gi >> 1) + (i16 >> 2);
+              const int col = 16 * (gi & 1) + 4 * (i16 & 3);
+#pragma unroll
+              for (int part = 0; part < 2; ++part) {
+                const bf16* base = gt + part * 1024;
+                const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(base + k0 * 32 + col));
+                const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(base + (k0 + 4) * 32 + col));
+                (part ? al : ah)[s2] = cat8(x0, x1);
+              }
+            }
+            // the chunk's rows of G_Q (query head of the unit's item), C layout
+            // [row 8(r/4) + 4h32 + r%4][dim 32db + l32]: 32 consecutive floats per half wave
+            const long row0 = ((bh0 + A_cur.hh) * (long)(a.T * TILE) + q0A + 32 * cs) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              f32x16 acc = mfma32(ah[0], kT[db][0], f32x16{});
+              acc = mfma32(ah[1], kT[db][1], acc);
+              acc = mfma32(al[0], kT[db][0], acc);
+              acc = mfma32(al[1], kT[db][1], acc);
+              float* dst = a.dqacc + row0 + 32 * db + l32;
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                atomicAdd(dst + (long)(8 * (r >> 2) + 4 * h32 + (r & 3)) * D, acc[r]);
+            }
+          }
         }
       });
       __builtin_amdgcn_sched_barrier(0);

@@ -228,6 +228,27 @@ int backlite_bwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                  uint16_t* dQ, uint16_t* dK, uint16_t* dV,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Fused single-pass variant of backlite_bwd with an fp32-atomic G_Q (the
+ * FlashAttention-style alternative to a second pass over each query tile's
+ * key tiles, "Flash Attention Backward Pass" of the tutorial computes dQ per
+ * query block instead): the G_K/G_V pass also multiplies each kept tile's
+ * G_S (bf16 hi + lo parts) by its K rows and adds the result to an fp32
+ * accumulator with global atomics; a conversion pass writes G_Q = scale * acc
+ * in bf16.  128-row query tiles only.  The atomics' order varies, so G_Q is
+ * not bit-reproducible (G_K, G_V are, and equal backlite_bwd's).  workspace:
+ * at least backlite_bwd_atomic_workspace_bytes() = the base workspace plus an
+ * fp32 [B, H, 128 ceil(n/128), d] accumulator.  Other arguments, layouts and
+ * errors as backlite_bwd.  Measured slower than backlite_bwd on the workloads
+ * here (the accumulator's atomic traffic); kept as the measured alternative. */
+size_t backlite_bwd_atomic_workspace_bytes(int B, int H, int H_k, int n, int d);
+int backlite_bwd_atomic(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                        const uint16_t* O, const uint16_t* O_lo, const uint16_t* dO, const float* lse_row,
+                        const int32_t* qcnt, const uint16_t* qidx,
+                        const int32_t* kcnt, const uint16_t* kidx,
+                        int B, int n, int H, int H_k, int d, float scale, int causal, int window,
+                        uint16_t* dQ, uint16_t* dK, uint16_t* dV,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Allocation-free backward, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same computation as backlite_bwd with a workspace of the base

@@ -397,3 +397,22 @@ def test_stats_counters():
     m = bl.mask(r["tl"], r["lse"], w.n, w.causal, NEGL, stats=st)
     s = st.cpu().tolist()
     assert s[0] == w.B * w.H * 64 and s[1] == int(m["keep"].sum().item())
+
+
+@pytest.mark.parametrize("w", [CASES[0], CASES[1], CASES[2], CASES[5]], ids=[IDS[0], IDS[1], IDS[2], IDS[5]])
+def test_backward_atomic_gq_variant(w):
+    """The fused single-pass variant with an fp32-atomic G_Q: G_K and G_V equal
+    the two-pass backward's bit for bit (the same G_K/G_V pass), G_Q matches the
+    oracle on the same mask and the two-pass G_Q to fp32 summation order."""
+    r = _setup(w)
+    bl, x, xg = r["bl"], r["x"], r["xg"]
+    keep = orc.mask_from_stats(r["ref"]["tile_lse"], r["ref"]["lse"], w.n, w.causal, NEGL)
+    lists = lists_to_torch(keep, r["dev"])
+    a = bl._lib.bwd_atomic(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], lists, causal=w.causal,
+                           o_lo=r["olo"])
+    b = _bwd_path(r, lists, "recompute")
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+    assert torch.equal(a[2].view(torch.int16), b[2].view(torch.int16))
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal)
+    rl, cs = assert_close_grad("dQ", a[0].cpu(), g["dQ"])
+    flush_print(f"  atomic dQ rel-L2 {rl:.2e} cos {cs:.6f}; vs two-pass {orc.rel_l2(a[0].cpu(), orc.to_f64(b[0].cpu())):.1e}")
