@@ -6,13 +6,17 @@
 //   C (32x32):      lane holds C[m = 8(r/4) + 4h + r%4][n = l % 32], r = 0..15
 //
 // LDS tiles hold 128 rows x D bf16, row-major, in 16-byte chunks.  Chunk c of
-// row r is stored at chunk position c ^ swz<D>(r).  For D = 128 swz(r) =
-// 8(r%2) + (r/2)%8; for D = 64 (8 chunks per row) swz(r) = 2(r%4) + (r/4)%2.
-// Measured on MI355X, these keep both access patterns below near the LDS peak:
-// 32 lanes reading one chunk of 32 consecutive rows (ds_read_b128), and 16-lane
-// groups reading 4 consecutive rows x 32 bytes (ds_read_b64_tr_b16).  swz depends
-// on r % 16 only, so shifting a read by a multiple of 16 rows is a constant
-// offset.
+// row r is stored at chunk position c ^ swz<D>(r).  For D = 128 (16 chunks, one
+// 256-byte row of the 64 LDS banks) swz(r) = 4(r%4) + (r/4)%4: any 16
+// consecutive rows (from a multiple of 16) take 16 distinct positions, so 16
+// lanes reading one chunk of 16 rows (ds_read_b128) hit every bank once, and
+// rows 4j .. 4j+3 put an aligned group of 4 chunks into 4 different bank
+// quarters, so 32 lanes reading 4 rows x 64 bytes (two 16-lane groups of
+// ds_read_b64_tr_b16) are conflict-free as well.  (An earlier swz, 8(r%2) +
+// (r/2)%8, left rows r and r+2 in the same quarter: two-way conflicts on every
+// transpose read, a third of the forward's LDS cycles on MI355X.)  For D = 64
+// (8 chunks per row) swz(r) = 2(r%4) + (r/4)%2.  swz depends on r % 16 only, so
+// shifting a read by a multiple of 16 rows is a constant offset.
 //
 // ds_read_b64_tr_b16 (transpose read, per 16-lane group): lane i of the group
 // supplies the address of 4 bf16 at (row k0 + i/4, col n0 + 4(i%4)); lane j of
@@ -45,7 +49,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 1) << 3) | ((r >> 1) & 7);
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 
@@ -143,22 +147,6 @@ __device__ __forceinline__ bf16x8 pack8_lo(const f32x16& c, int s, float& lo) {
   return o;
 }
 
-// Copy a [128 x D] bf16 tile from global rows (row r at src + r*stride
-// elements) into a swizzled LDS tile; rows >= nvalid are zero-filled.
-template <int D, int NT>
-__device__ __forceinline__ void load_tile(bf16* tile, const uint16_t* src, long stride, int nvalid,
-                                          int tid) {
-  constexpr int CH = D / 8;
-#pragma unroll
-  for (int it = 0; it < TILE * CH / NT; ++it) {
-    const int c = tid + it * NT;
-    const int row = c / CH, ch = c % CH;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < nvalid) v = *reinterpret_cast<const u32x4*>(src + (long)row * stride + ch * 8);
-    *reinterpret_cast<u32x4*>(tile + tile_off<D>(row, ch)) = v;
-  }
-}
-
 // Asynchronous copies global -> LDS with the load-to-LDS instructions: the
 // wave's 64 lanes fill 64 consecutive LDS slots (slot = lane).  Two encodings:
 // the buffer form (buffer_load_dword{,x4} ... lds) and the global form
@@ -218,11 +206,15 @@ struct DmaOffsets {
   }
 };
 
+// With the buffer form, `range` (bytes from src) bounds the copy: chunks at or
+// past it read as zero, so a ragged tile is copied with range = (nvalid - 1) *
+// row stride + D elements, and its padding rows arrive zero-filled.
 template <int D, int NT, bool BUF>
-__device__ __forceinline__ void dma_tile(bf16* tile, const uint16_t* src, const DmaOffsets<D, NT>& o, int tid) {
+__device__ __forceinline__ void dma_tile(bf16* tile, const uint16_t* src, const DmaOffsets<D, NT>& o, int tid,
+                                         uint32_t range = 0x7FFFFFFFu) {
   constexpr int NW = NT / 64;
   const int wave = tid >> 6;
-  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, range);
 #pragma unroll
   for (int i = 0; i < DmaOffsets<D, NT>::NI; ++i) {
     const int slot0 = (i * NW + wave) * 64;  // first slot of this wave instruction

@@ -13,8 +13,12 @@
 // tile.
 //
 // Work decomposition (gfx950): one workgroup of 8 waves (2 per SIMD) per
-// (b, h, pair of query tiles); wave w owns 32 query rows.  S^T = K Q^T is formed with 32x32x16 bf16 MFMA
-// (K from LDS as the A operand, the wave's Q fragment resident in registers as
+// (b, h, pair of query tiles); wave w owns 32 query rows.  The MFMA blocks run
+// at raised wave priority, so the two waves of a SIMD settle into opposite
+// phases and one's MFMAs overlap the other's softmax.  Each 128-key tile is
+// consumed in two halves of 64 keys, which keeps S at 32 registers per lane and
+// leaves room for LDS operand reads issued several MFMAs ahead.  S^T = K Q^T is
+// formed with 32x32x16 bf16 MFMA (K from LDS as the A operand, the wave's Q fragment resident in registers as
 // B), so each lane holds one query row and the row reductions stay in-lane
 // plus one exchange between the two lane halves.  O^T += V^T P^T takes P^T
 // straight from the S^T accumulators and V^T from the row-major V tile with the
@@ -47,32 +51,30 @@ __device__ __forceinline__ int window_kt_lo(int qt, int window) {
   return (window == 0 || first <= 0) ? 0 : first / TILE;
 }
 
-// Stage one K and one V tile of keys key0 .. key0+127 into LDS: asynchronously
-// when the tile is full, else synchronously with zero-filled padding rows.
-template <int D, int NT>
-__device__ __forceinline__ void stage_kv(bf16* Ks, bf16* Vs, const uint16_t* kbase, const uint16_t* vbase,
-                                         long stride, const DmaOffsets<D, NT>& dmo, int key0, int n, int tid) {
-  if (key0 + TILE <= n) {
-    dma_tile<D, NT, false>(Ks, kbase + (long)key0 * stride, dmo, tid);
-    dma_tile<D, NT, false>(Vs, vbase + (long)key0 * stride, dmo, tid);
-  } else {
-    load_tile<D, NT>(Ks, kbase + (long)key0 * stride, stride, n - key0, tid);
-    load_tile<D, NT>(Vs, vbase + (long)key0 * stride, stride, n - key0, tid);
-  }
-}
-
 // One workgroup of 8 waves per (b, h, pair of query tiles 2p, 2p+1); wave w owns
-// rows 32(w%4) .. +31 of query tile 2p + w/4.  K/V tiles are double-buffered in
-// LDS: the copy of tile kt+1 is in flight while tile kt is consumed.
+// rows 32(w%4) .. +31 of query tile 2p + w/4.  K and V tiles are each
+// double-buffered in LDS.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   constexpr int NT = 512;
   constexpr int NKS = D / 16;  // MFMA k-steps over the head dimension
   constexpr int NDB = D / 32;  // 32-wide blocks of the head dimension
-  __shared__ __attribute__((aligned(16))) bf16 Ks0[TILE * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs0[TILE * D];
-  __shared__ __attribute__((aligned(16))) bf16 Ks1[TILE * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs1[TILE * D];
+  // V stages in the first 64 KiB, then the K stages: every operand read of
+  // either V stage is one per-lane address plus an immediate offset (the
+  // instruction's offset field reaches 64 KiB), and so is every read of either
+  // K stage with the K base folded into the per-lane address, so the MFMA
+  // blocks issue no address arithmetic.  (V takes the low half: it has two
+  // transpose reads per MFMA, K one row read.)  Four separate arrays, not one:
+  // the compiler then knows which stage an asynchronous copy writes, and does
+  // not make the reads of the other stages wait for it.
+  __shared__ __attribute__((aligned(16))) bf16 lds0_v[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 lds1_v[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 lds2_k[TILE * D];
+  __shared__ __attribute__((aligned(16))) bf16 lds3_k[TILE * D];
+  bf16* const Vs0 = lds0_v;
+  bf16* const Vs1 = lds1_v;
+  bf16* const Ks0 = lds2_k;
+  bf16* const Ks1 = lds3_k;
   __shared__ float lse_s[2 * TILE];  // row LSEs of both query tiles (compact statistics)
 
   const int T = a.T;
@@ -85,7 +87,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   const int g = h / (a.H / a.Hk);
   const int n = a.n;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, h32 = lane >> 5;
   const int qt = 2 * p + (wave >> 2);            // this wave's query tile
   const bool active = qt < T;                     // odd T: the last pair has one tile
@@ -135,93 +138,168 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   DmaOffsets<D, NT> dmo;
   dmo.init(kvstride, tid);
 
-  // one visit of key tile kt: prefetch tile kt+1 into the other stage, then
-  // consume tile kt from (Kc, Vc).  Called with static stage arrays so that the
-  // compiler sees the prefetch target and the operands as distinct objects.
-  auto visit = [&](int kt, const bf16* Kc, const bf16* Vc, bf16* Kn, bf16* Vn) {
-    wait_vmem();
-    __syncthreads();  // tile kt is in (Kc, Vc); nobody reads (Kn, Vn) any more
-    if (kt + 1 < nkt) stage_kv<D, NT>(Kn, Vn, kbase, vbase, kvstride, dmo, (kt + 1) * TILE, n, tid);
-    if (!active || (CAUSAL && (kt > qt || kt < kt_lo))) return;  // wave-uniform
-    const int key0 = kt * TILE;
+  // Main loop: one barrier per key tile.  The copies of K and V of tile t+1 are
+  // issued right after the barrier and have the whole visit of tile t to land;
+  // the two waves of a SIMD run freely between barriers, so one's MFMAs overlap
+  // the other's softmax.  Each tile is consumed in two halves of 64 keys
+  // (scores, softmax, O update each), which keeps S at 32 registers and leaves
+  // room for operand reads issued well ahead of their MFMAs.
+  const int N = nkt - kt0;
+  // The tile statistic is stored after the next barrier: the barrier waits for
+  // all of the wave's memory operations, stores included, and a store issued
+  // just before it would stall the wave for the whole write latency.
+  float tl_val = 0.f;
+  int tl_idx = 0;
+  bool tl_pend = false;
+  auto flush_tl = [&]() __attribute__((always_inline)) {
+    if (tl_pend) {
+      if (h32 == 0) tl_row[tl_idx] = tl_val;
+      tl_pend = false;
+    }
+  };
+  auto mine = [&](int t) __attribute__((always_inline)) -> bool {  // wave-uniform
+    const int kt = kt0 + t;
+    return active && !(CAUSAL && (kt > qt || kt < kt_lo));
+  };
+  // one K or V tile into LDS, asynchronously; the rows of a ragged last tile
+  // past n arrive zero-filled (the copy's range ends at the last valid row), so
+  // every tile takes the same path
+  auto stage_one = [&](bf16* dst, const uint16_t* base, int key0) __attribute__((always_inline)) {
+    const int nv = min(TILE, n - key0);
+    const uint32_t range = (uint32_t)(((long)(nv - 1) * kvstride + D) * 2);
+    dma_tile<D, NT, true>(dst, base + (long)key0 * kvstride, dmo, tid, range);
+  };
 
-    // S^T for the 4 key blocks of 32
-    f32x16 s[4];
+  f32x16 s[2];      // S^T of one 64-key half: key blocks 2hh, 2hh+1
+  bf16x8 pb[2][2];  // its probabilities, packed as B operands
+  float ts = 0.f;   // the tile's row sum so far (relative to m_run)
+  // S^T = K Q^T for key blocks 2hh, 2hh+1.  The K operands of k-step ks+1 are
+  // read before the MFMAs of k-step ks.
+  auto scores = [&](const bf16* Kc, int hh) __attribute__((always_inline)) {
+    bf16x8 kr[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16{};
+    for (int j = 0; j < 2; ++j) kr[0][j] = rd_row<D>(Kc, lo, 2 * hh + j, 0);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 1 < NKS) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)  // four independent accumulators back to back
-        s[kb] = mfma32(rd_row<D>(Kc, lo, kb, ks), qf[ks], s[kb]);
-    // mask padded keys (last tile) and, on the diagonal tile, keys after the row
-    // (and, with a sliding window, keys at or below row - window)
-    const bool need_mask = (key0 + TILE > n) || (CAUSAL && (kt == qt || key0 <= wedge_kt));
+        for (int j = 0; j < 2; ++j) kr[(ks + 1) & 1][j] = rd_row<D>(Kc, lo, 2 * hh + j, ks + 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) s[j] = mfma32(kr[ks & 1][j], qf[ks], ks ? s[j] : f32x16{});
+    }
+    // keep the reads three k-steps ahead of their MFMAs
+    sched_interleave<6, NKS - 3, 2, 2, 6>();
+  };
+  // softmax of half hh of tile t: mask, running maximum (lazy rescale), the
+  // probabilities, row sums; P^T packed into pb
+  auto softmax = [&](int t, int hh) __attribute__((always_inline)) {
+    const int key0 = (kt0 + t) * TILE + 64 * hh;
+    // mask padded keys and, on the diagonal, keys after the row (and, with a
+    // sliding window, keys at or below row - window)
+    const bool need_mask = (key0 + 64 > n) || (CAUSAL && (key0 + 63 > qt * TILE || key0 <= wedge_kt));
     if (need_mask) {
-      // register r of block kb holds key key0 + 4*h32 + off, off = 32kb + 8(r/4) + r%4;
+      // register r of block j holds key key0 + 4*h32 + off, off = 32j + 8(r/4) + r%4;
       // it is kept iff lo_off < off <= hi_off
       const int hi_off = (CAUSAL ? min(qrow, n - 1) : n - 1) - (key0 + 4 * h32);
       const int lo_off = (CAUSAL && a.window) ? (qrow - a.window) - (key0 + 4 * h32) : -(1 << 30);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-          s[kb][r] = (off <= hi_off && off > lo_off) ? s[kb][r] : -INFINITY;
+          const int off = j * 32 + 8 * (r >> 2) + (r & 3);
+          s[j][r] = (off <= hi_off && off > lo_off) ? s[j][r] : -INFINITY;
         }
     }
     float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[j][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // Lazy rescaling: the running maximum (and with it O and l) moves only when
-    // some row's maximum grows by more than 2^8; otherwise the tile's
-    // probabilities are taken against the old maximum (at most 2^8, exact in
-    // fp32 and in the bf16 operand's relative precision).  Every quantity is
-    // m + log2(sum 2^(s - m)) for whichever m is used, so the result is the same
-    // softmax; the wave skips the rescale of its O accumulators in most tiles.
+    // Lazy rescaling: the running maximum (and with it O, l and the tile's
+    // partial sum) moves only when some row's maximum grows by more than 2^8;
+    // otherwise the probabilities are taken against the old maximum (at most
+    // 2^8, exact in fp32 and in the bf16 operand's relative precision).  Every
+    // quantity is m + log2(sum 2^(s - m)) for whichever m is used, so the
+    // result is the same softmax; the rescale of O is skipped in most halves.
     const float m_cand = fmaxf(m_run, mt * c);
     if (__any(m_cand - m_run > 8.f)) {
       const float alpha = fast_exp2(m_run - m_cand);
       l_run *= alpha;
+      ts *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
       m_run = m_cand;
     }
-    float ts = 0.f;
+    float hs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(fmaf(s[kb][r], c, -m_run));
-        s[kb][r] = pv;
-        ts += pv;
+        const float pv = fast_exp2(fmaf(s[j][r], c, -m_run));
+        s[j][r] = pv;
+        hs += pv;
       }
-    ts += __shfl_xor(ts, 32);
-    l_run += ts;
-    if (tl_row && h32 == 0) {
-      const float t = (qrow < n) ? (m_run + __log2f(ts)) * LN2 : -INFINITY;
-      tl_row[pair_index(qt, kt, T, CAUSAL) * TILE + lrow] = t;
-    }
-    // O^T += V^T P^T.  Step st of key block kb covers keys 32kb + 16st + 4*h32 + 0..3
-    // and 32kb + 16st + 8 + 4*h32 + 0..3, i.e. C registers 8st .. 8st+7.
+    hs += __shfl_xor(hs, 32);
+    l_run += hs;
+    ts += hs;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 pb = pack8(s[kb], st);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(rd_tr<D>(Vc, lo, kb, st, db), pb, oacc[db]);
-      }
+      for (int st = 0; st < 2; ++st) pb[j][st] = pack8(s[j], st);
   };
-
-  stage_kv<D, NT>(Ks0, Vs0, kbase, vbase, kvstride, dmo, kt0 * TILE, n, tid);
-  for (int kt = kt0; kt < nkt; kt += 2) {
-    visit(kt, Ks0, Vs0, Ks1, Vs1);
-    if (kt + 1 < nkt) visit(kt + 1, Ks1, Vs1, Ks0, Vs0);
+  // O^T += V^T P^T over key blocks 2hh, 2hh+1.  Step st of block kb covers keys
+  // 32kb + 16st + 4*h32 + 0..3 and 32kb + 16st + 8 + 4*h32 + 0..3, i.e. C
+  // registers 8st .. 8st+7.
+  auto update = [&](const bf16* Vc, int hh) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = mfma32(rd_tr<D>(Vc, lo, 2 * hh + j, st, db), pb[j][st], oacc[db]);
+    sched_interleave<12, 4 * NDB - 6, 1, 2, 6>();
+  };
+  auto visit = [&](int t, auto par) __attribute__((always_inline)) {
+    constexpr int PAR = decltype(par)::value;
+    wait_vmem();
+    __syncthreads();  // tile t has landed; every wave is done with tile t-1
+    flush_tl();
+    if (t + 1 < N) {
+      stage_one(PAR ? Ks0 : Ks1, kbase, (kt0 + t + 1) * TILE);
+      stage_one(PAR ? Vs0 : Vs1, vbase, (kt0 + t + 1) * TILE);
+    }
+    if (mine(t)) {
+      ts = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        // MFMA blocks at raised wave priority: a wave that reaches its MFMAs
+        // issues them ahead of the other wave of the SIMD, which meanwhile
+        // does its softmax, so the two drift into opposite phases
+        __builtin_amdgcn_s_setprio(1);
+        scores(PAR ? Ks1 : Ks0, hh);
+        __builtin_amdgcn_s_setprio(0);
+        softmax(t, hh);
+        __builtin_amdgcn_s_setprio(1);
+        update(PAR ? Vs1 : Vs0, hh);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      if (tl_row) {
+        tl_val = (qrow < n) ? (m_run + __log2f(ts)) * LN2 : -INFINITY;
+        tl_idx = (int)pair_index(qt, kt0 + t, T, CAUSAL) * TILE + lrow;
+        tl_pend = true;
+      }
+    }
+  };
+  stage_one(Ks0, kbase, kt0 * TILE);
+  stage_one(Vs0, vbase, kt0 * TILE);
+  for (int t = 0; t < N; t += 2) {
+    visit(t, std::integral_constant<int, 0>{});
+    if (t + 1 < N) visit(t + 1, std::integral_constant<int, 1>{});
   }
+  flush_tl();
 
   // epilogue: normalise, stage O (and its residual) through LDS as [row][dim],
   // store coalesced.  Query tile 2p + j uses Ks[j] / Vs[j].
