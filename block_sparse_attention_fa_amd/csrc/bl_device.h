@@ -263,10 +263,10 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // own L2); measured on MI355X, the plain order (consecutive workgroups = tiles
 // of the same head, so the whole chip works through one head's K/V or Q/G_O
 // at a time and the 256 MB Infinity Cache holds it) beats grouping each head
-// on one XCD by 20% in the backward, so no remapping is applied.
+// on one XCD by 20% in the backward, so no remapping is applied.  (A finer
+// grouping, 32 consecutive key tiles per XCD within each chip-wide group of
+// 256, measured no change in the G_K/G_V pass either: 12.96 vs 12.93 ms.)
 __device__ __forceinline__ int work_index(int bid) { return bid; }
-
-
 __device__ __forceinline__ long pair_index(int qt, int kt, int T, bool causal) {
   return causal ? (long)qt * (qt + 1) / 2 + kt : (long)qt * T + kt;
 }
