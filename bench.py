@@ -49,7 +49,10 @@ def parse():
                     help="sliding window of a causal workload (key j visible to query i iff i - window < j <= i)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-rows", type=int, default=20480,
-                    help="query rows of head 0 in the oracle's timed sample")
+                    help="query rows per sampled head in the oracle's timed sample")
+    ap.add_argument("--cpu-heads", default=None,
+                    help="comma-separated query heads the oracle is timed on (default: every head up to 8k "
+                         "tokens, else the first, middle and last head, or first and last with H < 16)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-backward comparison")
     ap.add_argument("--grad-check", action="store_true",
                     help="report cosine and rel-L2 of the sparse gradients against the dense (negl_prob = 0) ones")
@@ -99,46 +102,66 @@ def visible_pairs(rows, window):
     return window * (window + 1) / 2 + (rows - window) * float(window)
 
 
-def cpu_baseline(w, x_h0, negl, rows, window=0):
-    """fp64 oracle on head 0, query rows [0, rows): forward, mask and backward of
-    those rows against all keys.  Rate = dense-equivalent backward FLOP of the
-    sample / the oracle's backward seconds."""
+def default_cpu_heads(w):
+    if w.n <= 8192:
+        return list(range(w.H))
+    return [0, w.H // 2, w.H - 1] if w.H >= 16 else [0, w.H - 1]
+
+
+def cpu_baseline(w, x_cpu, heads, negl, rows, window=0):
+    """fp64 oracle on the sampled query heads, query rows [0, rows) of each:
+    forward, mask and backward of those rows against all keys.  Rate = the
+    sample's dense-equivalent backward FLOP / the oracle's backward seconds;
+    the full job's oracle backward time is extrapolated from that rate (x H
+    heads and the full row count)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import backlite_oracle as orc
-    q, k, v, do = (orc.to_f64(x_h0[nm]) for nm in ("q", "k", "v", "do"))
     n, d = w.n, w.d
     rows = min(rows, n)
     rr = np.arange(rows)
-    t0 = time.perf_counter()
-    f = orc.forward(q, k, v, causal=w.causal, rows=rr, window=window)
-    t1 = time.perf_counter()
-    # tile weights / selection on the sampled query tiles only
     nt = (rows + TILE - 1) // TILE
-    tl = np.full((1, 1, n, f["tile_lse"].shape[-1]), -np.inf)
-    ls = np.zeros((1, 1, n))
-    tl[:, :, :rows] = f["tile_lse"]
-    ls[:, :, :rows] = f["lse"]
-    a = orc.tile_log_weights(tl, ls, n, w.causal, window=window)
-    cand = orc.candidates(n, w.causal, window=window).copy()
-    cand[nt:] = False                       # only the sampled query tiles
-    keep = orc.select_keep(a, cand, negl)
-    t2 = time.perf_counter()
-    orc.backward(q, k, v, do, keep=keep, causal=w.causal, q_rows=rr, window=window)
-    t3 = time.perf_counter()
-    # dense-equivalent: every (row, key) pair the causal rule (and window) allows
-    flops = 10.0 * d * (visible_pairs(rows, window) if w.causal else rows * n)
+    per_head = []
+    fl_total = 0.0
+    for j, h in enumerate(heads):
+        q, k, v, do = (orc.to_f64(x_cpu[nm][:, :, j:j + 1]) for nm in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        f = orc.forward(q, k, v, causal=w.causal, rows=rr, window=window)
+        t1 = time.perf_counter()
+        # tile weights / selection on the sampled query tiles only
+        tl = np.full((1, 1, n, f["tile_lse"].shape[-1]), -np.inf)
+        ls = np.zeros((1, 1, n))
+        tl[:, :, :rows] = f["tile_lse"]
+        ls[:, :, :rows] = f["lse"]
+        a = orc.tile_log_weights(tl, ls, n, w.causal, window=window)
+        cand = orc.candidates(n, w.causal, window=window).copy()
+        cand[nt:] = False                       # only the sampled query tiles
+        keep = orc.select_keep(a, cand, negl)
+        t2 = time.perf_counter()
+        orc.backward(q, k, v, do, keep=keep, causal=w.causal, q_rows=rr, window=window)
+        t3 = time.perf_counter()
+        per_head.append((h, t1 - t0, t2 - t1, t3 - t2))
+        # dense-equivalent: every (row, key) pair the causal rule (and window) allows
+        fl_total += 10.0 * d * (visible_pairs(rows, window) if w.causal else rows * n)
+        log(f"[bench] oracle head {h}: forward {t1 - t0:.2f} s, mask {t2 - t1:.2f} s, backward {t3 - t2:.2f} s")
+    bwd_s = sum(p[3] for p in per_head)
+    rate = fl_total / bwd_s / 1e12
+    full_fl = 10.0 * d * w.B * w.H * (visible_pairs(n, window) if w.causal else float(n) * n)
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     return {
-        "value": flops / (t3 - t2) / 1e12,
+        "value": rate,
         "unit": "TFLOP/s (dense-equivalent backward)",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"head 0, query rows 0-{rows - 1} of the {w.name} problem against all {n} keys, fp64 numpy: "
-                   f"forward {t1 - t0:.2f} s, mask {t2 - t1:.2f} s, backward {t3 - t2:.2f} s"),
-        "bwd_s": t3 - t2,
-        "fwd_s": t1 - t0,
+        "sample": (f"query heads {','.join(str(h) for h in heads)}, rows 0-{rows - 1} of each, of the {w.name} "
+                   f"problem against all {n} keys, fp64 numpy; per head (forward / mask / backward s): "
+                   + "; ".join(f"h{h} {a:.2f}/{b:.2f}/{c:.2f}" for h, a, b, c in per_head)),
+        "heads": list(heads),
+        "rows_per_head": rows,
+        "bwd_s": bwd_s,
+        "fwd_s": sum(p[1] for p in per_head),
+        "full_job_bwd_s_extrapolated": full_fl / (rate * 1e12),
     }
 
 
@@ -169,8 +192,12 @@ def main():
     t = time.time()
     x = make_inputs(w)
     log(f"[bench] inputs generated in {time.time() - t:.1f} s")
-    x_h0 = {nm: x[nm][:, :, :1].contiguous() for nm in ("q", "do")}
-    x_h0.update({nm: x[nm][:, :, :1].contiguous() for nm in ("k", "v")})
+    cpu_heads = ([int(h) for h in args.cpu_heads.split(",")] if args.cpu_heads else default_cpu_heads(w))
+    if any(h < 0 or h >= H for h in cpu_heads):
+        sys.exit(f"--cpu-heads {args.cpu_heads}: heads must lie in [0, {H})")
+    # the oracle's sample: the chosen query heads and their key/value heads
+    x_cpu = {nm: x[nm][:, :, cpu_heads].contiguous() for nm in ("q", "do")}
+    x_cpu.update({nm: x[nm][:, :, [h // (H // Hk) for h in cpu_heads]].contiguous() for nm in ("k", "v")})
     q, k, v, do = (x[nm].to(dev) for nm in ("q", "k", "v", "do"))
     del x
     T = (n + TILE - 1) // TILE
@@ -423,8 +450,8 @@ def main():
             f"{q64['sparsity']:.3f}  speedup vs dense {q64['bwd_speedup_vs_dense']:.2f}x")
     if args.cpu_baseline == "on":
         del q, k, v, do, tl, ws, dq, dk, dv
-        log(f"[bench] oracle CPU baseline on {args.cpu_rows} rows of head 0 ...")
-        out["cpu_baseline"] = cpu_baseline(w, x_h0, negl, args.cpu_rows, win)
+        log(f"[bench] oracle CPU baseline on {min(args.cpu_rows, n)} rows of heads {cpu_heads} ...")
+        out["cpu_baseline"] = cpu_baseline(w, x_cpu, cpu_heads, negl, args.cpu_rows, win)
     print(json.dumps(out), flush=True)
 
 
