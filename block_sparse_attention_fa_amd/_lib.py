@@ -228,6 +228,8 @@ def bwd_state(workspace, B, H, Hk, n, d) -> tuple:
     """(all kept tiles had a slot, kept tile pairs, kept tiles with a slot) from
     the state words of a workspace the last backward used (synchronises)."""
     off = bwd_state_offset(B, H, Hk, n, d)
+    if workspace.numel() < off + 12:
+        raise ValueError("bwd_state: the workspace has no G_S slots (a recompute-only workspace keeps no state words)")
     w = workspace[off:off + 12].view(torch.int32).tolist()
     return bool(w[0]), int(w[1]), int(w[2])
 
