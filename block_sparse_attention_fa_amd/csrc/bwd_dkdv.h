@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
     // TileSched; chunk c's softmax (exp, mask, G_S) is spread over the MFMAs
     // between A(c) and B(c) so the VALU work hides under the matrix pipe.
     // Operands stream through a 4-slot ring fetched 3 MFMAs ahead;
-    // sched_barrier fences keep that order.
+    // a sched_barrier fence before each MFMA keeps that order.
     using SC = TileSched<2 * NKS, 4 * NDB>;
     constexpr int NSTEP = SC::total;
     constexpr int LB = 4 * NDB;
@@ -532,7 +532,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
           }
         }
       });
-      __builtin_amdgcn_sched_barrier(0);
+      // (no fence after the step: the next step's operand read and copy may be
+      // scheduled among this step's VALU work; measured 2.4% faster than
+      // fencing both sides)
     });
     A_cur = A_nxt;
     B_cur = B_nxt;
