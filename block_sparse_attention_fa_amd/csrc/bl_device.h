@@ -147,14 +147,13 @@ __device__ __forceinline__ bf16x8 pack8_lo(const f32x16& c, int s, float& lo) {
   return o;
 }
 
-// Asynchronous copies global -> LDS with the load-to-LDS instructions: the
-// wave's 64 lanes fill 64 consecutive LDS slots (slot = lane).  Two encodings:
-// the buffer form (buffer_load_dword{,x4} ... lds) and the global form
-// (global_load_lds_dword{,x4}).  With the buffer form the compiler keeps
-// counting LDS reads precisely while a copy is in flight; the global form
-// makes it wait for every outstanding LDS read at each use, so kernels whose
-// LDS reads are scheduled ahead of their MFMAs take the buffer form.
-// Completion either way: s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
+// Asynchronous copies global -> LDS with the load-to-LDS instructions, in
+// their buffer form (buffer_load_dword{,x4} ... lds): the wave's 64 lanes fill
+// 64 consecutive LDS slots (slot = lane).  With the buffer form the compiler
+// keeps counting LDS reads precisely while a copy is in flight; with the
+// global form (global_load_lds_dword{,x4}) it made every MFMA wait for all
+// outstanding LDS reads, so only the buffer form is used.  Completion:
+// s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
 // raw buffer resource: stride 0, `range` bytes (loads at or past it read 0), dword format word
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t range = 0x7FFFFFFFu) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)range, 0x00020000);
@@ -163,27 +162,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 typedef __attribute__((address_space(3))) char lds_byte;
 __device__ __forceinline__ lds_byte* lds_ptr(const void* p) { return (lds_byte*)(p); }
 
-#define BL_LOAD_LDS(BYTES)                                                                                 \
-  if constexpr (BUF) {                                                                                     \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, BYTES, boff, 0, 0, 0);                               \
-  } else {                                                                                                 \
-    __builtin_amdgcn_global_load_lds(                                                                      \
-        (__attribute__((address_space(1))) void*)(reinterpret_cast<const char*>(base) + boff), lds, BYTES,  \
-        0, 0);                                                                                             \
-  }
-// one lane's share of a load-to-LDS instruction: bytes at base + boff land in
-// slot `lane` of the LDS block at lds
-template <bool BUF>
-__device__ __forceinline__ void load_lds16(const __amdgpu_buffer_rsrc_t& rs, const void* base, lds_byte* lds,
-                                           uint32_t boff) {
-  BL_LOAD_LDS(16)
+// one lane's share of a load-to-LDS instruction: bytes at boff of the buffer
+// land in slot `lane` of the LDS block at lds
+__device__ __forceinline__ void load_lds16(const __amdgpu_buffer_rsrc_t& rs, lds_byte* lds, uint32_t boff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, boff, 0, 0, 0);
 }
-template <bool BUF>
-__device__ __forceinline__ void load_lds4(const __amdgpu_buffer_rsrc_t& rs, const void* base, lds_byte* lds,
-                                          uint32_t boff) {
-  BL_LOAD_LDS(4)
+__device__ __forceinline__ void load_lds4(const __amdgpu_buffer_rsrc_t& rs, lds_byte* lds, uint32_t boff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 4, boff, 0, 0, 0);
 }
-#undef BL_LOAD_LDS
 
 // Asynchronous copy of a full [128 x D] bf16 tile (every row valid) into a
 // swizzled LDS tile: lane l fetches the global chunk that belongs at its slot,
@@ -206,10 +192,10 @@ struct DmaOffsets {
   }
 };
 
-// With the buffer form, `range` (bytes from src) bounds the copy: chunks at or
-// past it read as zero, so a ragged tile is copied with range = (nvalid - 1) *
-// row stride + D elements, and its padding rows arrive zero-filled.
-template <int D, int NT, bool BUF>
+// `range` (bytes from src) bounds the copy: chunks at or past it read as
+// zero, so a ragged tile is copied with range = (nvalid - 1) * row stride + D
+// elements, and its padding rows arrive zero-filled.
+template <int D, int NT>
 __device__ __forceinline__ void dma_tile(bf16* tile, const uint16_t* src, const DmaOffsets<D, NT>& o, int tid,
                                          uint32_t range = 0x7FFFFFFFu) {
   constexpr int NW = NT / 64;
@@ -218,16 +204,8 @@ __device__ __forceinline__ void dma_tile(bf16* tile, const uint16_t* src, const 
 #pragma unroll
   for (int i = 0; i < DmaOffsets<D, NT>::NI; ++i) {
     const int slot0 = (i * NW + wave) * 64;  // first slot of this wave instruction
-    load_lds16<BUF>(rs, src, lds_ptr(tile + slot0 * 8), o.off[i]);
+    load_lds16(rs, lds_ptr(tile + slot0 * 8), o.off[i]);
   }
-}
-
-// Asynchronous copy of n32 4-byte words (n32 a multiple of 64) into LDS by one
-// wave: lane l of instruction i lands word 64i + l.
-template <bool BUF>
-__device__ __forceinline__ void dma_words(float* lds, const float* src, int n32, int lane) {
-  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src);
-  for (int i = 0; i < n32 / 64; ++i) load_lds4<BUF>(rs, src, lds_ptr(lds + 64 * i), (uint32_t)(64 * i + lane) * 4u);
 }
 
 // Scheduling hints (instruction classes of __builtin_amdgcn_sched_group_barrier).

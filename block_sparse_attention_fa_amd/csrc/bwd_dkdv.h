@@ -49,8 +49,8 @@ __device__ __forceinline__ void stage_ld(float* Ld, float* Dd, const QgSrc& sa, 
 #pragma unroll
   for (int i = 0; i < TILE / 64; ++i) {
     const QgSrc& s = i ? sb : sa;
-    if (wave == 0) load_lds4<true>(s.l, nullptr, lds_ptr(Ld + 64 * i), (uint32_t)(64 * i + lane) * 4u);
-    if (wave == 1) load_lds4<true>(s.d, nullptr, lds_ptr(Dd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
+    if (wave == 0) load_lds4(s.l, lds_ptr(Ld + 64 * i), (uint32_t)(64 * i + lane) * 4u);
+    if (wave == 1) load_lds4(s.d, lds_ptr(Dd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
   }
 }
 
@@ -62,7 +62,7 @@ __device__ __forceinline__ void stage_qg_part(bf16* Qd, bf16* Gd, const QgSrc& s
   constexpr int NI = DmaOffsets<D, NT>::NI, II = I % NI;
   const QgSrc& s = II < NI / 2 ? sa : sb;  // instruction II covers stage rows 64 II / (NI / 2) ..
   lds_byte* dst = lds_ptr((I < NI ? Qd : Gd) + ((II * (NT / 64) + wave) * 64) * 8);
-  load_lds16<true>(I < NI ? s.q : s.g, nullptr, dst, dmo.off[II]);
+  load_lds16(I < NI ? s.q : s.g, dst, dmo.off[II]);
 }
 
 // The two results of v_permlane16_swap: x receives y's even 16-lane rows in

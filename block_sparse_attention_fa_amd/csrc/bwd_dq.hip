@@ -36,7 +36,7 @@ __device__ __forceinline__ void stage_kv_part(bf16* Kd, bf16* Vd, const KvSrc& s
                                               int wave) {
   constexpr int NI = DmaOffsets<D, NT>::NI, II = I % NI;
   lds_byte* dst = lds_ptr((I < NI ? Kd : Vd) + ((II * (NT / 64) + wave) * 64) * 8);
-  load_lds16<true>(I < NI ? s.k : s.v, nullptr, dst, dmo.off[II]);
+  load_lds16(I < NI ? s.k : s.v, dst, dmo.off[II]);
 }
 
 // the key mean of a staged key tile: wave 0, D / 64 instructions
@@ -44,7 +44,7 @@ template <int D>
 __device__ __forceinline__ void stage_kbar(float* Bd, const KvSrc& s, int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < D / 64; ++i)
-    if (wave == 0) load_lds4<true>(s.m, nullptr, lds_ptr(Bd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
+    if (wave == 0) load_lds4(s.m, lds_ptr(Bd + 64 * i), (uint32_t)(64 * i + lane) * 4u);
 }
 
 // One workgroup of 4 waves (one per SIMD) per (b, h, query tile qt).  Wave w

@@ -112,7 +112,7 @@ template <int D, int NT, int I>
 __device__ __forceinline__ void stage_k_part(bf16* Kd, const __amdgpu_buffer_rsrc_t& rs,
                                              const DmaOffsets<D, NT>& dmo, int wave) {
   lds_byte* dst = lds_ptr(Kd + ((I * (NT / 64) + wave) * 64) * 8);
-  load_lds16<true>(rs, nullptr, dst, dmo.off[I]);
+  load_lds16(rs, dst, dmo.off[I]);
 }
 
 template <int D, int QR>
@@ -210,10 +210,10 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int e = lane + 64 * it;
-      load_lds4<true>(rl, nullptr, lds_ptr(l_of(st) + wave * TILE + 64 * it),
+      load_lds4(rl, lds_ptr(l_of(st) + wave * TILE + 64 * it),
                       (uint32_t)((e >> 5) * QR + 32 * rw + (e & 31)) * 4u);
     }
-    load_lds4<true>(rb, nullptr, lds_ptr(b_of(st) + 64 * kb_part), (uint32_t)(64 * kb_part + lane) * 4u);
+    load_lds4(rb, lds_ptr(b_of(st) + 64 * kb_part), (uint32_t)(64 * kb_part + lane) * 4u);
     static_for<0, NI>([&](auto ic) { stage_k_part<D, NT, decltype(ic)::value>(k_of(st), rk, dmo, wave); });
   };
   // the wave's NGS blocks of item i's G_S into registers: block ib = (kw, s) of

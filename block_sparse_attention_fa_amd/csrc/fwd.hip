@@ -167,7 +167,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdArgs a) {
   auto stage_one = [&](bf16* dst, const uint16_t* base, int key0) __attribute__((always_inline)) {
     const int nv = min(TILE, n - key0);
     const uint32_t range = (uint32_t)(((long)(nv - 1) * kvstride + D) * 2);
-    dma_tile<D, NT, true>(dst, base + (long)key0 * kvstride, dmo, tid, range);
+    dma_tile<D, NT>(dst, base + (long)key0 * kvstride, dmo, tid, range);
   };
 
   f32x16 s[2];      // S^T of one 64-key half: key blocks 2hh, 2hh+1
