@@ -129,11 +129,17 @@ __global__ __launch_bounds__(256) void kmean_kernel(BwdArgs a) {
 // m > CH items makes ceil(m / CH) < 2m / CH chunks, so all split chunks
 // together are fewer than 2 * items / CH <= P.  That bounds the partial slots
 // by P and the chunks by NK + P <= 2 NK without reading anything back.
+// The ragged last key tile (n not a multiple of 128) takes the shorter chunk
+// length CHR = max(minimum, ceil(CH / 4)) when the partial slots still fit P
+// with it (else CHR = CH): in the stored non-causal pass its chunks run in a
+// launch of their own after the main one, where the longest chunk is the
+// launch's whole duration.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void dk_plan_kernel(BwdArgs a) {
   __shared__ long long part[1024];
   __shared__ long long part2[1024];
-  __shared__ int chs;
+  __shared__ int chs, chr;
+  __shared__ long long red2[2][1024];
   const int T = a.T, G = a.H / a.Hk;
   const int NK = a.B * a.Hk * T;
   int32_t* items = a.dkplan + 4 + 8 * NK;
@@ -157,19 +163,40 @@ __global__ __launch_bounds__(1024) void dk_plan_kernel(BwdArgs a) {
     if (tid < off) part[tid] += part[tid + off];
     __syncthreads();
   }
-  if (tid == 0) {
-    const long long total = part[0];
-    const long long P = max(1, min(a.dk_pcap, NK));
-    chs = (int)max((long long)a.dk_chmin, (2 * total + P - 1) / P);
-  }
+  const long long P = max(1, min(a.dk_pcap, NK));
+  if (tid == 0) chs = (int)max((long long)a.dk_chmin, (2 * part[0] + P - 1) / P);
   __syncthreads();
-  const int CH = chs;
+  const bool ragged = T * TILE != a.n;
+  const int CH = chs, CHR0 = max(a.dk_chmin, (CH + 3) / 4);
+  auto split_slots = [](int m, int L) { return m <= L ? 0 : (m + L - 1) / L; };
+  {
+    // partial slots with CH everywhere, and the ragged tiles' extra with CHR0
+    long long ps = 0, px = 0;
+    for (int k = s0; k < s1; ++k) {
+      const int m = items[k];
+      ps += split_slots(m, CH);
+      if (ragged && k % T == T - 1) px += split_slots(m, CHR0) - split_slots(m, CH);
+    }
+    red2[0][tid] = ps;
+    red2[1][tid] = px;
+    __syncthreads();
+    for (int off = 512; off >= 1; off >>= 1) {
+      if (tid < off) {
+        red2[0][tid] += red2[0][tid + off];
+        red2[1][tid] += red2[1][tid + off];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) chr = red2[0][0] + red2[1][0] <= P ? CHR0 : CH;
+    __syncthreads();
+  }
+  const int CHR = chr;
   long long csum = 0, psum = 0;
   for (int k = s0; k < s1; ++k) {
-    const int m = items[k];
-    const int c = m <= CH ? 1 : (m + CH - 1) / CH;
+    const int m = items[k], L = (ragged && k % T == T - 1) ? CHR : CH;
+    const int c = m <= L ? 1 : (m + L - 1) / L;
     csum += c;
-    psum += m <= CH ? 0 : c;
+    psum += m <= L ? 0 : c;
   }
   __syncthreads();
   part[tid] = csum;
@@ -184,18 +211,18 @@ __global__ __launch_bounds__(1024) void dk_plan_kernel(BwdArgs a) {
   }
   long long cr = part[tid] - csum, pr = part2[tid] - psum;
   for (int k = s0; k < s1; ++k) {
-    const int m = items[k];
-    const int c = m <= CH ? 1 : (m + CH - 1) / CH;
+    const int m = items[k], L = (ragged && k % T == T - 1) ? CHR : CH;
+    const int c = m <= L ? 1 : (m + L - 1) / L;
     cbase[k] = (int)cr;
     pbase[k] = (int)pr;
     cr += c;
-    pr += m <= CH ? 0 : c;
+    pr += m <= L ? 0 : c;
   }
   if (tid == 1023) {
     a.dkplan[0] = (int)part[1023];
     a.dkplan[1] = (int)part2[1023];
     a.dkplan[2] = CH;
-    a.dkplan[3] = 0;
+    a.dkplan[3] = CHR;
   }
 }
 
@@ -205,7 +232,7 @@ __global__ __launch_bounds__(256) void dk_fill_kernel(BwdArgs a) {
   const int k = blockIdx.x * 256 + threadIdx.x;
   if (k >= NK) return;
   const int32_t* items = a.dkplan + 4 + 8 * NK;
-  const int m = items[k], cb = items[NK + k], pb = items[2 * NK + k], CH = a.dkplan[2];
+  const int m = items[k], cb = items[NK + k], pb = items[2 * NK + k], CH = dk_chunk_len(a, k);
   int4* tab = reinterpret_cast<int4*>(a.dkplan + 4);
   if (m <= CH) {
     tab[cb] = int4{k, 0, m, -1};
@@ -226,7 +253,7 @@ __global__ __launch_bounds__(256) void dk_reduce_kernel(BwdArgs a) {
   const int NK = a.B * a.Hk * T;
   const int k = blockIdx.x / DK_RS, sl = blockIdx.x % DK_RS;
   const int32_t* items = a.dkplan + 4 + 8 * NK;
-  const int m = items[k], CH = a.dkplan[2];
+  const int m = items[k], CH = dk_chunk_len(a, k);
   if (m <= CH) return;
   const int c = (m + CH - 1) / CH, pb = items[2 * NK + k];
   const int kt = k % T, bg = k / T;

@@ -31,7 +31,7 @@ struct BwdArgs {
   float* gsl;          // per slot, [4 key quarters][qrows rows] sums of the G_S rounding residual
   long long gs_cap;    // slots available
   // Chunked G_K/G_V work (always present): header [4] = {chunks, partial slots,
-  // chunk length, -}, then the chunk table int4 [2 * NK] = {key tile (b, g, kt)
+  // chunk length, chunk length of the ragged last key tile}, then the chunk table int4 [2 * NK] = {key tile (b, g, kt)
   // index, first item, end item, partial slot or -1}, then per key tile the
   // item count, first chunk and first partial slot (int32 [NK] each), where
   // NK = B * Hk * T.
@@ -46,6 +46,20 @@ struct BwdArgs {
   float scale;
   float scale_log2;
 };
+
+// Chunk length of key tile k's G_K/G_V list in the plan (header word 2; word 3
+// for the ragged last key tile when n is not a multiple of 128).
+__device__ inline int dk_chunk_len(const BwdArgs& a, int k) {
+  return (k % a.T == a.T - 1 && a.T * TILE != a.n) ? a.dkplan[3] : a.dkplan[2];
+}
+
+// Most chunks one key tile's G_K/G_V list can split into: the list holds at
+// most G * Tq items (every query tile of every head of the group) and a chunk
+// holds at least dk_chmin of them.
+__host__ __device__ inline int ragged_chunks_max(const BwdArgs& a) {
+  const int cm = a.dk_chmin < 1 ? 1 : a.dk_chmin;
+  return ((a.H / a.Hk) * a.Tq + cm - 1) / cm;
+}
 
 // Issue order of the MFMAs of one tile in the backward passes: 8 phases,
 // A0 A1 B0 A2 B1 A3 B2 B3.  A(c) (LA MFMAs) forms the scores and G_P of 32-row

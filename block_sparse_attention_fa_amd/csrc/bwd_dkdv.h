@@ -134,14 +134,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a) {
   // this workgroup's chunk of the work: items [i0, i1) of key tile bgk's list
   // (long lists are split over several workgroups; see dk_plan_kernel)
   const int NK = a.B * a.Hk * T;
-  const int nchunks = a.dkplan[0];
-  if ((int)blockIdx.x >= nchunks) return;
-  const int4 chunk = reinterpret_cast<const int4*>(a.dkplan + 4)[work_index(blockIdx.x)];
-  const int kt = chunk.x % T;
-  if constexpr (GS && !CAUSAL) {
-    // the ragged last key tile belongs to the RAGGED instance
-    if (RAGGED != (kt == T - 1 && T * TILE != n)) return;
+  int4 chunk;
+  if constexpr (RAGGED) {
+    // workgroup j * B*Hk + (b*Hk + g) takes chunk j of the ragged last key
+    // tile of (b, g) (chunk-major: the first chunks of all (b, g), the long
+    // ones, sit next to each other and spread over the XCDs); a list of
+    // m <= G*Tq items makes at most ragged_chunks_max chunks
+    const int nbg = a.B * a.Hk;
+    const int k = (int)(blockIdx.x % nbg) * T + T - 1, j = blockIdx.x / nbg;
+    const int32_t* items = a.dkplan + 4 + 8 * NK;
+    const int m = items[k], CH = a.dkplan[3];
+    if (j >= (m <= CH ? 1 : (m + CH - 1) / CH)) return;
+    chunk = reinterpret_cast<const int4*>(a.dkplan + 4)[items[NK + k] + j];
+  } else {
+    if ((int)blockIdx.x >= a.dkplan[0]) return;  // past the plan's chunk count
+    chunk = reinterpret_cast<const int4*>(a.dkplan + 4)[work_index(blockIdx.x)];
+    // the ragged last key tile of the stored non-causal pass belongs to the
+    // RAGGED instance
+    if (GS && !CAUSAL && chunk.x % T == T - 1 && T * TILE != n) return;
   }
+  const int kt = chunk.x % T;
   const int bg = chunk.x / T;
   const int g = bg % a.Hk, b = bg / a.Hk;
   const int G = a.H / a.Hk;

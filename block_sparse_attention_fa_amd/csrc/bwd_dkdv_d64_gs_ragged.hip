@@ -5,7 +5,8 @@
 namespace backlite {
 
 hipError_t launch_dkdv_d64_gs_ragged(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(2 * a.B * a.Hk * a.T), block(256);  // chunks of other key tiles return at once
+  // one workgroup per (b, g) and possible chunk of its last key tile
+  const dim3 grid(a.B * a.Hk * ragged_chunks_max(a)), block(256);
   hipLaunchKernelGGL((dkdv_kernel<64, false, true, true>), grid, block, 0, st, a);
   return hipGetLastError();
 }

@@ -73,6 +73,10 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   __shared__ uint8_t fl[2][MAX_TILES];  // 64-row tiles: which half keeps each key tile
   __shared__ int red[NT / 64];
 
+  // with G_S slots, the query tiles whose kept tiles all have a slot take G_Q
+  // from the stored tiles (dqs_kernel); only the others are recomputed here.
+  // When every tile had a slot the workgroup leaves before any other load.
+  if (a.gsinfo != nullptr && a.gsinfo[0] != 0) return;
   const int T = a.T, n = a.n;
   const int L = work_index(blockIdx.x);
   const int qt = L % T;
@@ -111,9 +115,6 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a) {
   const uint16_t* kbase = a.k + ((long)b * n) * kvstride + (long)g * D;
   const uint16_t* vbase = a.v + ((long)b * n) * kvstride + (long)g * D;
   const float* kbar = a.kbar + (long)(b * a.Hk + g) * T * D;
-  // with G_S slots, the query tiles whose kept tiles all have a slot take G_Q
-  // from the stored tiles (dqs_kernel); only the others are recomputed here
-  if (a.gsinfo != nullptr && a.gsinfo[0] != 0) return;  // every tile had a slot
   const bool split = a.qrows != TILE;                     // two 64-row query tiles
   const int Tq = a.Tq;
   int cnt_h[2] = {0, 0};

@@ -322,6 +322,41 @@ def test_backward_split_lists(chmin, path, monkeypatch):
         assert torch.equal(u.view(torch.int16), v.view(torch.int16))
 
 
+# non-causal with a ragged last key tile (1000 = 7 x 128 + 104 keys), used
+# with a constructed keep pattern: the diagonal, and the ragged tile kept by
+# every query tile, so that tile's list (4 heads x 8 query tiles) is several
+# times the chunk length
+RAGGED_COL = small(1000, H=4, Hk=1, d=128, causal=False, kind="gaussian", seed=13)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_backward_split_ragged_tile(path, monkeypatch):
+    """The ragged last key tile's G_K/G_V list split into chunks (chunk minimum
+    1): on the stored path these chunks run in the instance that masks the
+    padded keys, launched over the ragged tiles' chunks only.  Gradients match
+    the oracle on the same keep pattern and repeat bit for bit."""
+    w = RAGGED_COL
+    r = _setup(w)
+    x = r["x"]
+    T = orc.ntiles(w.n)
+    keep = np.zeros((w.B, w.H, T, T), dtype=bool)
+    keep[:, :, np.arange(T), np.arange(T)] = True
+    keep[:, :, :, T - 1] = True
+    lists = lists_to_torch(keep, r["dev"])
+    longest, ch = _expected_split(lists, w.B, w.Hk, w.H // w.Hk, T, 1)
+    flush_print(f"  ragged tile list {longest} items, chunk length {ch}")
+    assert longest > 2 * ch, "the ragged tile's list must split into several chunks"
+    monkeypatch.setenv("BACKLITE_DKDV_MIN_CHUNK", "1")
+    dq, dk, dv = _bwd_path(r, lists, path)
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal)
+    for name, got, ref in (("dQ", dq, g["dQ"]), ("dK", dk, g["dK"]), ("dV", dv, g["dV"])):
+        rl, cs = assert_close_grad(name, got.cpu(), ref)
+        flush_print(f"  ragged split {path} {name}: rel-L2 {rl:.2e} cos {cs:.6f}")
+    again = _bwd_path(r, lists, path)
+    for u, v in zip((dq, dk, dv), again):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_backward_deterministic(path):
     r = _setup(CASES[1])
