@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void kmean_kernel(BwdArgs a) {
 // together are fewer than 2 * items / CH <= P.  That bounds the partial slots
 // by P and the chunks by NK + P <= 2 NK without reading anything back.
 // The ragged last key tile (n not a multiple of 128) takes the shorter chunk
-// length CHR = max(minimum, ceil(CH / 4)) when the partial slots still fit P
+// length CHR = max(minimum, ceil(CH / 8)) when the partial slots still fit P
 // with it (else CHR = CH): in the stored non-causal pass its chunks run in a
 // launch of their own after the main one, where the longest chunk is the
 // launch's whole duration.
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(1024) void dk_plan_kernel(BwdArgs a) {
   if (tid == 0) chs = (int)max((long long)a.dk_chmin, (2 * part[0] + P - 1) / P);
   __syncthreads();
   const bool ragged = T * TILE != a.n;
-  const int CH = chs, CHR0 = max(a.dk_chmin, (CH + 3) / 4);
+  const int CH = chs, CHR0 = max(a.dk_chmin, (CH + 7) / 8);
   auto split_slots = [](int m, int L) { return m <= L ? 0 : (m + L - 1) / L; };
   {
     // partial slots with CH everywhere, and the ragged tiles' extra with CHR0
