@@ -115,6 +115,14 @@ __device__ __forceinline__ void stage_k_part(bf16* Kd, const __amdgpu_buffer_rsr
   load_lds16(rs, dst, dmo.off[I]);
 }
 
+// lanes 0-31 and 32-63 of x added: the sum in every lane
+__device__ __forceinline__ float add_halves(float x) {
+  const uint64_t u = __builtin_bit_cast(
+      uint64_t, __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                 false, false));
+  return __builtin_bit_cast(float, (uint32_t)u) + __builtin_bit_cast(float, (uint32_t)(u >> 32));
+}
+
 template <int D, int QR>
 __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   constexpr int NT = 256;
@@ -193,8 +201,9 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     constexpr int S = decltype(st)::value;
     return S == 0 ? Kb0 : S == 1 ? Kb1 : Kb2;
   };
-  auto stage_k = [&](int i, auto st) {
-    int kt = i < cnt ? (int)__builtin_amdgcn_readfirstlane(itab[i]) : 0;
+  // kt_raw: the list entry itab[i], read a visit ahead so no LDS wait sits here
+  auto stage_k = [&](int i, int kt_raw, auto st) {
+    int kt = i < cnt ? (int)__builtin_amdgcn_readfirstlane(kt_raw) : 0;
     const bool valid = i < cnt && kt < T;  // entries past the last tile read as empty
     if (!valid) kt = 0;
     const int key0 = kt * TILE;
@@ -234,12 +243,13 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
 
   // prologue, in the order the steady state keeps: G_S 0, K 0, G_S 1, K 1, G_S 2
   load_gs(gr[0], 0);
-  stage_k(0, std::integral_constant<int, 0>{});
+  stage_k(0, itab[0], std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
   load_gs(gr[1], 1);
-  stage_k(1, std::integral_constant<int, 1>{});
+  stage_k(1, itab[1], std::integral_constant<int, 1>{});
   __builtin_amdgcn_sched_barrier(0);
   load_gs(gr[2], 2);
+  int kt_ahead = itab[2];  // list entry of the next K stage (entries past cnt are never used)
 
   const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
   // item j in K stage and G_S register set S = j % 3
@@ -267,7 +277,8 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     // The memory clobber keeps the compiler from moving LDS accesses across.
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    stage_k(j + 2, std::integral_constant<int, (S + 2) % NST>{});
+    stage_k(j + 2, kt_ahead, std::integral_constant<int, (S + 2) % NST>{});
+    kt_ahead = itab[min(j + 3, MAX_TILES - 1)];
     __builtin_amdgcn_sched_barrier(0);
     load_gs(gr[S], j + 3);  // the register set just written to LDS takes item j + 3
     float hsum = 0.f;  // this row's sum of the bf16 G_S operands over the lane's 64 keys
@@ -292,17 +303,19 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     // sum to zero, so that vector would otherwise multiply the rounding
     // error).  sum_j lo_ij = (fp32 row sum of G_S, from the G_K/G_V pass) -
     // (sum of the bf16 operands).  A rank-1 MFMA per 32-dim block, operands
-    // nonzero only in contraction slot 0.
+    // nonzero only in contraction slot 0 (lanes 0-31); every lane loads and
+    // selects, so no branch splits the wave.
     {
-      hsum += __shfl_xor(hsum, 32);
+      hsum = add_halves(hsum);
       const float* lw = Lc + wave * TILE + l32;
       const float ls = ((lw[0] + lw[32]) + (lw[64] + lw[96])) - hsum;
       bf16x8 bl = {};
-      if (h32 == 0) bl[0] = (bf16)ls;
+      bl[0] = (bf16)(h32 == 0 ? ls : 0.f);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
+        const float kb = Bc[(dh * NDB + db) * 32 + l32];
         bf16x8 al = {};
-        if (h32 == 0) al[0] = (bf16)Bc[(dh * NDB + db) * 32 + l32];
+        al[0] = (bf16)(h32 == 0 ? kb : 0.f);
         dq[db] = mfma32(al, bl, dq[db]);
       }
     }
