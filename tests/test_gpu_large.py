@@ -18,7 +18,7 @@ from workloads import DIT480, DIT720, LLM8K, LLM128K, make_inputs
 
 pytestmark = pytest.mark.gpu
 
-# host threads for the oracle's row statistics (the GPU machine's CPU share is 16)
+# host threads for the oracle's row statistics (16: the CPU share of a one-GPU host)
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 LARGE = {
