@@ -201,8 +201,10 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     constexpr int S = decltype(st)::value;
     return S == 0 ? Kb0 : S == 1 ? Kb1 : Kb2;
   };
-  // kt_raw: the list entry itab[i], read a visit ahead so no LDS wait sits here
-  auto stage_k = [&](int i, int kt_raw, auto st) {
+  // kt_raw: the list entry itab[i], read a visit ahead so no LDS wait sits
+  // here.  Issues the row-sum and key-mean copies and returns the resource of
+  // item i's K rows.
+  auto stage_small = [&](int i, int kt_raw, auto st) -> __amdgpu_buffer_rsrc_t {
     int kt = i < cnt ? (int)__builtin_amdgcn_readfirstlane(kt_raw) : 0;
     const bool valid = i < cnt && kt < T;  // entries past the last tile read as empty
     if (!valid) kt = 0;
@@ -223,22 +225,30 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
                       (uint32_t)((e >> 5) * QR + 32 * rw + (e & 31)) * 4u);
     }
     load_lds4(rb, lds_ptr(b_of(st) + 64 * kb_part), (uint32_t)(64 * kb_part + lane) * 4u);
+    return rk;
+  };
+  auto stage_k = [&](int i, int kt_raw, auto st) {
+    const __amdgpu_buffer_rsrc_t rk = stage_small(i, kt_raw, st);
     static_for<0, NI>([&](auto ic) { stage_k_part<D, NT, decltype(ic)::value>(k_of(st), rk, dmo, wave); });
   };
   // the wave's NGS blocks of item i's G_S into registers: block ib = (kw, s) of
   // its row group (kw = 2 dh + ib / 2 when QR = 64), lane l takes the 16 bytes
   // at position l ^ 8s
   u32x4 gr[NST][NGS];
-  auto load_gs = [&](u32x4 (&r)[NGS], int i) {
+  auto gs_rsrc = [&](int i) {
     const size_t slot = (size_t)sbase + (size_t)i;
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.gs + slot * (QR * TILE), i < cnt ? QR * TILE * 2u : 0u);
+    return buffer_rsrc(a.gs + slot * (QR * TILE), i < cnt ? QR * TILE * 2u : 0u);
+  };
+  auto load_gs_block = [&](u32x4& r, const __amdgpu_buffer_rsrc_t& rs, int ib) {
+    const int kw = (QR == TILE ? 0 : 2 * dh) + (ib >> 1), s2 = ib & 1;
+    r = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)((lane ^ (8 * s2)) * 16),
+                                                                       ((kw * (QR / 32) + rw) * 2 + s2) * 1024,
+                                                                       CPOL_NT));
+  };
+  auto load_gs = [&](u32x4 (&r)[NGS], int i) {
+    const __amdgpu_buffer_rsrc_t rs = gs_rsrc(i);
 #pragma unroll
-    for (int ib = 0; ib < NGS; ++ib) {
-      const int kw = (QR == TILE ? 0 : 2 * dh) + (ib >> 1), s2 = ib & 1;
-      r[ib] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, (uint32_t)((lane ^ (8 * s2)) * 16),
-                                            ((kw * (QR / 32) + rw) * 2 + s2) * 1024, CPOL_NT));
-    }
+    for (int ib = 0; ib < NGS; ++ib) load_gs_block(r[ib], rs, ib);
   };
 
   // prologue, in the order the steady state keeps: G_S 0, K 0, G_S 1, K 1, G_S 2
@@ -277,25 +287,51 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     // The memory clobber keeps the compiler from moving LDS accesses across.
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    stage_k(j + 2, kt_ahead, std::integral_constant<int, (S + 2) % NST>{});
+    // Item j + 2's K copies and item j + 3's G_S loads go out a few per 16-key
+    // step between the MFMAs (the K copies over the first half of the steps,
+    // the G_S loads over the second: the order the wait above counts).
+    // Issued back to back they stall the wave until the copy pipeline takes
+    // them, with nothing else to issue meanwhile.
+    constexpr std::integral_constant<int, (S + 2) % NST> nxt;
+    const __amdgpu_buffer_rsrc_t rk = stage_small(j + 2, kt_ahead, nxt);
     kt_ahead = itab[min(j + 3, MAX_TILES - 1)];
-    __builtin_amdgcn_sched_barrier(0);
-    load_gs(gr[S], j + 3);  // the register set just written to LDS takes item j + 3
+    const __amdgpu_buffer_rsrc_t rg = gs_rsrc(j + 3);  // into the register set just written to LDS
     float hsum = 0.f;  // this row's sum of the bf16 G_S operands over the lane's 64 keys
-    static_for<0, NKS>([&](auto kc) {
+    // operands of one 16-key step (the G_S fragment, the K fragments of the
+    // wave's head-dimension blocks), read one step ahead
+    auto fetch = [&](auto kc, bf16x8& gop, bf16x8 (&kop)[NDB]) {
       constexpr int ks = decltype(kc)::value;
       const char* gb = gb0 + (ks >> 1) * 2048 + (ks & 1) * 512 + goff;
       const bf16x4 g0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(gb));
       const bf16x4 g1 =
           __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(gb + 256));
-      const bf16x8 bop = cat8(g0, g1);
+      gop = cat8(g0, g1);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(rd_tr<D>(Kc, lo, ks >> 1, ks & 1, db), bop, dq[db]);
+      for (int db = 0; db < NDB; ++db) kop[db] = rd_tr<D>(Kc, lo, ks >> 1, ks & 1, db);
+    };
+    constexpr int HALF = NKS / 2;
+    bf16x8 gop[2], kop[2][NDB];
+    fetch(std::integral_constant<int, 0>{}, gop[0], kop[0]);
+    static_for<0, NKS>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      if constexpr (ks + 1 < NKS) fetch(std::integral_constant<int, ks + 1>{}, gop[(ks + 1) & 1], kop[(ks + 1) & 1]);
+      static_for<0, NI>([&](auto ic) {  // K copy c in step c HALF / NI
+        constexpr int c = decltype(ic)::value;
+        if constexpr (c * HALF / NI == ks) stage_k_part<D, NT, c>(k_of(nxt), rk, dmo, wave);
+      });
+      static_for<0, NGS>([&](auto ic) {  // G_S block ib in step HALF + ib HALF / NGS
+        constexpr int ib = decltype(ic)::value;
+        if constexpr (HALF + ib * HALF / NGS == ks) load_gs_block(gr[S][ib], rg, ib);
+      });
+      const bf16x8 bop = gop[ks & 1];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dq[db] = mfma32(kop[ks & 1][db], bop, dq[db]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bf16x2 pr = {bop[2 * u], bop[2 * u + 1]};
         hsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, hsum, false);
       }
+      __builtin_amdgcn_sched_barrier(0);
     });
     // Rounding compensation: the stored G_S is bf16.  Its rounding residual lo
     // contributes sum_j lo_ij K_j, whose dominant part when the tile's keys
