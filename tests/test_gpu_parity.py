@@ -358,6 +358,56 @@ def test_backward_split_ragged_tile(path, monkeypatch):
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_backward_plan_mixed_lists(path, monkeypatch):
+    """A keep pattern that exercises the G_K/G_V chunk plan's ordering: most
+    key tiles (the ragged last one included) have empty lists, one is kept by
+    every query tile of every head (32 items, split into four chunks at chunk
+    minimum 1), two have short lists, so the tiles fall in several length
+    classes and the chunk table holds zero-length chunks.  Gradients match
+    the oracle on the same pattern and repeat bit for bit."""
+    w = RAGGED_COL
+    r = _setup(w)
+    x = r["x"]
+    T = orc.ntiles(w.n)
+    keep = np.zeros((w.B, w.H, T, T), dtype=bool)
+    keep[:, :, :, 2] = True
+    keep[:, 0, 3, 5] = True
+    keep[:, 1, :4, 6] = True
+    lists = lists_to_torch(keep, r["dev"])
+    longest, ch = _expected_split(lists, w.B, w.Hk, w.H // w.Hk, T, 1)
+    assert longest > 2 * ch, "the long list must split into several chunks"
+    monkeypatch.setenv("BACKLITE_DKDV_MIN_CHUNK", "1")
+    dq, dk, dv = _bwd_path(r, lists, path)
+    g = orc.backward(x["q"], x["k"], x["v"], x["do"], keep=keep, causal=w.causal)
+    for name, got, ref in (("dQ", dq, g["dQ"]), ("dK", dk, g["dK"]), ("dV", dv, g["dV"])):
+        rl, cs = assert_close_grad(name, got.cpu(), ref)
+        flush_print(f"  mixed lists {path} {name}: rel-L2 {rl:.2e} cos {cs:.6f}")
+    # key tiles no query tile keeps get exactly zero gradients
+    dk_c, dv_c = dk.cpu().float(), dv.cpu().float()  # [B, n, H_k, d]
+    for kt in (0, 1, 3, 4, 7):
+        rows = slice(kt * 128, min(w.n, (kt + 1) * 128))
+        assert (dk_c[:, rows] == 0).all() and (dv_c[:, rows] == 0).all()
+    again = _bwd_path(r, lists, path)
+    for u, v in zip((dq, dk, dv), again):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+
+
+def test_backward_nothing_kept():
+    """Lists that keep no tile at all (a caller may build them): every
+    gradient is exactly zero."""
+    w = RAGGED_COL
+    r = _setup(w)
+    bl, xg = r["bl"], r["xg"]
+    T = orc.ntiles(w.n)
+    lists = lists_to_torch(np.zeros((w.B, w.H, T, T), dtype=bool), r["dev"])
+    dq, dk, dv = bl.bwd(xg["q"], xg["k"], xg["v"], r["o"], xg["do"], r["lse"], lists, causal=w.causal,
+                        o_lo=r["olo"])
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert (t.float() == 0).all(), name
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_backward_deterministic(path):
     r = _setup(CASES[1])
     bl, w = r["bl"], r["w"]
