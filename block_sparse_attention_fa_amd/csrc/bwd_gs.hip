@@ -262,6 +262,19 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   int kt_ahead = itab[2];  // list entry of the next K stage (entries past cnt are never used)
 
   const bf16x2 one2 = {(bf16)1.f, (bf16)1.f};
+  // rounding-compensation operands of the current group of NST items, item j
+  // in contraction slot j % NST (see the end of visit); zero elsewhere
+  bf16x8 cal[NDB], cbl = {};
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) cal[db] = bf16x8{};
+  auto flush_comp = [&]() {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dq[db] = mfma32(cal[db], cbl, dq[db]);
+      cal[db] = bf16x8{};
+    }
+    cbl = bf16x8{};
+  };
   // item j in K stage and G_S register set S = j % 3
   auto visit = [&](int j, auto stage) {
     constexpr int S = decltype(stage)::value;
@@ -363,22 +376,21 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
     // share a large common vector is (sum_j lo_ij) * kbar (rows of G_S nearly
     // sum to zero, so that vector would otherwise multiply the rounding
     // error).  sum_j lo_ij = (fp32 row sum of G_S, from the G_K/G_V pass) -
-    // (sum of the bf16 operands).  A rank-1 MFMA per 32-dim block, operands
-    // nonzero only in contraction slot 0 (lanes 0-31); every lane loads and
-    // selects, so no branch splits the wave.
+    // (sum of the bf16 operands).  Each item's rank-1 term goes into
+    // contraction slot S of the group's operands (lanes 0-31; every lane
+    // loads and selects, so no branch splits the wave), and one MFMA per
+    // 32-dim block adds the NST items' terms at the end of the group.
     {
       hsum = add_halves(hsum);
       const float* lw = Lc + wave * TILE + l32;
       const float ls = ((lw[0] + lw[32]) + (lw[64] + lw[96])) - hsum;
-      bf16x8 bl = {};
-      bl[0] = (bf16)(h32 == 0 ? ls : 0.f);
+      cbl[S] = (bf16)(h32 == 0 ? ls : 0.f);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const float kb = Bc[(dh * NDB + db) * 32 + l32];
-        bf16x8 al = {};
-        al[0] = (bf16)(h32 == 0 ? kb : 0.f);
-        dq[db] = mfma32(al, bl, dq[db]);
+        cal[db][S] = (bf16)(h32 == 0 ? kb : 0.f);
       }
+      if constexpr (S == NST - 1) flush_comp();
     }
   };
   int j = 0;
@@ -389,6 +401,7 @@ __global__ __launch_bounds__(256, 1) void dqs_kernel(BwdArgs a) {
   }
   if (j < cnt) visit(j, std::integral_constant<int, 0>{});
   if (j + 1 < cnt) visit(j + 1, std::integral_constant<int, 1>{});
+  flush_comp();  // the tail's items (zero operands when there is no tail)
 
   // epilogue: dq C layout is [dim = 32db + 8(r/4) + 4*h32 + r%4][query l32]
   // (db counted from the wave's head-dimension slice)
